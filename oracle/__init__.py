@@ -1,0 +1,12 @@
+"""CPU oracle for the Gated DeltaNet ReplaySSM verify / rollback / flush path.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path imports, calls or links
+anything in this package. Only the tests, the smoke check and the benchmark's
+CPU-baseline leg use it. It shares no code with the HIP library.
+
+  gdn_oracle   fp64 token-by-token recurrence, full-state snapshot / restore on
+               rejection, and an independent replay mode.
+  bookkeeping  pure-integer model of the ring pointers and error bits.
+  wy_check     fp64 chunk (WY / UT) form of the same replay, used only to pin
+               the algebra that the HIP kernels implement.
+"""

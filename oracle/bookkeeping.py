@@ -1,0 +1,75 @@
+"""Pure-integer model of the replay ring pointers and the sticky error word.
+
+TEST INFRASTRUCTURE ONLY. Follows "The inference stack behind OCRia"
+(LlamaIndex), section "Making speculative verification cheaper": a rejection
+only moves a buffer pointer so that the accepted prefix is kept; the full
+checkpoint is written only at a periodic flush.
+
+Per slot: head (ring position of the first committed token), len (number of
+committed tokens not yet folded into the checkpoint), capacity C.
+
+  verify(D):    needs len + D <= C; the draft occupies ring positions
+                (head + len + j) mod C, j < D. Pointers unchanged.
+  rollback(a):  needs 0 <= a <= D and len + a <= C; len += a.
+  flush(m):     if len >= max(m, 1): head = (head + len) mod C, len = 0.
+Violations set CAPACITY=1 / ACCEPT=2 / SLOT=4 and leave the slot untouched.
+"""
+from __future__ import annotations
+
+ERR_CAPACITY = 1
+ERR_ACCEPT = 2
+ERR_SLOT = 4
+
+
+class RingPointers:
+    def __init__(self, head, length, cap: int):
+        self.head = [int(h) for h in head]
+        self.len = [int(n) for n in length]
+        self.cap = int(cap)
+        self.err = 0
+
+    def _ok(self, s: int) -> bool:
+        if not 0 <= s < len(self.head):
+            self.err |= ERR_SLOT
+            return False
+        return True
+
+    def verify(self, slots, draft_len: int):
+        """Returns {slot: [ring positions written]} for the requests accepted."""
+        written = {}
+        for s in slots:
+            s = int(s)
+            if not self._ok(s):
+                continue
+            if self.len[s] + draft_len > self.cap:
+                self.err |= ERR_CAPACITY
+                continue
+            written[s] = [(self.head[s] + self.len[s] + j) % self.cap for j in range(draft_len)]
+        return written
+
+    def rollback(self, slots, draft_len: int, accepted):
+        for s, a in zip(slots, accepted):
+            s, a = int(s), int(a)
+            if not self._ok(s):
+                continue
+            if not 0 <= a <= draft_len:
+                self.err |= ERR_ACCEPT
+                continue
+            if self.len[s] + a > self.cap:
+                self.err |= ERR_CAPACITY
+                continue
+            self.len[s] += a
+
+    def flush(self, slots, min_len: int):
+        """Returns {slot: number of tokens folded} for the slots that were due."""
+        folded = {}
+        for s in slots:
+            s = int(s)
+            if not self._ok(s):
+                continue
+            n = self.len[s]
+            if n >= max(int(min_len), 1):
+                folded[s] = n
+                self.head[s] = (self.head[s] + n) % self.cap
+                self.len[s] = 0
+        return folded

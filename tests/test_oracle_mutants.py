@@ -1,0 +1,126 @@
+"""Each plausible slip planted in the oracle (on the CPU) must fail at least one pin.
+
+The mutants stand for the mistakes a re-implementation of the gated delta rule
+replay typically makes: a transposed operand, a dropped or sign-flipped term, an
+off-by-one ring index, the output taken before the update, the wrong GVA head
+grouping, a wrong pointer move at flush.
+"""
+import numpy as np
+import pytest
+
+from oracle import gdn_oracle as go
+from tests import test_bookkeeping as bkpins
+from tests import test_oracle as pins
+
+PIN_TESTS = [
+    lambda: pins.test_exact_rational_brute_force(),
+    lambda: pins.test_golden_hand_worked_d2(),
+    lambda: pins.test_beta_zero_is_pure_decay(False),
+    lambda: pins.test_beta_zero_is_pure_decay(True),
+    lambda: pins.test_alpha_one_beta_zero_is_identity_and_flush_keeps_bits(),
+    lambda: pins.test_delta_rule_writes_value_at_key(False),
+    lambda: pins.test_delta_rule_writes_value_at_key(True),
+    lambda: pins.test_orthonormal_keys_closed_form(),
+    lambda: pins.test_scalar_recurrence_closed_form(),
+    lambda: pins.test_state_layout_is_transpose(),
+    lambda: pins.test_linearity_in_state_and_values(),
+    lambda: pins.test_replay_equals_sequential_recurrence(),
+    lambda: pins.test_rollback_prefix_equals_recurrence_over_prefix(),
+    lambda: pins.test_flush_then_verify_equals_verify_without_flush(),
+    lambda: pins.test_gva_head_grouping(),
+    lambda: pins.test_error_bits_and_skips(),
+    lambda: bkpins.test_pointer_walk_on_oracle(),
+    lambda: bkpins.test_committed_window_holds_accepted_tokens_in_order(),
+]
+
+
+def _output_transposed(S, q):
+    return np.einsum("...ji,...j->...i", S, q) if S.shape[-1] == S.shape[-2] else \
+        np.einsum("...ij,...j->...i", S, q)[..., ::-1]
+
+
+def _step_no_alpha_in_correction(S, k, v, alpha, beta):
+    Sk = np.einsum("...ij,...j->...i", S, k)
+    u = beta[..., None] * (v - Sk)
+    return alpha[..., None, None] * S + u[..., :, None] * k[..., None, :]
+
+
+def _step_sign(S, k, v, alpha, beta):
+    Sk = np.einsum("...ij,...j->...i", S, k)
+    u = beta[..., None] * (v + alpha[..., None] * Sk)
+    return alpha[..., None, None] * S + u[..., :, None] * k[..., None, :]
+
+
+def _step_literal_sign(S, k, v, alpha, beta):
+    dk = S.shape[-1]
+    M = np.eye(dk) + beta[..., None, None] * (k[..., :, None] * k[..., None, :])
+    return alpha[..., None, None] * (S @ M) + beta[..., None, None] * (v[..., :, None] * k[..., None, :])
+
+
+def _step_decay_after(S, k, v, alpha, beta):
+    # decays the write too: alpha (S (I - b k k^T) + b v k^T)
+    dk = S.shape[-1]
+    M = np.eye(dk) - beta[..., None, None] * (k[..., :, None] * k[..., None, :])
+    return alpha[..., None, None] * (S @ M + beta[..., None, None] * (v[..., :, None] * k[..., None, :]))
+
+
+def _kv_heads_interleaved(self, kh_vec):
+    return np.tile(kh_vec, (self.group, 1))
+
+
+def _advance_ring_off_by_one(self, S, s, start, count):
+    for t in range(count):
+        pos = (int(self.head[s]) + start + t + 1) % self.cap
+        S = self._step(S, *self._ring_record(s, pos))
+    return S
+
+
+_orig_flush = go.ReplayOracle.flush
+
+
+def _flush_bad_head(self, slot_idx, min_len):
+    h = self.head.copy()
+    n = self.len.copy()
+    _orig_flush(self, slot_idx, min_len)
+    for s in np.asarray(slot_idx):
+        s = int(s)
+        if 0 <= s < self.num_slots and n[s] >= max(min_len, 1):
+            self.head[s] = (h[s] + n[s] - 1) % self.cap
+
+
+_orig_verify = go.ReplayOracle.verify
+
+
+def _verify_output_before_update(self, slot_idx, q, k, v, alpha, beta):
+    # emits S_{t-1} q_t: shift each request's outputs by one token
+    out = _orig_verify(self, slot_idx, q, k, v, alpha, beta)
+    return np.concatenate([out[:, :1] * 0.0 + out[:, :1], out[:, :-1]], axis=1)
+
+
+MUTANTS = {
+    "output_transposed": ("gdn_output", _output_transposed, None),
+    "rank1_drops_alpha": ("gdn_step", _step_no_alpha_in_correction, None),
+    "rank1_sign": ("gdn_step", _step_sign, None),
+    "literal_sign": ("gdn_step_literal", _step_literal_sign, None),
+    "literal_decays_write": ("gdn_step_literal", _step_decay_after, None),
+    "gva_interleaved": (None, _kv_heads_interleaved, "_kv_heads"),
+    "ring_off_by_one": (None, _advance_ring_off_by_one, "_advance_ring"),
+    "flush_head": (None, _flush_bad_head, "flush"),
+    "output_before_update": (None, _verify_output_before_update, "verify"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    fn_name, fn, method = MUTANTS[name]
+    if fn_name:
+        monkeypatch.setattr(go, fn_name, fn)
+    else:
+        monkeypatch.setattr(go.ReplayOracle, method, fn)
+    failures = 0
+    for t in PIN_TESTS:
+        try:
+            t()
+        except AssertionError:
+            failures += 1
+    assert failures > 0, f"mutant {name} passed every pin"

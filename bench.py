@@ -1,0 +1,241 @@
+"""Benchmark of the GDN ReplaySSM verify / rollback / flush path on one MI355X.
+
+One step = the whole path over every GDN layer of the model for one batch:
+verify on all layers, then rollback on all layers, then flush on all layers
+(the order of a speculative decode step; "The inference stack behind OCRia",
+section "Making speculative verification cheaper": 32 concurrent requests,
+24 GDN layers). Each layer has its own cache (state + ring + pointers), so the
+24 states (1.5 GiB at 32 requests) do not fit in the 256 MB Infinity Cache and
+every verify streams its state from HBM.
+
+Timing: HIP events on the launch stream bracket the 24 verify launches, the 24
+rollback launches and the 24 flush launches of every timed step. The headline
+value is (verify time + flush time) per layer in microseconds, averaged over the
+timed steps. Algorithmic bytes come from the byte model below, evaluated with
+the actual buffer lengths of every call (tracked on the host from the known
+schedule).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GDN replay verify+flush us/layer and HBM GB/s (% roofline) at 32 reqs"
+HBM_PEAK_GBPS = 8000.0
+
+
+def byte_model(wl, lens_at_verify, folded):
+    """Algorithmic HBM bytes of one layer's verify and flush calls.
+
+    verify: state read R*HV*dk*dv*4; committed ring read sum_r B_r*(HK*dk*ib +
+    HV*dv*ib + HV*8); draft read and ring append R*D*(2*HK*dk*ib + HV*dv*ib +
+    HV*8) each (q is appended too); out write R*D*HV*dv*4.
+    flush: for each folded slot, state read + write HV*dk*dv*8 and ring read
+    n*(HK*dk*ib + HV*dv*ib + HV*8)."""
+    ib = wl.in_bytes
+    R, D, HV, HK, dk, dv = wl.num_reqs, wl.draft, wl.hv, wl.hk, wl.dk, wl.dv
+    tok_ring = HK * dk * ib + HV * dv * ib + HV * 8
+    tok_draft = 2 * HK * dk * ib + HV * dv * ib + HV * 8
+    v_bytes = (R * HV * dk * dv * 4 + int(np.sum(lens_at_verify)) * tok_ring
+               + 2 * R * D * tok_draft + R * D * HV * dv * 4)
+    f_bytes = sum(HV * dk * dv * 8 + int(n) * tok_ring for n in folded)
+    return v_bytes, f_bytes
+
+
+def cpu_baseline(wl, seconds_budget=15.0):
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload:
+    verify + rollback + flush of whole layers (every request, buffer 5 + draft D,
+    every slot flushed) until about `seconds_budget` seconds of CPU work."""
+    from threadpoolctl import threadpool_limits
+
+    from gated_deltanet_state_replayssm_amd import synth
+    from oracle import gdn_oracle as go
+
+    done = 0
+    spent = 0.0
+    while spent < seconds_budget and done < wl.layers:
+        rng = np.random.default_rng(synth.seed_for(wl.name, done, 999))
+        init = synth.make_cache_init(wl, rng, init_len=np.full(wl.num_slots, 5, np.int32))
+        orc = go.ReplayOracle(init, wl.hv, wl.hk, wl.dk, wl.dv, wl.cap, mode="replay")
+        dr = synth.make_draft(wl, rng)
+        slots = np.arange(wl.num_reqs, dtype=np.int32)
+        acc = synth.sample_accepted(wl, rng)
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            orc.verify(slots, dr["q"], dr["k"], dr["v"], dr["alpha"], dr["beta"])
+            orc.rollback(slots, wl.draft, acc)
+            orc.flush(slots, 1)
+            spent += time.perf_counter() - t0
+        done += 1
+    us_per_layer = spent / done * 1e6
+    return {"value": round(us_per_layer, 1), "unit": "us/layer", "cores": 1, "kind": "oracle",
+            "sample": f"{done} whole layer(s) of {wl.num_reqs} requests, committed buffer 5 + "
+                      f"draft {wl.draft}, every slot flushed; fp64 NumPy, 1 thread, "
+                      f"{spent:.1f} s timed"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="r32_hv32_hk16_d128_f16")
+    ap.add_argument("--layers", type=int, default=None)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the replay path needs no collective and this "
+              "build runs on a single MI355X (--gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from gated_deltanet_state_replayssm_amd import binding, synth
+    from gated_deltanet_state_replayssm_amd.cache import ReplayCache, to_device
+
+    binding.load()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    wl = synth.WORKLOADS[args.workload]
+    layers = args.layers or wl.layers
+    stream = torch.cuda.current_stream()
+
+    rng = np.random.default_rng(synth.seed_for(wl.name, 0, 0))
+    caches = []
+    for L in range(layers):
+        lrng = np.random.default_rng(synth.seed_for(wl.name, L, 0))
+        init = synth.make_cache_init(wl, lrng)
+        caches.append(ReplayCache.from_numpy(init, wl.hv, wl.hk, wl.dk, wl.dv, wl.cap,
+                                             wl.in_dtype))
+    init_len = caches[0].len.cpu().numpy().astype(np.int64)
+    # two draft sets per layer, alternated: values do not change the work done
+    drafts = []
+    for L in range(layers):
+        ds = []
+        for j in range(2):
+            d = synth.make_draft(wl, np.random.default_rng(synth.seed_for(wl.name, L, 50 + j)))
+            ds.append({k: to_device(v) for k, v in d.items()})
+        drafts.append(ds)
+    out = torch.empty((wl.num_reqs, wl.draft, wl.hv, wl.dv), dtype=torch.float32, device="cuda")
+
+    total = args.warmup + args.steps
+    sched = []
+    lens = init_len.copy()  # identical across layers (same init lengths, same accepts)
+    for step in range(total):
+        slots = synth.make_slot_idx(wl, rng)
+        acc = synth.sample_accepted(wl, rng)
+        lv = lens[slots].copy()
+        lens[slots] += acc
+        due = lens[slots] >= max(wl.flush_min_len, 1)
+        folded = lens[slots][due].copy()
+        lens[slots[due]] = 0
+        sched.append(dict(slots=to_device(slots), acc=to_device(acc), lv=lv, folded=folded))
+    torch.cuda.synchronize()
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def run_step(step, marks):
+        sc = sched[step]
+        e = [ev() for _ in range(4)]
+        e[0].record(stream)
+        for L in range(layers):
+            d = drafts[L][step % 2]
+            caches[L].verify(sc["slots"], d["q"], d["k"], d["v"], d["alpha"], d["beta"], out=out)
+        e[1].record(stream)
+        for L in range(layers):
+            caches[L].rollback(sc["slots"], wl.draft, sc["acc"])
+        e[2].record(stream)
+        for L in range(layers):
+            caches[L].flush(sc["slots"], wl.flush_min_len)
+        e[3].record(stream)
+        marks.append(e)
+
+    warm_marks, marks = [], []
+    for step in range(args.warmup):
+        run_step(step, warm_marks)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for step in range(args.warmup, total):
+        run_step(step, marks)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+
+    tv = tr = tf = 0.0
+    vb = fb = 0
+    for step in range(args.warmup, total):
+        e = marks[step - args.warmup]
+        tv += e[0].elapsed_time(e[1])
+        tr += e[1].elapsed_time(e[2])
+        tf += e[2].elapsed_time(e[3])
+        b_v, b_f = byte_model(wl, sched[step]["lv"], sched[step]["folded"])
+        vb += b_v * layers          # every layer sees the same lengths
+        fb += b_f * layers
+    K = args.steps
+    n_launch = K * layers
+    us_verify = tv * 1e3 / n_launch
+    us_rollback = tr * 1e3 / n_launch
+    us_flush = tf * 1e3 / n_launch
+    us_layer = us_verify + us_flush
+    bytes_layer = (vb + fb) / n_launch
+    gbps = bytes_layer / (us_layer * 1e-6) / 1e9
+    v_bytes = vb / n_launch
+    f_bytes = fb / n_launch
+    v_gbps = v_bytes / (us_verify * 1e-6) / 1e9
+    f_gbps = f_bytes / (us_flush * 1e-6) / 1e9 if us_flush > 0 else 0.0
+    errs = [int(c.err.item()) for c in caches]
+    assert not any(errs), f"device error bits set: {errs}"
+
+    dominant = "verify" if us_verify >= us_flush else "flush"
+    dom_gbps, dom_bytes, dom_us = ((v_gbps, v_bytes, us_verify) if dominant == "verify"
+                                   else (f_gbps, f_bytes, us_flush))
+    line = {
+        "metric": METRIC,
+        "value": round(us_layer, 2),
+        "unit": "us/layer",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / K, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "requests": wl.num_reqs, "v_heads": wl.hv,
+                   "k_heads": wl.hk, "d_k": wl.dk, "d_v": wl.dv, "draft": wl.draft,
+                   "ring_cap": wl.cap, "flush_min_len": wl.flush_min_len, "layers": layers,
+                   "inputs": wl.in_dtype, "state": "f32"},
+        "hbm_gbps": round(gbps, 1),
+        "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "bytes_per_layer": int(bytes_layer),
+        "kernels": {
+            "verify": {"us": round(us_verify, 2), "bytes": int(v_bytes), "gbps": round(v_gbps, 1)},
+            "flush": {"us": round(us_flush, 2), "bytes": int(f_bytes), "gbps": round(f_gbps, 1)},
+            "rollback": {"us": round(us_rollback, 2)},
+        },
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(dom_gbps, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(dom_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "bytes_per_launch": int(dom_bytes), "us_per_launch": round(dom_us, 2)},
+        "pages_context": {"b200_custom_kernel_us_per_layer": "23-24",
+                          "b200_triton_us_per_layer": "72-80"},
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,116 @@
+"""Thin ctypes binding of libgdnreplay.so (include/gdn_replay.h).
+
+Argument marshalling only: every step of verify / rollback / flush runs in the
+HIP kernels behind the C ABI. PyTorch provides device memory and the stream.
+If the library is missing this module raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libgdnreplay.so")
+
+GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EHIP = 0, -1, -2, -3
+GDN_BF16, GDN_F32 = 0, 1
+GDN_DERR_CAPACITY, GDN_DERR_ACCEPT, GDN_DERR_SLOT, GDN_DERR_POINTER = 1, 2, 4, 8
+
+EXPORTED = ("gdn_replay_verify", "gdn_replay_rollback", "gdn_replay_flush",
+            "gdn_replay_strerror", "gdn_replay_version")
+
+
+class GdnReplayCache(ctypes.Structure):
+    """Mirror of gdn_replay_cache."""
+    _fields_ = [
+        ("num_slots", ctypes.c_int32),
+        ("num_v_heads", ctypes.c_int32),
+        ("num_k_heads", ctypes.c_int32),
+        ("d_k", ctypes.c_int32),
+        ("d_v", ctypes.c_int32),
+        ("ring_cap", ctypes.c_int32),
+        ("in_dtype", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("state", ctypes.c_void_p),
+        ("ring_q", ctypes.c_void_p),
+        ("ring_k", ctypes.c_void_p),
+        ("ring_v", ctypes.c_void_p),
+        ("ring_alpha", ctypes.c_void_p),
+        ("ring_beta", ctypes.c_void_p),
+        ("head", ctypes.c_void_p),
+        ("len", ctypes.c_void_p),
+        ("sync", ctypes.c_void_p),
+        ("err", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load the library (once) and declare the signatures. Raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run gated_deltanet_state_replayssm_amd.build")
+    lib = ctypes.CDLL(path)
+    P, I32, VP = ctypes.POINTER(GdnReplayCache), ctypes.c_int32, ctypes.c_void_p
+    lib.gdn_replay_verify.argtypes = [P, I32, VP, I32, VP, VP, VP, VP, VP, VP, VP]
+    lib.gdn_replay_verify.restype = ctypes.c_int
+    lib.gdn_replay_rollback.argtypes = [P, I32, VP, I32, VP, VP]
+    lib.gdn_replay_rollback.restype = ctypes.c_int
+    lib.gdn_replay_flush.argtypes = [P, I32, VP, I32, VP]
+    lib.gdn_replay_flush.restype = ctypes.c_int
+    lib.gdn_replay_strerror.argtypes = [ctypes.c_int]
+    lib.gdn_replay_strerror.restype = ctypes.c_char_p
+    lib.gdn_replay_version.argtypes = []
+    lib.gdn_replay_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+class GdnError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        msg = load().gdn_replay_strerror(status).decode()
+        super().__init__(f"{fn} returned {status}: {msg}")
+        self.status = status
+
+
+def _check(fn: str, status: int) -> None:
+    if status != GDN_OK:
+        raise GdnError(fn, status)
+
+
+def verify_raw(cache: GdnReplayCache, num_reqs, slot_idx, draft_len, q, k, v, alpha, beta,
+               out, stream) -> int:
+    return load().gdn_replay_verify(ctypes.byref(cache), num_reqs, slot_idx, draft_len, q, k, v,
+                                    alpha, beta, out, stream)
+
+
+def rollback_raw(cache: GdnReplayCache, num_reqs, slot_idx, draft_len, num_accepted,
+                 stream) -> int:
+    return load().gdn_replay_rollback(ctypes.byref(cache), num_reqs, slot_idx, draft_len,
+                                      num_accepted, stream)
+
+
+def flush_raw(cache: GdnReplayCache, num_reqs, slot_idx, min_len, stream) -> int:
+    return load().gdn_replay_flush(ctypes.byref(cache), num_reqs, slot_idx, min_len, stream)
+
+
+def verify(cache, num_reqs, slot_idx, draft_len, q, k, v, alpha, beta, out, stream) -> None:
+    _check("gdn_replay_verify",
+           verify_raw(cache, num_reqs, slot_idx, draft_len, q, k, v, alpha, beta, out, stream))
+
+
+def rollback(cache, num_reqs, slot_idx, draft_len, num_accepted, stream) -> None:
+    _check("gdn_replay_rollback",
+           rollback_raw(cache, num_reqs, slot_idx, draft_len, num_accepted, stream))
+
+
+def flush(cache, num_reqs, slot_idx, min_len, stream) -> None:
+    _check("gdn_replay_flush", flush_raw(cache, num_reqs, slot_idx, min_len, stream))
+
+
+def version() -> int:
+    return load().gdn_replay_version()

@@ -1,0 +1,136 @@
+// C-ABI entry points of libgdnreplay.so: synchronous host validation, then one
+// asynchronous launch on the caller's stream. No allocation, no host/device sync.
+#include <stdint.h>
+
+#include "internal.h"
+
+namespace {
+
+using gdnr::CacheView;
+
+constexpr int32_t kMaxRingCap = 256;
+constexpr int32_t kMaxHeads = 4096;  // grid.y limit headroom
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Checks shared by all three calls.
+int check_cache(const gdn_replay_cache *c) {
+  if (!c) return GDN_EINVAL;
+  if (c->num_slots < 1 || c->num_v_heads < 1 || c->num_k_heads < 1 || c->d_k < 1 ||
+      c->d_v < 1 || c->ring_cap < 1)
+    return GDN_EINVAL;
+  if (c->num_v_heads % c->num_k_heads != 0) return GDN_EINVAL;
+  if (c->num_v_heads > kMaxHeads) return GDN_EUNSUPPORTED;
+  if (c->in_dtype != GDN_BF16 && c->in_dtype != GDN_F32) return GDN_EINVAL;
+  if (!gdnr::dims_supported(c->d_k, c->d_v)) return GDN_EUNSUPPORTED;
+  if (c->ring_cap > kMaxRingCap) return GDN_EUNSUPPORTED;
+  if (!c->state || !c->ring_k || !c->ring_v || !c->ring_alpha || !c->ring_beta || !c->head ||
+      !c->len || !c->sync)
+    return GDN_EINVAL;
+  if (!aligned(c->state, 16) || !aligned(c->ring_k, 16) || !aligned(c->ring_v, 16) ||
+      (c->ring_q && !aligned(c->ring_q, 16)) || !aligned(c->ring_alpha, 4) ||
+      !aligned(c->ring_beta, 4) || !aligned(c->head, 4) || !aligned(c->len, 4) ||
+      !aligned(c->sync, 4) || (c->err && !aligned(c->err, 4)))
+    return GDN_EINVAL;
+  return GDN_OK;
+}
+
+CacheView view_of(const gdn_replay_cache *c) {
+  CacheView v;
+  v.num_slots = c->num_slots;
+  v.hv = c->num_v_heads;
+  v.hk = c->num_k_heads;
+  v.dk = c->d_k;
+  v.dv = c->d_v;
+  v.cap = c->ring_cap;
+  v.state = c->state;
+  v.ring_q = c->ring_q;
+  v.ring_k = c->ring_k;
+  v.ring_v = c->ring_v;
+  v.ring_alpha = c->ring_alpha;
+  v.ring_beta = c->ring_beta;
+  v.head = c->head;
+  v.len = c->len;
+  v.sync = c->sync;
+  v.err = c->err;
+  return v;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_replay_verify(const gdn_replay_cache *c, int32_t num_reqs, const int32_t *slot_idx,
+                      int32_t draft_len, const void *q, const void *k, const void *v,
+                      const float *alpha, const float *beta, float *out, hipStream_t stream) {
+  int st = check_cache(c);
+  if (st != GDN_OK) return st;
+  if (num_reqs < 0 || num_reqs > c->num_slots) return GDN_EINVAL;
+  if (draft_len < 1 || draft_len > c->ring_cap) return GDN_EINVAL;
+  if (num_reqs == 0) return GDN_OK;
+  if (!slot_idx || !q || !k || !v || !alpha || !beta || !out) return GDN_EINVAL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(alpha, 4) ||
+      !aligned(beta, 4) || !aligned(out, 16) || !aligned(slot_idx, 4))
+    return GDN_EINVAL;
+  gdnr::VerifyArgs a;
+  a.c = view_of(c);
+  a.num_reqs = num_reqs;
+  a.draft = draft_len;
+  a.slot_idx = slot_idx;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.alpha = alpha;
+  a.beta = beta;
+  a.out = out;
+  return gdnr::launch_verify(a, c->in_dtype == GDN_F32, stream) == hipSuccess ? GDN_OK
+                                                                              : GDN_EHIP;
+}
+
+int gdn_replay_rollback(const gdn_replay_cache *c, int32_t num_reqs, const int32_t *slot_idx,
+                        int32_t draft_len, const int32_t *num_accepted, hipStream_t stream) {
+  int st = check_cache(c);
+  if (st != GDN_OK) return st;
+  if (num_reqs < 0 || num_reqs > c->num_slots) return GDN_EINVAL;
+  if (draft_len < 1 || draft_len > c->ring_cap) return GDN_EINVAL;
+  if (num_reqs == 0) return GDN_OK;
+  if (!slot_idx || !num_accepted) return GDN_EINVAL;
+  if (!aligned(slot_idx, 4) || !aligned(num_accepted, 4)) return GDN_EINVAL;
+  gdnr::RollbackArgs a;
+  a.c = view_of(c);
+  a.num_reqs = num_reqs;
+  a.draft = draft_len;
+  a.slot_idx = slot_idx;
+  a.num_accepted = num_accepted;
+  return gdnr::launch_rollback(a, stream) == hipSuccess ? GDN_OK : GDN_EHIP;
+}
+
+int gdn_replay_flush(const gdn_replay_cache *c, int32_t num_reqs, const int32_t *slot_idx,
+                     int32_t min_len, hipStream_t stream) {
+  int st = check_cache(c);
+  if (st != GDN_OK) return st;
+  if (num_reqs < 0 || num_reqs > c->num_slots) return GDN_EINVAL;
+  if (num_reqs == 0) return GDN_OK;
+  if (!slot_idx || !aligned(slot_idx, 4)) return GDN_EINVAL;
+  gdnr::FlushArgs a;
+  a.c = view_of(c);
+  a.num_reqs = num_reqs;
+  a.min_len = min_len;
+  a.slot_idx = slot_idx;
+  return gdnr::launch_flush(a, c->in_dtype == GDN_F32, stream) == hipSuccess ? GDN_OK
+                                                                             : GDN_EHIP;
+}
+
+const char *gdn_replay_strerror(int status) {
+  switch (status) {
+    case GDN_OK: return "ok";
+    case GDN_EINVAL: return "invalid argument";
+    case GDN_EUNSUPPORTED: return "unsupported configuration (head dims, dtype or ring capacity)";
+    case GDN_EHIP: return "HIP kernel launch failed";
+  }
+  return "unknown status";
+}
+
+int gdn_replay_version(void) { return GDN_REPLAY_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,33 @@
+// Device helpers shared by the replay kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdnr {
+
+// q/k/v element loads: bf16 bits (upcast is exact) or fp32.
+template <bool F32IN>
+__device__ __forceinline__ float ld_in(const void *p, int64_t i) {
+  if constexpr (F32IN) {
+    return static_cast<const float *>(p)[i];
+  } else {
+    const uint32_t b = static_cast<const uint16_t *>(p)[i];
+    return __uint_as_float(b << 16);
+  }
+}
+
+// Bit copy of one q/k/v element (ring append keeps the caller's bits).
+template <bool F32IN>
+__device__ __forceinline__ void copy_in(void *dst, int64_t di, const void *src, int64_t si) {
+  if constexpr (F32IN) {
+    static_cast<uint32_t *>(dst)[di] = static_cast<const uint32_t *>(src)[si];
+  } else {
+    static_cast<uint16_t *>(dst)[di] = static_cast<const uint16_t *>(src)[si];
+  }
+}
+
+__device__ __forceinline__ void raise_err(int32_t *err, int32_t bit) {
+  if (err) atomicOr(err, bit);
+}
+
+}  // namespace gdnr

@@ -1,0 +1,51 @@
+// Internal launch interface between the C-ABI layer (api.cpp) and the kernels.
+#pragma once
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#include "../../include/gdn_replay.h"
+
+namespace gdnr {
+
+// Everything a kernel needs about one layer's cache, passed by value.
+struct CacheView {
+  int32_t num_slots, hv, hk, dk, dv, cap;
+  float *state;
+  void *ring_q, *ring_k, *ring_v;
+  float *ring_alpha, *ring_beta;
+  int32_t *head, *len, *sync, *err;
+};
+
+struct VerifyArgs {
+  CacheView c;
+  int32_t num_reqs, draft;
+  const int32_t *slot_idx;
+  const void *q, *k, *v;
+  const float *alpha, *beta;
+  float *out;
+};
+
+struct RollbackArgs {
+  CacheView c;
+  int32_t num_reqs, draft;
+  const int32_t *slot_idx;
+  const int32_t *num_accepted;
+};
+
+struct FlushArgs {
+  CacheView c;
+  int32_t num_reqs, min_len;
+  const int32_t *slot_idx;
+};
+
+// Launchers return hipSuccess or the launch error. in_f32 selects fp32 inputs.
+hipError_t launch_verify(const VerifyArgs &a, bool in_f32, hipStream_t stream);
+hipError_t launch_rollback(const RollbackArgs &a, hipStream_t stream);
+hipError_t launch_flush(const FlushArgs &a, bool in_f32, hipStream_t stream);
+
+// head dims with a compiled kernel
+inline bool dims_supported(int dk, int dv) {
+  return dk == dv && (dk == 16 || dk == 32 || dk == 64 || dk == 128);
+}
+
+}  // namespace gdnr

@@ -1,0 +1,174 @@
+/*
+ * gdn_replay.h — C ABI of libgdnreplay.so: ReplaySSM verify / rollback / flush
+ * for Gated DeltaNet (GDN) layers under block speculative decoding, MI355X
+ * (gfx950).
+ *
+ * The scheme is the one described in "The inference stack behind OCRia"
+ * (LlamaIndex), section "Making speculative verification cheaper": a GDN layer
+ * summarises its history in a fixed-size recurrent state; instead of writing
+ * that state back per token and restoring it when a speculative token is
+ * rejected, each (request, value head) keeps a state checkpoint plus a small
+ * buffer of recent inputs. Outputs are computed from the checkpoint and the
+ * buffered inputs, the full checkpoint is rewritten only at a periodic flush,
+ * and a rejection only moves the buffer pointer so the accepted prefix is kept.
+ *
+ * The recurrence replayed is the gated delta rule (Yang et al., "Gated Delta
+ * Networks", 2025), per value head, with S of shape d_v x d_k:
+ *     S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *     o_t = S_t q_t   (output after the update).
+ * No q scaling and no normalisation happen inside: the caller passes final
+ * q, k, alpha (multiplicative decay) and beta (write strength).
+ *
+ * Memory: every pointer below is a DEVICE pointer unless stated otherwise. The
+ * caller owns all memory. The library allocates nothing, keeps no pointer after
+ * a call returns and holds no global state; calls are reentrant.
+ *
+ * Ordering: every call only enqueues work on `stream` (no host/device
+ * synchronisation). Stream order gives verify -> rollback -> flush.
+ *
+ * Errors: host-side validation is synchronous: a non-zero gdn_status is
+ * returned and nothing is enqueued. Contract violations that only the device
+ * can see (they depend on device-resident pointers) skip the offending
+ * request with no writes at all and OR a GDN_DERR_* bit into *err (a sticky
+ * word the caller clears). A failed kernel launch returns GDN_EHIP.
+ */
+#ifndef GDN_REPLAY_H
+#define GDN_REPLAY_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_REPLAY_VERSION 1
+
+typedef enum {
+  GDN_OK = 0,
+  GDN_EINVAL = -1,        /* bad argument: NULL, negative size, D outside 1..C, ... */
+  GDN_EUNSUPPORTED = -2,  /* valid but not built: head dims, dtype, ring capacity   */
+  GDN_EHIP = -3           /* the HIP runtime refused the launch                     */
+} gdn_status;
+
+typedef enum { GDN_BF16 = 0, GDN_F32 = 1 } gdn_dtype; /* dtype of q, k, v (ring and draft) */
+
+/* sticky device error bits */
+enum {
+  GDN_DERR_CAPACITY = 1,  /* verify: len + D > C;  rollback: len + a > C  */
+  GDN_DERR_ACCEPT = 2,    /* rollback: a outside [0, D]                  */
+  GDN_DERR_SLOT = 4,      /* slot index outside [0, num_slots)           */
+  GDN_DERR_POINTER = 8    /* head outside [0, C) or len outside [0, C]   */
+};
+
+/*
+ * One layer's replay cache. Host struct describing caller-owned device memory.
+ * All arrays are dense row-major.
+ *
+ *   state      [num_slots][HV][d_k][d_v] fp32. Element (i, j) holds S[j][i]:
+ *              the checkpoint is stored as H = S^T (d_k rows of d_v floats).
+ *              16-byte aligned.
+ *   ring_q     [num_slots][HK][C][d_k] in_dtype, or NULL. Written by verify
+ *              (draft append), never read: a buffered token's q is not needed
+ *              because its output was already emitted.
+ *   ring_k     [num_slots][HK][C][d_k] in_dtype.
+ *   ring_v     [num_slots][HV][C][d_v] in_dtype.
+ *   ring_alpha [num_slots][HV][C] fp32, ring_beta [num_slots][HV][C] fp32.
+ *   head       [num_slots] int32: ring position of the first committed token.
+ *   len        [num_slots] int32: committed tokens not yet in the checkpoint.
+ *              The committed tokens sit at (head + t) mod C, t < len.
+ *   sync       [num_slots] int32 arrival counters used by flush to move the
+ *              pointers after every workgroup of a slot has read them. Must be
+ *              zero when created; every completed flush leaves it zero.
+ *   err        [1] int32 sticky error word, or NULL to drop device errors.
+ *
+ * Value head h reads key head h / (HV / HK) (consecutive grouping, HV % HK == 0).
+ * Built head dims: d_k = d_v in {16, 32, 64, 128}. Ring capacity 1..256.
+ */
+typedef struct {
+  int32_t num_slots;
+  int32_t num_v_heads;  /* HV */
+  int32_t num_k_heads;  /* HK */
+  int32_t d_k;
+  int32_t d_v;
+  int32_t ring_cap;     /* C */
+  int32_t in_dtype;     /* gdn_dtype */
+  int32_t reserved;
+  float *state;
+  void *ring_q;
+  void *ring_k;
+  void *ring_v;
+  float *ring_alpha;
+  float *ring_beta;
+  int32_t *head;
+  int32_t *len;
+  int32_t *sync;
+  int32_t *err;
+} gdn_replay_cache;
+
+/*
+ * gdn_replay_verify — outputs of a draft block, computed from the checkpoint and
+ * the buffered inputs without writing the state back ("Making speculative
+ * verification cheaper", as above).
+ *
+ * For request i with slot s = slot_idx[i] and every value head h: start from
+ * the checkpoint S_c[s, h], replay the len[s] committed ring tokens in order,
+ * then draft tokens j = 0..D-1, and write
+ *     out[i][j][h][:] = S q_j   for the state after draft token j.
+ * The draft (q if ring_q != NULL, k, v, alpha, beta) is appended to ring
+ * positions (head + len + j) mod C, so that a later rollback only has to move
+ * a pointer. state, head and len are NOT modified.
+ *
+ *   num_reqs   >= 0 (0 is a no-op returning GDN_OK).
+ *   slot_idx   [num_reqs] int32, unique within the call (caller's guarantee).
+ *   draft_len  D, 1..C.
+ *   q, k       [num_reqs][D][HK][d_k] in_dtype;  v [num_reqs][D][HV][d_v] in_dtype.
+ *   alpha,beta [num_reqs][D][HV] fp32.
+ *   out        [num_reqs][D][HV][d_v] fp32; must not alias any input.
+ * Device errors: len + D > C -> CAPACITY; slot out of range -> SLOT; head or len
+ * of the slot out of range -> POINTER. The request is skipped: its out rows and
+ * its ring are left untouched.
+ */
+int gdn_replay_verify(const gdn_replay_cache *c, int32_t num_reqs, const int32_t *slot_idx,
+                      int32_t draft_len, const void *q, const void *k, const void *v,
+                      const float *alpha, const float *beta, float *out, hipStream_t stream);
+
+/*
+ * gdn_replay_rollback — keep the accepted prefix by moving the buffer pointer
+ * only ("Making speculative verification cheaper": rejection adjusts the buffer
+ * pointer, no full-state restore). The first a = num_accepted[i] tokens of the
+ * draft last appended by verify become committed: len[s] += a. Tokens after the
+ * first rejection are dropped ("Inference Engineering", chapter 5, section 5.2:
+ * a rejected draft token rejects all later ones), so a in [0, D] says it all.
+ *
+ *   num_accepted [num_reqs] int32 (device).
+ * Device errors: a outside [0, D] -> ACCEPT; len + a > C -> CAPACITY; slot out
+ * of range -> SLOT; head or len out of range -> POINTER (request skipped).
+ */
+int gdn_replay_rollback(const gdn_replay_cache *c, int32_t num_reqs, const int32_t *slot_idx,
+                        int32_t draft_len, const int32_t *num_accepted, hipStream_t stream);
+
+/*
+ * gdn_replay_flush — the periodic checkpoint update ("Making speculative
+ * verification cheaper": the full checkpoint is only updated at a periodic
+ * flush). For every slot s = slot_idx[i] with len[s] >= max(min_len, 1): fold
+ * its len[s] committed tokens into state[s] (all value heads), then
+ * head[s] = (head[s] + len[s]) mod C and len[s] = 0. Other slots are untouched
+ * (their state bytes are not rewritten).
+ *
+ * Device errors: slot out of range -> SLOT; head or len out of range -> POINTER
+ * (request skipped).
+ */
+int gdn_replay_flush(const gdn_replay_cache *c, int32_t num_reqs, const int32_t *slot_idx,
+                     int32_t min_len, hipStream_t stream);
+
+/* Human-readable text of a gdn_status (static storage). */
+const char *gdn_replay_strerror(int status);
+
+/* GDN_REPLAY_VERSION of the built library. */
+int gdn_replay_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GDN_REPLAY_H */

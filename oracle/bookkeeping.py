@@ -12,13 +12,15 @@ committed tokens not yet folded into the checkpoint), capacity C.
                 (head + len + j) mod C, j < D. Pointers unchanged.
   rollback(a):  needs 0 <= a <= D and len + a <= C; len += a.
   flush(m):     if len >= max(m, 1): head = (head + len) mod C, len = 0.
-Violations set CAPACITY=1 / ACCEPT=2 / SLOT=4 and leave the slot untouched.
+Violations set CAPACITY=1 / ACCEPT=2 / SLOT=4 / POINTER=8 (head outside [0, C)
+or len outside [0, C]) and leave the slot untouched.
 """
 from __future__ import annotations
 
 ERR_CAPACITY = 1
 ERR_ACCEPT = 2
 ERR_SLOT = 4
+ERR_POINTER = 8
 
 
 class RingPointers:
@@ -31,6 +33,9 @@ class RingPointers:
     def _ok(self, s: int) -> bool:
         if not 0 <= s < len(self.head):
             self.err |= ERR_SLOT
+            return False
+        if not (0 <= self.head[s] < self.cap and 0 <= self.len[s] <= self.cap):
+            self.err |= ERR_POINTER
             return False
         return True
 

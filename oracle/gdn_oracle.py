@@ -48,7 +48,8 @@ Readings taken where the pages are silent (each listed in the design notes)
   len >= max(min_len, 1) and sets head = (head + len) mod C, len = 0.
 * contract violations skip the request and OR a bit into a sticky error word:
   CAPACITY (len + D > C at verify, len + a > C at rollback), ACCEPT
-  (a outside [0, D]), SLOT (slot index outside [0, num_slots)).
+  (a outside [0, D]), SLOT (slot index outside [0, num_slots)), POINTER
+  (head outside [0, C) or len outside [0, C]).
 * a buffered token's q is never read.
 """
 from __future__ import annotations
@@ -58,6 +59,7 @@ import numpy as np
 ERR_CAPACITY = 1
 ERR_ACCEPT = 2
 ERR_SLOT = 4
+ERR_POINTER = 8
 
 
 def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
@@ -155,6 +157,9 @@ class ReplayOracle:
     def _slot_ok(self, s) -> bool:
         if s < 0 or s >= self.num_slots:
             self.err |= ERR_SLOT
+            return False
+        if not (0 <= self.head[s] < self.cap and 0 <= self.len[s] <= self.cap):
+            self.err |= ERR_POINTER
             return False
         return True
 

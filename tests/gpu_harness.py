@@ -1,0 +1,149 @@
+"""Runs the HIP path (through the C ABI) and the fp64 oracle side by side on the
+same seeded inputs and compares them after every call.
+
+Bars:
+  * outputs and flushed states: max |x_gpu - x_ref| <= 2e-3 * max |x_ref| over
+    the call's whole tensor (outputs) / the flushed slots' state (states);
+  * bit-exact: head, len, error word, sync counters, the whole ring (written
+    window and canaries), the state bytes of slots not flushed, and the state
+    bytes after verify / rollback (unchanged).
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+from gated_deltanet_state_replayssm_amd import synth
+from gated_deltanet_state_replayssm_amd.cache import ReplayCache, to_device
+from oracle import gdn_oracle as go
+
+TOL = 2e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def rel_err(x_gpu: np.ndarray, x_ref: np.ndarray) -> float:
+    scale = float(np.max(np.abs(x_ref))) if x_ref.size else 0.0
+    diff = float(np.max(np.abs(x_gpu.astype(np.float64) - x_ref))) if x_ref.size else 0.0
+    return diff / scale if scale > 0 else diff
+
+
+class Pair:
+    """GPU cache + oracle for one layer, driven by the same calls."""
+
+    def __init__(self, wl: synth.Workload, init: dict, with_q=True, mode="replay",
+                 oracle_slots=None):
+        self.wl = wl
+        self.gpu = ReplayCache.from_numpy(init, wl.hv, wl.hk, wl.dk, wl.dv, wl.cap,
+                                          wl.in_dtype, with_q=with_q)
+        oinit = dict(init)
+        if not with_q:
+            oinit["ring_q"] = None
+        self.orc = go.ReplayOracle(oinit, wl.hv, wl.hk, wl.dk, wl.dv, wl.cap, mode=mode)
+        # which slots the oracle follows (None = all): requests are independent,
+        # so a sample of slots can be checked at full batch size
+        self.oracle_slots = None if oracle_slots is None else set(int(s) for s in oracle_slots)
+        self.worst = {"out": 0.0, "state": 0.0}
+        self.flushed_count = 0
+
+    def _sel(self, slot_idx):
+        idx = np.arange(len(slot_idx))
+        if self.oracle_slots is None:
+            return idx
+        return np.array([i for i in idx if int(slot_idx[i]) in self.oracle_slots], dtype=np.int64)
+
+    def _check_common(self, host):
+        o = self.orc
+        slots = list(range(self.wl.num_slots)) if self.oracle_slots is None else sorted(self.oracle_slots)
+        assert np.array_equal(host["len"][slots], o.len[slots].astype(np.int32)), (host["len"], o.len)
+        assert np.array_equal(host["head"][slots], o.head[slots].astype(np.int32)), (host["head"], o.head)
+        if self.oracle_slots is None:
+            assert int(host["err"][0]) == o.err, (int(host["err"][0]), o.err)
+        assert not host["sync"].any()
+        for s in slots:
+            assert np.array_equal(host["ring_k"][s], o.ring_k[s]), f"ring_k slot {s}"
+            assert np.array_equal(host["ring_v"][s], o.ring_v[s]), f"ring_v slot {s}"
+            assert np.array_equal(host["ring_alpha"][s], o.ring_alpha[s]), f"ring_alpha slot {s}"
+            assert np.array_equal(host["ring_beta"][s], o.ring_beta[s]), f"ring_beta slot {s}"
+            if host["ring_q"] is not None:
+                assert np.array_equal(host["ring_q"][s], o.ring_q[s]), f"ring_q slot {s}"
+
+    def verify(self, slot_idx, dr, label=""):
+        say(f"  verify {label} R={len(slot_idx)} D={dr['alpha'].shape[1]}")
+        before = self.gpu.state.clone()
+        dev = {k: to_device(v) for k, v in dr.items()}
+        out = self.gpu.verify(to_device(slot_idx), dev["q"], dev["k"], dev["v"], dev["alpha"],
+                              dev["beta"])
+        torch.cuda.synchronize()
+        sel = self._sel(slot_idx)
+        ref = self.orc.verify(slot_idx[sel], *(dr[x][sel] for x in ("q", "k", "v", "alpha", "beta")))
+        got = out.cpu().numpy()[sel]
+        ok = ~np.isnan(ref).any(axis=(1, 2, 3))
+        if ok.any():
+            e = rel_err(got[ok], ref[ok])
+            self.worst["out"] = max(self.worst["out"], e)
+            assert e <= TOL, f"verify outputs: rel err {e:.3e} > {TOL}"
+        assert torch.equal(before, self.gpu.state), "verify modified the state"
+        host = self.gpu.to_numpy()
+        self._check_common(host)
+        return out
+
+    def rollback(self, slot_idx, draft_len, acc, label=""):
+        say(f"  rollback {label}")
+        before = self.gpu.state.clone()
+        self.gpu.rollback(to_device(slot_idx), draft_len, to_device(acc))
+        torch.cuda.synchronize()
+        sel = self._sel(slot_idx)
+        self.orc.rollback(slot_idx[sel], draft_len, acc[sel])
+        assert torch.equal(before, self.gpu.state), "rollback modified the state"
+        self._check_common(self.gpu.to_numpy())
+
+    def flush(self, slot_idx, min_len, label=""):
+        say(f"  flush {label} min_len={min_len}")
+        before = self.gpu.state.cpu().numpy()
+        len_before = self.orc.len.copy()
+        self.gpu.flush(to_device(slot_idx), min_len)
+        torch.cuda.synchronize()
+        sel = self._sel(slot_idx)
+        self.orc.flush(slot_idx[sel], min_len)
+        host = self.gpu.to_numpy()
+        self._check_common(host)
+        ref_state = self.orc.state_abi()
+        flushed = [int(slot_idx[i]) for i in sel
+                   if 0 <= slot_idx[i] < self.wl.num_slots and
+                   len_before[slot_idx[i]] >= max(min_len, 1) and self.orc.len[slot_idx[i]] == 0]
+        if flushed:
+            e = rel_err(host["state"][flushed], ref_state[flushed])
+            self.worst["state"] = max(self.worst["state"], e)
+            assert e <= TOL, f"flushed states: rel err {e:.3e} > {TOL}"
+            self.flushed_count += len(flushed)
+        others = [s for s in range(self.wl.num_slots) if s not in set(flushed)
+                  and (self.oracle_slots is None or s in self.oracle_slots)]
+        assert np.array_equal(host["state"][others].view(np.uint32),
+                              before[others].view(np.uint32)), "unflushed slot state changed"
+
+
+def run_schedule(wl: synth.Workload, steps: int, seed: int, layers: int = 1, with_q=True,
+                 oracle_slots=None, label=""):
+    """verify -> rollback -> flush for `steps` steps over `layers` independent caches."""
+    rng = np.random.default_rng(seed)
+    pairs = []
+    for L in range(layers):
+        init = synth.make_cache_init(wl, rng)
+        pairs.append(Pair(wl, init, with_q=with_q, oracle_slots=oracle_slots))
+    for step in range(steps):
+        slots = synth.make_slot_idx(wl, rng)
+        acc = synth.sample_accepted(wl, rng)
+        for L, p in enumerate(pairs):
+            dr = synth.make_draft(wl, rng)
+            p.verify(slots, dr, f"{label} L{L} step{step}")
+        for L, p in enumerate(pairs):
+            p.rollback(slots, wl.draft, acc, f"{label} L{L} step{step}")
+        for L, p in enumerate(pairs):
+            p.flush(slots, wl.flush_min_len, f"{label} L{L} step{step}")
+    return pairs

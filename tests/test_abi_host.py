@@ -1,0 +1,114 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and host validation rejects bad arguments synchronously,
+before any HIP call (so nothing here launches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_deltanet_state_replayssm_amd import binding as b
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "gdn_replay.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_replay_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = b.load()
+    declared = _declared_functions()
+    assert set(declared) == set(b.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_strerror():
+    assert b.version() == 1
+    for st in (b.GDN_OK, b.GDN_EINVAL, b.GDN_EUNSUPPORTED, b.GDN_EHIP):
+        assert b.load().gdn_replay_strerror(st)
+    assert b.load().gdn_replay_strerror(12345) == b"unknown status"
+
+
+FAKE = 1 << 20  # a non-NULL, 16-byte-aligned address that is never dereferenced
+
+
+def _cache(**over):
+    kw = dict(num_slots=4, num_v_heads=4, num_k_heads=2, d_k=16, d_v=16, ring_cap=8,
+              in_dtype=b.GDN_BF16, reserved=0, state=FAKE, ring_q=None, ring_k=FAKE,
+              ring_v=FAKE, ring_alpha=FAKE, ring_beta=FAKE, head=FAKE, len=FAKE, sync=FAKE,
+              err=FAKE)
+    kw.update(over)
+    return b.GdnReplayCache(**kw)
+
+
+def _verify(c, num_reqs=2, draft=4, **ptrs):
+    p = dict(slot=FAKE, q=FAKE, k=FAKE, v=FAKE, a=FAKE, be=FAKE, out=FAKE)
+    p.update(ptrs)
+    return b.verify_raw(c, num_reqs, p["slot"], draft, p["q"], p["k"], p["v"], p["a"], p["be"],
+                        p["out"], None)
+
+
+def test_null_cache_rejected():
+    lib = b.load()
+    assert lib.gdn_replay_verify(None, 1, FAKE, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == b.GDN_EINVAL
+    assert lib.gdn_replay_rollback(None, 1, FAKE, 1, FAKE, None) == b.GDN_EINVAL
+    assert lib.gdn_replay_flush(None, 1, FAKE, 1, None) == b.GDN_EINVAL
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(num_slots=0), b.GDN_EINVAL),
+    (dict(num_v_heads=0), b.GDN_EINVAL),
+    (dict(num_k_heads=3), b.GDN_EINVAL),          # 4 % 3 != 0
+    (dict(d_k=48, d_v=48), b.GDN_EUNSUPPORTED),
+    (dict(d_k=128, d_v=64), b.GDN_EUNSUPPORTED),
+    (dict(d_k=256, d_v=256), b.GDN_EUNSUPPORTED),
+    (dict(in_dtype=7), b.GDN_EINVAL),
+    (dict(ring_cap=0), b.GDN_EINVAL),
+    (dict(ring_cap=257), b.GDN_EUNSUPPORTED),
+    (dict(state=None), b.GDN_EINVAL),
+    (dict(ring_k=None), b.GDN_EINVAL),
+    (dict(sync=None), b.GDN_EINVAL),
+    (dict(len=None), b.GDN_EINVAL),
+    (dict(state=FAKE + 4), b.GDN_EINVAL),          # misaligned
+    (dict(ring_v=FAKE + 2), b.GDN_EINVAL),
+    (dict(num_v_heads=8192, num_k_heads=8192), b.GDN_EUNSUPPORTED),
+])
+def test_cache_validation(over, status):
+    c = _cache(**over)
+    assert _verify(c) == status
+    assert b.rollback_raw(c, 2, FAKE, 4, FAKE, None) == status
+    assert b.flush_raw(c, 2, FAKE, 1, None) == status
+
+
+def test_call_validation():
+    c = _cache()
+    assert _verify(c, num_reqs=-1) == b.GDN_EINVAL
+    assert _verify(c, num_reqs=5) == b.GDN_EINVAL            # more requests than slots
+    assert _verify(c, draft=0) == b.GDN_EINVAL
+    assert _verify(c, draft=9) == b.GDN_EINVAL               # D > C
+    assert _verify(c, q=None) == b.GDN_EINVAL
+    assert _verify(c, out=None) == b.GDN_EINVAL
+    assert _verify(c, out=FAKE + 4) == b.GDN_EINVAL
+    assert _verify(c, slot=FAKE + 2) == b.GDN_EINVAL
+    assert b.rollback_raw(c, 2, FAKE, 0, FAKE, None) == b.GDN_EINVAL
+    assert b.rollback_raw(c, 2, FAKE, 4, None, None) == b.GDN_EINVAL
+    assert b.flush_raw(c, -3, FAKE, 1, None) == b.GDN_EINVAL
+    assert b.flush_raw(c, 2, None, 1, None) == b.GDN_EINVAL
+
+
+def test_zero_requests_is_a_noop_without_launch():
+    c = _cache()
+    assert _verify(c, num_reqs=0, q=None, k=None) == b.GDN_OK
+    assert b.rollback_raw(c, 0, None, 4, None, None) == b.GDN_OK
+    assert b.flush_raw(c, 0, None, 1, None) == b.GDN_OK
+
+
+def test_struct_layout_matches_header():
+    # 8 int32 then 10 pointers
+    assert ctypes.sizeof(b.GdnReplayCache) == 8 * 4 + 10 * 8
+    assert b.GdnReplayCache.state.offset == 32
+    assert b.GdnReplayCache.err.offset == 32 + 9 * 8

@@ -83,8 +83,11 @@ int gdn_replay_verify(const gdn_replay_cache *c, int32_t num_reqs, const int32_t
   a.alpha = alpha;
   a.beta = beta;
   a.out = out;
-  return gdnr::launch_verify(a, c->in_dtype == GDN_F32, stream) == hipSuccess ? GDN_OK
-                                                                              : GDN_EHIP;
+  const bool f32 = c->in_dtype == GDN_F32;
+  const hipError_t e = gdnr::chunked_supported(c->d_k, c->d_v, f32)
+                           ? gdnr::launch_verify_chunked(a, stream)
+                           : gdnr::launch_verify_recurrent(a, f32, stream);
+  return e == hipSuccess ? GDN_OK : GDN_EHIP;
 }
 
 int gdn_replay_rollback(const gdn_replay_cache *c, int32_t num_reqs, const int32_t *slot_idx,
@@ -117,8 +120,11 @@ int gdn_replay_flush(const gdn_replay_cache *c, int32_t num_reqs, const int32_t 
   a.num_reqs = num_reqs;
   a.min_len = min_len;
   a.slot_idx = slot_idx;
-  return gdnr::launch_flush(a, c->in_dtype == GDN_F32, stream) == hipSuccess ? GDN_OK
-                                                                             : GDN_EHIP;
+  const bool f32 = c->in_dtype == GDN_F32;
+  const hipError_t e = gdnr::chunked_supported(c->d_k, c->d_v, f32)
+                           ? gdnr::launch_flush_chunked(a, stream)
+                           : gdnr::launch_flush_recurrent(a, f32, stream);
+  return e == hipSuccess ? GDN_OK : GDN_EHIP;
 }
 
 const char *gdn_replay_strerror(int status) {

@@ -39,9 +39,14 @@ struct FlushArgs {
 };
 
 // Launchers return hipSuccess or the launch error. in_f32 selects fp32 inputs.
-hipError_t launch_verify(const VerifyArgs &a, bool in_f32, hipStream_t stream);
+// Chunked MFMA kernels (bf16 inputs, d_k = d_v in {64, 128}):
+bool chunked_supported(int dk, int dv, bool in_f32);
+hipError_t launch_verify_chunked(const VerifyArgs &a, hipStream_t stream);
+hipError_t launch_flush_chunked(const FlushArgs &a, hipStream_t stream);
+// Token-by-token fp32 kernels (every built shape, bf16 or fp32 inputs):
+hipError_t launch_verify_recurrent(const VerifyArgs &a, bool in_f32, hipStream_t stream);
+hipError_t launch_flush_recurrent(const FlushArgs &a, bool in_f32, hipStream_t stream);
 hipError_t launch_rollback(const RollbackArgs &a, hipStream_t stream);
-hipError_t launch_flush(const FlushArgs &a, bool in_f32, hipStream_t stream);
 
 // head dims with a compiled kernel
 inline bool dims_supported(int dk, int dv) {

@@ -214,11 +214,11 @@ hipError_t dispatch_flush(const FlushArgs &a, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_verify(const VerifyArgs &a, bool in_f32, hipStream_t stream) {
+hipError_t launch_verify_recurrent(const VerifyArgs &a, bool in_f32, hipStream_t stream) {
   return in_f32 ? dispatch_verify<true>(a, stream) : dispatch_verify<false>(a, stream);
 }
 
-hipError_t launch_flush(const FlushArgs &a, bool in_f32, hipStream_t stream) {
+hipError_t launch_flush_recurrent(const FlushArgs &a, bool in_f32, hipStream_t stream) {
   return in_f32 ? dispatch_flush<true>(a, stream) : dispatch_flush<false>(a, stream);
 }
 

@@ -54,6 +54,13 @@ def load(path: str = LIB_PATH):
         return _lib
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built; run gated_deltanet_state_replayssm_amd.build")
+    # PyTorch ships its own HIP runtime. Load it first when it is installed, so
+    # that the library binds to the same runtime as the tensors it is handed
+    # (two runtimes in one process do not share devices).
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     P, I32, VP = ctypes.POINTER(GdnReplayCache), ctypes.c_int32, ctypes.c_void_p
     lib.gdn_replay_verify.argtypes = [P, I32, VP, I32, VP, VP, VP, VP, VP, VP, VP]

@@ -84,7 +84,7 @@ int gdn_replay_verify(const gdn_replay_cache *c, int32_t num_reqs, const int32_t
   a.beta = beta;
   a.out = out;
   const bool f32 = c->in_dtype == GDN_F32;
-  const hipError_t e = gdnr::chunked_supported(c->d_k, c->d_v, f32)
+  const hipError_t e = gdnr::chunked_supported(c->d_k, c->d_v, f32, draft_len)
                            ? gdnr::launch_verify_chunked(a, stream)
                            : gdnr::launch_verify_recurrent(a, f32, stream);
   return e == hipSuccess ? GDN_OK : GDN_EHIP;
@@ -121,7 +121,7 @@ int gdn_replay_flush(const gdn_replay_cache *c, int32_t num_reqs, const int32_t 
   a.min_len = min_len;
   a.slot_idx = slot_idx;
   const bool f32 = c->in_dtype == GDN_F32;
-  const hipError_t e = gdnr::chunked_supported(c->d_k, c->d_v, f32)
+  const hipError_t e = gdnr::chunked_supported(c->d_k, c->d_v, f32, 0)
                            ? gdnr::launch_flush_chunked(a, stream)
                            : gdnr::launch_flush_recurrent(a, f32, stream);
   return e == hipSuccess ? GDN_OK : GDN_EHIP;

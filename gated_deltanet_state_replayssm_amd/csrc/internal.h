@@ -39,8 +39,8 @@ struct FlushArgs {
 };
 
 // Launchers return hipSuccess or the launch error. in_f32 selects fp32 inputs.
-// Chunked MFMA kernels (bf16 inputs, d_k = d_v in {64, 128}):
-bool chunked_supported(int dk, int dv, bool in_f32);
+// Chunked MFMA kernels (bf16 inputs, d_k = d_v in {64, 128}, draft <= 32):
+bool chunked_supported(int dk, int dv, bool in_f32, int draft);
 hipError_t launch_verify_chunked(const VerifyArgs &a, hipStream_t stream);
 hipError_t launch_flush_chunked(const FlushArgs &a, hipStream_t stream);
 // Token-by-token fp32 kernels (every built shape, bf16 or fp32 inputs):

@@ -161,11 +161,11 @@ __global__ __launch_bounds__(kLanes) void flush_recurrent(FlushArgs a) {
     for (int i = 0; i < DK; ++i) st[(int64_t)i * DV + j] = H[i];
   }
 
-  // The last workgroup of this slot to arrive moves the pointers: every other
-  // workgroup has read head/len before its own arrival.
+  // The last workgroup of this slot to arrive moves the pointers. Every
+  // workgroup's head/len loads were consumed (by the branches above) before
+  // its arrival, so none can observe the update; no memory fence is needed.
   __syncthreads();
   if (lane == 0) {
-    __threadfence();
     const int total = HV * (int)gridDim.z;
     const int prev = atomicAdd(&c.sync[s], 1);
     if (prev == total - 1) {

@@ -33,6 +33,26 @@ if ROOT not in sys.path:
 
 METRIC = "GDN replay verify+flush us/layer and HBM GB/s (% roofline) at 32 reqs"
 HBM_PEAK_GBPS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "gated_deltanet_state_replayssm_amd", "csrc", "chunked.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` ("verify" / "flush") measured with rocprofv3
+    FETCH_SIZE / WRITE_SIZE (scaled by a copy of known size) and recorded in a
+    profiles/ summary, or None when no summary matches the current kernel source."""
+    import glob
+    import hashlib
+    import re
+    sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    for path in sorted(glob.glob(os.path.join(PROFILES, "*.md"))):
+        for line in open(path):
+            m = re.search(r"traffic source_sha=(\w+) verify_mb_per_launch=([\d.]+) "
+                          r"flush_mb_per_launch=([\d.]+)", line)
+            if m and m.group(1) == sha:
+                mb = float(m.group(2) if kernel == "verify" else m.group(3))
+                return int(mb * 1e6)
+    return None
 
 
 def byte_model(wl, lens_at_verify, folded):
@@ -93,6 +113,9 @@ def main():
     ap.add_argument("--workload", default="r32_hv32_hk16_d128_f16")
     ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calib", type=int, default=0,
+                    help="after the timed steps, copy a buffer of this many MiB once (a plain "
+                         "copy kernel of known size that scales the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the replay path needs no collective and this "
@@ -194,6 +217,14 @@ def main():
     f_bytes = fb / n_launch
     v_gbps = v_bytes / (us_verify * 1e-6) / 1e9
     f_gbps = f_bytes / (us_flush * 1e-6) / 1e9 if us_flush > 0 else 0.0
+    if args.copy_calib:
+        nbytes = args.copy_calib << 20
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     errs = [int(c.err.item()) for c in caches]
     assert not any(errs), f"device error bits set: {errs}"
 
@@ -227,7 +258,8 @@ def main():
         },
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(dom_gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(dom_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic(dominant),
                      "bytes_per_launch": int(dom_bytes), "us_per_launch": round(dom_us, 2)},
         "pages_context": {"b200_custom_kernel_us_per_layer": "23-24",
                           "b200_triton_us_per_layer": "72-80"},

@@ -88,12 +88,12 @@ struct Smem {
     uint16_t q[kCh][DK + kPadK];   // output chunk: queries (draft rows, zero elsewhere)
     uint16_t kt[DK][kCh + kPadT];  // folded chunk: keys, transposed
   };
-  float L[kCh][kCh + kPadF];       // decay ratios L[t][i], 0 above the diagonal
   float A[kCh][kCh + kPadF];       // beta_t L[t][i] (k_t . k_i), strictly lower;
                                    // its upper-right block is scratch for the inverse
   float Ti[kCh][kCh + kPadF];      // (I + A)^-1
   float Cm[kCh][kCh + kPadF];      // L[t][i] (q_t . k_i), lower incl. diagonal
   float gam[kCh], bet[kCh], alp[kCh];
+  float lg[kCh];                   // log2(alpha_0 ... alpha_t), each log clamped at -126
 };
 
 // 8 bf16 of a token row in k-step s order: columns 32s+4g+{0..3}, 32s+16+4g+{0..3}
@@ -329,10 +329,35 @@ struct Stage {
   }
 };
 
+// Inclusive scan over lanes 0..31 of a wave with DPP row shifts (within rows of
+// 16 lanes) and a row broadcast of lane 15 into the second row. Lanes 32..63 get
+// their own scan of lanes 32..63.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_or(float identity, float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(identity), __float_as_int(v),
+                                                    CTRL, ROW_MASK, 0xf, false));
+}
+__device__ __forceinline__ float scan32_add(float v) {
+  v += dpp_or<0x111, 0xf>(0.f, v);  // row_shr:1
+  v += dpp_or<0x112, 0xf>(0.f, v);  // row_shr:2
+  v += dpp_or<0x114, 0xf>(0.f, v);  // row_shr:4
+  v += dpp_or<0x118, 0xf>(0.f, v);  // row_shr:8
+  v += dpp_or<0x142, 0xa>(0.f, v);  // row_bcast:15 into rows 1 and 3
+  return v;
+}
+__device__ __forceinline__ float scan32_mul(float v) {
+  v *= dpp_or<0x111, 0xf>(1.f, v);
+  v *= dpp_or<0x112, 0xf>(1.f, v);
+  v *= dpp_or<0x114, 0xf>(1.f, v);
+  v *= dpp_or<0x118, 0xf>(1.f, v);
+  v *= dpp_or<0x142, 0xa>(1.f, v);
+  return v;
+}
+
 // The chunk's T x T matrices, built by one wave (no workgroup barriers inside:
 // each step reads only what this wave wrote, in program order): decay table
-// L and gamma, A = beta L o (K K^T), C = L o (Q K^T) (output chunk) and
-// (I + A)^-1. `al` is the staged alpha of token (lane % 32).
+// gamma and log2 gamma, A = beta L o (K K^T), C = L o (Q K^T) (output chunk) and
+// (I + A)^-1. al_staged is this lane's staged alpha, of token lane % 32.
 template <int DK>
 __device__ __forceinline__ void build_tt(Smem<DK> &sm, float al_staged, int lane, int g, int l16,
                                          bool out_chunk) {
@@ -340,26 +365,16 @@ __device__ __forceinline__ void build_tt(Smem<DK> &sm, float al_staged, int lane
   // Reads, arithmetic and writes of each step below are kept in separate
   // groups: LDS reads are then issued back to back instead of one by one.
   //
-  // ---- decay table: lane t builds row t, L[t][i] = alpha_{i+1} ... alpha_t,
-  // from the chunk's alphas broadcast out of lanes 0..31 (lane t staged alpha_t)
+  // ---- decays: gamma_t = alpha_0 ... alpha_t (product scan) and
+  // lg_t = log2 gamma_t (sum scan of log2 alpha, clamped at -126 so that a zero
+  // alpha stays finite); L[t][j] = alpha_{j+1} ... alpha_t = 2^(lg_t - lg_j).
   {
-    const int t = lane & (kCh - 1);
-    const uint32_t abits = __float_as_uint(al_staged);
-    float Lrow[kCh];
-    float prod = 1.f;
-#pragma unroll
-    for (int i = kCh - 1; i >= 0; --i) {
-      Lrow[i] = (i <= t) ? prod : 0.f;
-      const float ai = __uint_as_float(__builtin_amdgcn_readlane(abits, i));
-      if (i >= 1 && i <= t) prod *= ai;
-    }
-    const float g0 = prod * __uint_as_float(__builtin_amdgcn_readlane(abits, 0));
+    const float lg2a = fmaxf(__log2f(al_staged), -126.f);
+    const float lg = scan32_add(lg2a);
+    const float gm = scan32_mul(al_staged);
     if (lane < kCh) {
-#pragma unroll
-      for (int i = 0; i < kCh; i += 4)
-        *reinterpret_cast<float4 *>(&sm.L[t][i]) =
-            float4{Lrow[i], Lrow[i + 1], Lrow[i + 2], Lrow[i + 3]};
-      sm.gam[t] = g0;
+      sm.lg[lane] = lg;
+      sm.gam[lane] = gm;
     }
   }
   // ---- Gram matrices K K^T and Q K^T (exact bf16 products, fp32 sums)
@@ -393,13 +408,20 @@ __device__ __forceinline__ void build_tt(Smem<DK> &sm, float al_staged, int lane
   // ---- A = beta L o (K K^T) strictly lower, C = L o (Q K^T) lower; tile b of
   // (0,0), (1,0), (1,1) holds rows 16 ta + 4 g + i, column 16 tb + l16
   {
-    float Lv[3][4], bv[2][4];
+    float Lv[3][4], bv[2][4], lgv[2][4], lgc[2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      lgc[a] = sm.lg[16 * a + l16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lgv[a][i] = sm.lg[16 * a + 4 * g + i];
+    }
 #pragma unroll
     for (int b = 0; b < 3; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int ta = b == 0 ? 0 : 1, tb = b == 2 ? 1 : 0;
-        Lv[b][i] = sm.L[16 * ta + 4 * g + i][16 * tb + l16];
+        const int t = 16 * ta + 4 * g + i, j = 16 * tb + l16;
+        Lv[b][i] = (j <= t) ? exp2f(lgv[ta][i] - lgc[tb]) : 0.f;
       }
 #pragma unroll
     for (int a = 0; a < 2; ++a)
@@ -426,29 +448,91 @@ __device__ __forceinline__ void build_tt(Smem<DK> &sm, float al_staged, int lane
       }
   }
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  // ---- (I + A)^-1 = [[T0, 0], [T1, T2]]: diagonal 16 x 16 blocks by
-  // forward substitution (lane = block column), then T1 = -T2 (A10 T0)
+  // ---- (I + A)^-1 by recursive 2 x 2 blocking, T = [[T00, 0], [T10, T11]] with
+  // T10 = -T11 (A10 T00): 4 x 4 diagonal blocks by forward substitution, then
+  // 8 x 8 and 16 x 16 blocks on VALU, then the 32 x 32 level on MFMA. The
+  // strictly upper triangle of A (zero, never read) holds the A10 T00 products.
   {
-    const int b = (lane >> 4) & 1, cc = lane & 15, base = 16 * b;
-    float x[16];
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      float arow[16];
-#pragma unroll
-      for (int i = 0; i < t; ++i) arow[i] = sm.A[base + t][base + i];
-      float acc = 0.f;
-#pragma unroll
-      for (int i = 0; i < t; ++i) acc = fmaf(arow[i], x[i], acc);
-      x[t] = (t < cc) ? 0.f : (t == cc ? 1.f : -acc);
+    // 4 x 4 diagonal blocks q = 0..7: lane = (q, column cc)
+    const int q = (lane >> 2) & 7, cc = lane & 3, r0 = 4 * q;
+    const float a10 = sm.A[r0 + 1][r0], a20 = sm.A[r0 + 2][r0], a21 = sm.A[r0 + 2][r0 + 1];
+    const float a30 = sm.A[r0 + 3][r0], a31 = sm.A[r0 + 3][r0 + 1], a32 = sm.A[r0 + 3][r0 + 2];
+    const float x0 = cc == 0 ? 1.f : 0.f;
+    const float x1 = cc == 1 ? 1.f : (cc < 1 ? -a10 * x0 : 0.f);
+    const float x2 = cc == 2 ? 1.f : (cc < 2 ? -(a20 * x0 + a21 * x1) : 0.f);
+    const float x3 = cc == 3 ? 1.f : -(a30 * x0 + a31 * x1 + a32 * x2);
+    if (lane < 32) {
+      sm.Ti[r0][r0 + cc] = x0;
+      sm.Ti[r0 + 1][r0 + cc] = x1;
+      sm.Ti[r0 + 2][r0 + cc] = x2;
+      sm.Ti[r0 + 3][r0 + cc] = x3;
     }
-    if (lane < kCh) {
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  {
+    // 8 x 8 blocks p = 0..3: lane = (p, i, j) over the 4 x 4 lower-left block
+    const int p = lane >> 4, i = (lane >> 2) & 3, j = lane & 3, r0 = 8 * p;
+    float av[4], tv[4];
 #pragma unroll
-      for (int t = 0; t < 16; ++t) sm.Ti[base + t][base + cc] = x[t];
-      if (b == 0) {
-#pragma unroll
-        for (int t = 0; t < 16; ++t) sm.Ti[t][16 + cc] = 0.f;
-      }
+    for (int k = 0; k < 4; ++k) {
+      av[k] = sm.A[r0 + 4 + i][r0 + k];
+      tv[k] = sm.Ti[r0 + k][r0 + j];
     }
+    float m = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) m = fmaf(av[k], tv[k], m);
+    sm.A[r0 + i][r0 + 4 + j] = m;
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    float t11[4], mv[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      t11[k] = sm.Ti[r0 + 4 + i][r0 + 4 + k];
+      mv[k] = sm.A[r0 + k][r0 + 4 + j];
+    }
+    float t = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) t = fmaf(t11[k], mv[k], t);
+    sm.Ti[r0 + 4 + i][r0 + j] = -t;
+    sm.Ti[r0 + i][r0 + 4 + j] = 0.f;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  {
+    // 16 x 16 blocks b = 0, 1: lane = (b, i, j0) over the 8 x 8 lower-left block,
+    // two columns j0 and j0 + 4 per lane
+    const int b = lane >> 5, i = (lane >> 2) & 7, j0 = lane & 3, r0 = 16 * b;
+    float av[8], tv[2][8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      av[k] = sm.A[r0 + 8 + i][r0 + k];
+      tv[0][k] = sm.Ti[r0 + k][r0 + j0];
+      tv[1][k] = sm.Ti[r0 + k][r0 + j0 + 4];
+    }
+    float m0 = 0.f, m1 = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      m0 = fmaf(av[k], tv[0][k], m0);
+      m1 = fmaf(av[k], tv[1][k], m1);
+    }
+    sm.A[r0 + i][r0 + 8 + j0] = m0;
+    sm.A[r0 + i][r0 + 12 + j0] = m1;
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    float t11[8], mv[2][8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      t11[k] = sm.Ti[r0 + 8 + i][r0 + 8 + k];
+      mv[0][k] = sm.A[r0 + k][r0 + 8 + j0];
+      mv[1][k] = sm.A[r0 + k][r0 + 12 + j0];
+    }
+    float t0 = 0.f, t1 = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      t0 = fmaf(t11[k], mv[0][k], t0);
+      t1 = fmaf(t11[k], mv[1][k], t1);
+    }
+    sm.Ti[r0 + 8 + i][r0 + j0] = -t0;
+    sm.Ti[r0 + 8 + i][r0 + j0 + 4] = -t1;
+    sm.Ti[r0 + i][r0 + 8 + j0] = 0.f;
+    sm.Ti[r0 + i][r0 + 12 + j0] = 0.f;
   }
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   {
@@ -483,6 +567,7 @@ __device__ __forceinline__ void build_tt(Smem<DK> &sm, float al_staged, int lane
     T1 = mfma(al, bh, T1);
 #pragma unroll
     for (int i = 0; i < 4; ++i) sm.Ti[16 + 4 * g + i][l16] = -T1[i];
+    *reinterpret_cast<float4 *>(&sm.Ti[l16][16 + 4 * g]) = float4{0.f, 0.f, 0.f, 0.f};
   }
   
 }
@@ -635,14 +720,14 @@ template <int DK, int NT>
 __device__ __forceinline__ void fold_state(const Smem<DK> &sm, const f32x4 (&Wm)[2][NT], int g,
                                            int l16, typename Cols<NT>::F (&H)[DK / 16][4]) {
   constexpr int MT = DK / 16;
-  const float gT = sm.gam[kCh - 1];
+  const float gT = sm.gam[kCh - 1], lg31 = sm.lg[kCh - 1];
   bf16x8 wh[NT], wl[NT];
   {
     float lt[2][4];
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) lt[a][i] = sm.L[kCh - 1][16 * a + 4 * g + i];
+      for (int i = 0; i < 4; ++i) lt[a][i] = exp2f(lg31 - sm.lg[16 * a + 4 * g + i]);
     f32x4 Wp[2][NT];
 #pragma unroll
     for (int a = 0; a < 2; ++a)

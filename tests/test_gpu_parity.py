@@ -209,3 +209,27 @@ def test_checkpoint_save_restore_resume():
     ob = b.verify(slots, dr)
     assert int(a.gpu.err.item()) == 0 and int(b.gpu.err.item()) == 0
     assert torch.equal(oa, ob) and torch.equal(a.gpu.state, b.gpu.state)
+
+
+def test_degenerate_decays_and_write_strengths():
+    """alpha = 0 (full reset), alpha = 1, tiny alpha, beta = 0 and beta = 1 in the
+    committed buffer and the draft; the oracle replays them exactly."""
+    for cap in (32, 80):
+        wl = synth.Workload("dg", 4, 4, 4, 2, 128, 128, cap, 16, synth.BF16, 1, 1, "uniform",
+                            "uniform:8:15")
+        say(f"case degenerate decays C={cap}")
+        rng = np.random.default_rng(41 + cap)
+        init = synth.make_cache_init(wl, rng)
+        special = np.array([0.0, 1.0, 1e-30, 0.5], np.float32)
+        init["ring_alpha"] = rng.choice(special, init["ring_alpha"].shape).astype(np.float32)
+        init["ring_beta"] = rng.choice(np.array([0.0, 1.0, 0.3], np.float32),
+                                       init["ring_beta"].shape).astype(np.float32)
+        p = Pair(wl, init)
+        slots = synth.make_slot_idx(wl, rng)
+        dr = synth.make_draft(wl, rng)
+        dr["alpha"] = rng.choice(special, dr["alpha"].shape).astype(np.float32)
+        dr["beta"] = rng.choice(np.array([0.0, 1.0, 0.7], np.float32), dr["beta"].shape).astype(np.float32)
+        p.verify(slots, dr, "degenerate")
+        p.rollback(slots, wl.draft, synth.sample_accepted(wl, rng), "degenerate")
+        p.flush(slots, 1, "degenerate")
+        say(f"  worst {p.worst}")

@@ -81,19 +81,20 @@ struct Cols {
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-template <int DK>
+template <int DK, int DV>
 struct Smem {
   uint16_t k[kCh][DK + kPadK];     // chunk keys, token-major (bf16 bits)
   union {
     uint16_t q[kCh][DK + kPadK];   // output chunk: queries (draft rows, zero elsewhere)
     uint16_t kt[DK][kCh + kPadT];  // folded chunk: keys, transposed
   };
-  float A[kCh][kCh + kPadF];       // beta_t L[t][i] (k_t . k_i), strictly lower;
-                                   // its upper-right block is scratch for the inverse
-  float Ti[kCh][kCh + kPadF];      // (I + A)^-1
+  uint16_t v[kCh][DV + kPadK];     // chunk values, token-major (bf16 bits)
+  float T[kCh][kCh + kPadF];       // A = beta_t L[t][i] (k_t . k_i) (strictly lower),
+                                   // then (I + A)^-1 in place
   float Cm[kCh][kCh + kPadF];      // L[t][i] (q_t . k_i), lower incl. diagonal
   float gam[kCh], bet[kCh], alp[kCh];
   float lg[kCh];                   // log2(alpha_0 ... alpha_t), each log clamped at -126
+  float lgc[kCh];                  // the same, from the scan of the wave that builds Cm
 };
 
 // 8 bf16 of a token row in k-step s order: columns 32s+4g+{0..3}, 32s+16+4g+{0..3}
@@ -126,205 +127,270 @@ struct Unit {
   int r, h, s, kh, head, B, T, C;
 };
 
-// Chunk rows [t0, t0 + Treal) of the token stream (B committed ring tokens,
-// then the draft when verifying), loaded in two phases: load() issues every
-// global load into registers, store() writes LDS rows 0 .. Treal-1 (zero rows
-// after) and, for verify, appends the draft rows to the ring. The output chunk
-// (verify's last, which holds the whole draft) stages the queries; a folded
-// chunk stages the transposed keys instead. v stays in registers: each lane
-// keeps its NT columns of its 8 token rows 16 a + 4 g + i.
-// Per-workgroup base pointers of everything a chunk reads or appends (uniform,
-// computed once); rows are then addressed with 32-bit element offsets.
-struct Bases {
-  const uint16_t *rk, *rv, *dk, *dq, *dv;  // ring k / v rows; draft k / q / v rows
-  uint16_t *wk, *wq, *wv;                  // ring rows written by the append
-  const float *ra, *rb, *da, *db;          // ring / draft alpha and beta
-  float *wa, *wb;
-  int dk_stride, dv_stride, dab_stride;    // draft row strides (elements)
+// Raw buffer accesses: a uniform resource (base address and size in bytes)
+// plus a 32-bit per-lane byte offset. An offset at or past the size reads as
+// zero and drops a store, which the staging uses for rows that a resource does
+// not hold (ring vs draft rows, chunk padding) instead of branches or selects
+// of 64-bit addresses.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr uint32_t kOOB = 0x80000000u;  // an offset past every resource's end
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ Rsrc make_rsrc(const void *base, uint32_t bytes) {
+  // word 3 = 0x00020000: raw (untyped) 32-bit data, as every gfx9 buffer access
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// Cache policy bits of an access (gfx950: sc0 = 1, nt = 2, sc1 = 16).
+// kStream: data read once (the state tile, the draft).
+// kWriteOut: data written once and not read again by this kernel (outputs, ring
+// appends, the folded state). Plain write-back stores leave these lines dirty
+// in the XCD's L2, where the end-of-kernel release writes them back after all
+// the loads; written through, they reach memory while the loads still stream.
+constexpr int kStream = 2;
+constexpr int kWriteOut = 19;
+
+template <typename T, int AUX = 0>
+__device__ __forceinline__ T bload(Rsrc r, uint32_t voff, uint32_t soff = 0) {
+  if constexpr (sizeof(T) == 4)
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, AUX));
+  else if constexpr (sizeof(T) == 8)
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, AUX));
+  else
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, AUX));
+}
+
+template <typename T, int AUX = kWriteOut>
+__device__ __forceinline__ void bstore(const T &v, Rsrc r, uint32_t voff, uint32_t soff = 0) {
+  if constexpr (sizeof(T) == 4)
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, voff, soff, AUX);
+  else if constexpr (sizeof(T) == 8)
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, voff, soff, AUX);
+  else
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff, soff, AUX);
+}
+
+// One row from the ring or from the draft: a divergent pair of loads into one
+// destination (rows in neither read as zero through the draft resource). The
+// draft is read once, non-temporally; the differing policy bits also keep the
+// compiler from merging the two loads into one with a per-lane resource.
+template <typename T>
+__device__ __forceinline__ T bload_rd(bool in_ring, Rsrc ring, uint32_t roff, Rsrc draft,
+                                      uint32_t doff) {
+  T x;
+  if (in_ring)
+    x = bload<T, 0>(ring, roff);
+  else
+    x = bload<T, kStream>(draft, doff);
+  return x;
+}
+
+template <typename T>
+__device__ __forceinline__ T bits_or(const T &a, const T &b) {
+  if constexpr (sizeof(T) == 4)
+    return __builtin_bit_cast(T, __builtin_bit_cast(uint32_t, a) | __builtin_bit_cast(uint32_t, b));
+  else if constexpr (sizeof(T) == 8)
+    return __builtin_bit_cast(T, __builtin_bit_cast(u32x2, a) | __builtin_bit_cast(u32x2, b));
+  else
+    return __builtin_bit_cast(T, __builtin_bit_cast(u32x4, a) | __builtin_bit_cast(u32x4, b));
+}
+
+// The d_k x d_v state tile of one (slot, value head): lane (g, l16) of wave w
+// holds rows 16 mt + 4 g + i, columns colL .. colL + NT - 1 (colL = 16 NT w +
+// NT l16). voff = byte offset of row 4 g, column colL; the 16-row step goes in
+// the scalar offset and the row step i in the instruction's immediate.
+template <int DK, int DV, int NT>
+__device__ __forceinline__ void load_state(Rsrc st, uint32_t voff,
+                                           typename Cols<NT>::F (&H)[DK / 16][4]) {
+  typedef typename Cols<NT>::F F;
+#pragma unroll
+  for (int mt = 0; mt < DK / 16; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) H[mt][i] = bload<F, kStream>(st, voff + i * DV * 4, mt * 16 * DV * 4);
+}
+template <int DK, int DV, int NT>
+__device__ __forceinline__ void store_state(Rsrc st, uint32_t voff,
+                                            const typename Cols<NT>::F (&H)[DK / 16][4]) {
+#pragma unroll
+  for (int mt = 0; mt < DK / 16; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bstore(H[mt][i], st, voff + i * DV * 4, mt * 16 * DV * 4);
+}
+
+// Per-workgroup resources of everything a chunk reads or appends: the ring rows
+// of this (slot, key head) and (slot, value head), the draft rows of this
+// (request, key head) and (request, value head) with their row strides.
+struct Srcs {
+  Rsrc rk, rq, rv, ra, rb;  // ring k / q / v / alpha / beta (rq: appended only, may be empty)
+  Rsrc dk, dq, dv, da, db;  // draft k / q / v / alpha / beta
+  uint32_t dk_row, dv_row, dab_row;  // draft row strides in bytes
 };
 
 template <int DK, int DV>
-__device__ __forceinline__ Bases make_bases(const CacheView &c, const Unit &u,
-                                            const VerifyArgs *va, bool verify) {
+__device__ __forceinline__ Srcs make_srcs(const CacheView &c, const Unit &u, const VerifyArgs *va,
+                                          bool verify) {
   const int C = u.C, HV = c.hv, HK = c.hk;
-  Bases b;
   const int64_t kq_row0 = (int64_t)(u.s * HK + u.kh) * C;
   const int64_t vh_row0 = (int64_t)(u.s * HV + u.h) * C;
-  b.wk = static_cast<uint16_t *>(c.ring_k) + kq_row0 * DK;
-  b.wq = c.ring_q ? static_cast<uint16_t *>(c.ring_q) + kq_row0 * DK : nullptr;
-  b.wv = static_cast<uint16_t *>(c.ring_v) + vh_row0 * DV;
-  b.wa = c.ring_alpha + vh_row0;
-  b.wb = c.ring_beta + vh_row0;
-  b.rk = b.wk;
-  b.rv = b.wv;
-  b.ra = b.wa;
-  b.rb = b.wb;
-  b.dk = b.dq = b.dv = nullptr;
-  b.da = b.db = nullptr;
-  b.dk_stride = HK * DK;
-  b.dv_stride = HV * DV;
-  b.dab_stride = HV;
+  Srcs b;
+  b.rk = make_rsrc(static_cast<uint16_t *>(c.ring_k) + kq_row0 * DK, C * DK * 2);
+  b.rq = c.ring_q ? make_rsrc(static_cast<uint16_t *>(c.ring_q) + kq_row0 * DK, C * DK * 2)
+                  : make_rsrc(nullptr, 0);
+  b.rv = make_rsrc(static_cast<uint16_t *>(c.ring_v) + vh_row0 * DV, C * DV * 2);
+  b.ra = make_rsrc(c.ring_alpha + vh_row0, C * 4);
+  b.rb = make_rsrc(c.ring_beta + vh_row0, C * 4);
+  b.dk_row = HK * DK * 2;
+  b.dv_row = HV * DV * 2;
+  b.dab_row = HV * 4;
   if (verify) {
-    const int64_t d0 = (int64_t)u.r * va->draft;
-    b.dk = static_cast<const uint16_t *>(va->k) + (d0 * HK + u.kh) * DK;
-    b.dq = static_cast<const uint16_t *>(va->q) + (d0 * HK + u.kh) * DK;
-    b.dv = static_cast<const uint16_t *>(va->v) + (d0 * HV + u.h) * DV;
-    b.da = va->alpha + d0 * HV + u.h;
-    b.db = va->beta + d0 * HV + u.h;
+    const int D = va->draft;
+    const int64_t d0 = (int64_t)u.r * D;
+    const uint32_t kq_bytes = (D - 1) * b.dk_row + DK * 2;
+    b.dk = make_rsrc(static_cast<const uint16_t *>(va->k) + (d0 * HK + u.kh) * DK, kq_bytes);
+    b.dq = make_rsrc(static_cast<const uint16_t *>(va->q) + (d0 * HK + u.kh) * DK, kq_bytes);
+    b.dv = make_rsrc(static_cast<const uint16_t *>(va->v) + (d0 * HV + u.h) * DV,
+                     (D - 1) * b.dv_row + DV * 2);
+    b.da = make_rsrc(va->alpha + d0 * HV + u.h, (D - 1) * b.dab_row + 4);
+    b.db = make_rsrc(va->beta + d0 * HV + u.h, (D - 1) * b.dab_row + 4);
+  } else {
+    b.dk = b.dq = b.dv = b.da = b.db = make_rsrc(nullptr, 0);
   }
   return b;
 }
 
-// Chunk rows [t0, t0 + Treal) of the token stream (B committed ring tokens,
-// then the draft when verifying), loaded in two phases: load() issues every
-// global load into registers, store() writes LDS rows 0 .. Treal-1 (zero rows
-// after) and, for verify, appends the draft rows to the ring. The output chunk
-// (verify's last, which holds the whole draft) stages the queries; a folded
-// chunk stages the transposed keys instead. v stays in registers: each lane
-// keeps its NT columns of its 8 token rows 16 a + 4 g + i.
+// Where chunk row t (token t0 + t of the stream: B committed ring tokens, then
+// the draft when verifying) lives: its ring slot (head + token) mod C and its
+// draft index. Byte offsets for rows of the given sizes; kOOB where absent.
+template <bool VERIFY>
+struct RowAt {
+  uint32_t ring, draft, append;  // ring read, draft read, ring append (draft rows)
+  __device__ __forceinline__ RowAt(const Unit &u, int t0, int t, int Treal, uint32_t ring_row,
+                                   uint32_t draft_row) {
+    const int tok = t0 + t;
+    const bool real = t < Treal;
+    const bool in_ring = !VERIFY || tok < u.B;
+    int pos = u.head + tok;
+    pos -= pos >= u.C ? u.C : 0;  // head < C and tok < C for real rows
+    const uint32_t at = (uint32_t)pos * ring_row;
+    ring = (real && in_ring) ? at : kOOB;
+    append = (real && !in_ring) ? at : kOOB;
+    draft = (real && !in_ring) ? (uint32_t)(tok - u.B) * draft_row : kOOB;
+  }
+};
+
+// Chunk rows [t0, t0 + Treal) of the token stream. load() issues the loads of
+// k (and q), v, alpha and beta into registers; store() writes them to LDS rows
+// 0 .. 31 (rows past Treal read as zero). The output chunk (verify's last, which
+// holds the whole draft) stages the queries; a folded chunk stages the
+// transposed keys instead. append() copies the draft rows from LDS into the
+// ring once the chunk is done.
 template <int DK, int DV, int NT, bool VERIFY>
 struct Stage {
   static constexpr int THREADS = 64 * (DV / (16 * NT));
-  static constexpr int PARTS = DK / 8;  // 16-byte pieces per key row
-  static constexpr int ITER = kCh * PARTS / THREADS;
-  static_assert(kCh * PARTS % THREADS == 0, "key pieces per thread");
-  typedef typename Cols<NT>::U U;
+  static constexpr int PK = DK / 8, PV = DV / 8;  // 16-byte pieces per k / v row
+  static constexpr int IK = kCh * PK / THREADS, IV = kCh * PV / THREADS;
+  static_assert(kCh * PK % THREADS == 0 && kCh * PV % THREADS == 0, "pieces per thread");
 
-  uint4 kv[ITER], qv[ITER];
+  u32x4 kv[IK], qv[IK], vv[IV];
   float al, be;
-  U vv[2][4];
-  uint32_t ok_k, ok_q, ok_v;  // per-item "real row" bits (padding rows are zero)
-  bool ok_a;
 
-  // Chunk token t as a source: ring position (committed) or draft index.
-  // Padding rows (t >= Treal) read token 0 of the stream, which always exists,
-  // so every load below is unconditional and in bounds.
-  struct Src {
-    bool ring;
-    int pos, j;
-  };
-  __device__ __forceinline__ static Src src_of(const Unit &u, int t0, int t, int Treal) {
-    const int tok = (t < Treal) ? t0 + t : 0;
-    Src r;
-    r.ring = !VERIFY || tok < u.B;
-    const int pos = u.head + tok;
-    r.pos = pos - (pos >= u.C ? u.C : 0);
-    r.j = r.ring ? 0 : tok - u.B;
-    return r;
-  }
-
-  __device__ __forceinline__ void load(const Bases &bs, const Unit &u, int t0, int Treal,
-                                       bool out_chunk, int colL, int g) {
+  __device__ __forceinline__ void load(const Srcs &sr, const Unit &u, int t0, int Treal,
+                                       bool out_chunk) {
     const int tid = threadIdx.x;
-    ok_k = ok_q = ok_v = 0u;
 #pragma unroll
-    for (int it = 0; it < ITER; ++it) {
-      const int p = tid + it * THREADS, t = p / PARTS, part = p % PARTS;
-      const Src sr = src_of(u, t0, t, Treal);
-      const uint16_t *src = bs.rk + sr.pos * DK + part * 8;
+    for (int it = 0; it < IK; ++it) {
+      const int p = tid + it * THREADS, t = p / PK, part = p % PK;
+      const RowAt<VERIFY> at(u, t0, t, Treal, DK * 2, sr.dk_row);
       if constexpr (VERIFY) {
-        const int doff = sr.j * bs.dk_stride + part * 8;
-        if (!sr.ring) src = bs.dk + doff;
-        if (out_chunk) {
-          qv[it] = *reinterpret_cast<const uint4 *>(bs.dq + doff);
-          ok_q |= (t < Treal && !sr.ring) ? (1u << it) : 0u;
-        }
-      }
-      kv[it] = *reinterpret_cast<const uint4 *>(src);
-      ok_k |= (t < Treal) ? (1u << it) : 0u;
-    }
-    {
-      const int t = tid & (kCh - 1);
-      const Src sr = src_of(u, t0, t, Treal);
-      const float *pa = bs.ra + sr.pos, *pb = bs.rb + sr.pos;
-      if constexpr (VERIFY) {
-        if (!sr.ring) {
-          pa = bs.da + sr.j * bs.dab_stride;
-          pb = bs.db + sr.j * bs.dab_stride;
-        }
-      }
-      al = *pa;
-      be = *pb;
-      ok_a = t < Treal;
-    }
-#pragma unroll
-    for (int a = 0; a < 2; ++a) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 16 * a + 4 * g + i;
-        const Src sr = src_of(u, t0, t, Treal);
-        const uint16_t *src = bs.rv + sr.pos * DV + colL;
-        if constexpr (VERIFY) {
-          if (!sr.ring) src = bs.dv + sr.j * bs.dv_stride + colL;
-        }
-        vv[a][i] = *reinterpret_cast<const U *>(src);
-        ok_v |= (t < Treal) ? (1u << (4 * a + i)) : 0u;
-      }
-    }
-  }
-
-  // Zero the padding rows and write LDS; verify appends the draft rows it holds.
-  __device__ __forceinline__ void store(Smem<DK> &sm, const Bases &bs, const Unit &u, int t0,
-                                        int Treal, bool out_chunk, int colL, int g, int G) {
-    const int tid = threadIdx.x;
-    const uint4 zero = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int it = 0; it < ITER; ++it) {
-      const int p = tid + it * THREADS, t = p / PARTS, part = p % PARTS;
-      const uint4 k = (ok_k >> it & 1u) ? kv[it] : zero;
-      *reinterpret_cast<uint4 *>(&sm.k[t][part * 8]) = k;
-      if (out_chunk) {
-        const uint4 q = (ok_q >> it & 1u) ? qv[it] : zero;
-        *reinterpret_cast<uint4 *>(&sm.q[t][part * 8]) = q;
-        if constexpr (VERIFY) {  // one workgroup per key head appends k and q
-          if ((ok_q >> it & 1u) && u.h % G == 0) {
-            const Src sr = src_of(u, t0, t, Treal);
-            const int off = sr.pos * DK + part * 8;
-            *reinterpret_cast<uint4 *>(bs.wk + off) = k;
-            if (bs.wq) *reinterpret_cast<uint4 *>(bs.wq + off) = q;
-          }
-        }
+        kv[it] = bload_rd<u32x4>(at.ring != kOOB, sr.rk, at.ring + part * 16, sr.dk,
+                                 at.draft + part * 16);
+        // queries of committed rows are never read: those rows stay zero
+        if (out_chunk) qv[it] = bload<u32x4, kStream>(sr.dq, at.draft + part * 16);
       } else {
-        const uint32_t w[4] = {k.x, k.y, k.z, k.w};
+        kv[it] = bload<u32x4>(sr.rk, at.ring + part * 16);
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < IV; ++it) {
+      const int p = tid + it * THREADS, t = p / PV, part = p % PV;
+      const RowAt<VERIFY> at(u, t0, t, Treal, DV * 2, sr.dv_row);
+      if constexpr (VERIFY)
+        vv[it] = bload_rd<u32x4>(at.ring != kOOB, sr.rv, at.ring + part * 16, sr.dv,
+                                 at.draft + part * 16);
+      else
+        vv[it] = bload<u32x4>(sr.rv, at.ring + part * 16);
+    }
+    const int t = tid & (kCh - 1);
+    const RowAt<VERIFY> at(u, t0, t, Treal, 4, sr.dab_row);
+    if constexpr (VERIFY) {
+      al = bload_rd<float>(at.ring != kOOB, sr.ra, at.ring, sr.da, at.draft);
+      be = bload_rd<float>(at.ring != kOOB, sr.rb, at.ring, sr.db, at.draft);
+    } else {
+      al = bload<float>(sr.ra, at.ring);
+      be = bload<float>(sr.rb, at.ring);
+    }
+  }
+
+  __device__ __forceinline__ void store(Smem<DK, DV> &sm, int Treal, bool out_chunk) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int it = 0; it < IK; ++it) {
+      const int p = tid + it * THREADS, t = p / PK, part = p % PK;
+      const u32x4 k = kv[it];
+      *reinterpret_cast<u32x4 *>(&sm.k[t][part * 8]) = k;
+      if (out_chunk) {
+        *reinterpret_cast<u32x4 *>(&sm.q[t][part * 8]) = qv[it];
+      } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          sm.kt[part * 8 + 2 * e][t] = (uint16_t)(w[e] & 0xffffu);
-          sm.kt[part * 8 + 2 * e + 1][t] = (uint16_t)(w[e] >> 16);
+          sm.kt[part * 8 + 2 * e][t] = (uint16_t)(k[e] & 0xffffu);
+          sm.kt[part * 8 + 2 * e + 1][t] = (uint16_t)(k[e] >> 16);
         }
       }
     }
-    if (!ok_a) {
-      al = 1.f;  // padding rows: alpha = 1, beta = 0
-      be = 0.f;
+#pragma unroll
+    for (int it = 0; it < IV; ++it) {
+      const int p = tid + it * THREADS, t = p / PV, part = p % PV;
+      *reinterpret_cast<u32x4 *>(&sm.v[t][part * 8]) = vv[it];
     }
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (!(ok_v >> (4 * a + i) & 1u)) vv[a][i] = (U)0;
+    if ((tid & (kCh - 1)) >= Treal) al = 1.f;  // padding rows: alpha = 1, beta = 0 (read as 0)
     if (tid < kCh) {
       sm.alp[tid] = al;
       sm.bet[tid] = be;
     }
-    if constexpr (VERIFY) {
-      if (out_chunk) {
-        if (tid < kCh) {
-          const Src sr = src_of(u, t0, tid, Treal);
-          if (ok_a && !sr.ring) {
-            bs.wa[sr.pos] = al;
-            bs.wb[sr.pos] = be;
-          }
-        }
+  }
+
+  // Verify's output chunk: write the draft rows to ring slots (head + B + j) mod C,
+  // from LDS (one workgroup per key head writes k and q).
+  __device__ __forceinline__ void append(const Smem<DK, DV> &sm, const Srcs &sr, const Unit &u,
+                                         int t0, int Treal, bool kq_writer) const {
+    const int tid = threadIdx.x;
+    // Recompute the row offsets here rather than keep those of the loads alive
+    // in registers through the whole kernel: the copy of the unit is opaque to
+    // the compiler, so it cannot reuse them.
+    Unit u2 = u;
+    asm volatile("" : "+v"(u2.head));
+    if (kq_writer) {
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int t = 16 * a + 4 * g + i;
-            const Src sr = src_of(u, t0, t, Treal);
-            if ((ok_v >> (4 * a + i) & 1u) && !sr.ring)
-              *reinterpret_cast<U *>(bs.wv + sr.pos * DV + colL) = vv[a][i];
-          }
+      for (int it = 0; it < IK; ++it) {
+        const int p = tid + it * THREADS, t = p / PK, part = p % PK;
+        const RowAt<VERIFY> at(u2, t0, t, Treal, DK * 2, sr.dk_row);
+        bstore(*reinterpret_cast<const u32x4 *>(&sm.k[t][part * 8]), sr.rk, at.append + part * 16);
+        bstore(*reinterpret_cast<const u32x4 *>(&sm.q[t][part * 8]), sr.rq, at.append + part * 16);
       }
+    }
+#pragma unroll
+    for (int it = 0; it < IV; ++it) {
+      const int p = tid + it * THREADS, t = p / PV, part = p % PV;
+      const RowAt<VERIFY> at(u2, t0, t, Treal, DV * 2, sr.dv_row);
+      bstore(*reinterpret_cast<const u32x4 *>(&sm.v[t][part * 8]), sr.rv, at.append + part * 16);
+    }
+    if (tid < kCh) {
+      const RowAt<VERIFY> at(u2, t0, tid, Treal, 4, sr.dab_row);
+      bstore(sm.alp[tid], sr.ra, at.append);
+      bstore(sm.bet[tid], sr.rb, at.append);
     }
   }
 };
@@ -354,118 +420,141 @@ __device__ __forceinline__ float scan32_mul(float v) {
   return v;
 }
 
-// The chunk's T x T matrices, built by one wave (no workgroup barriers inside:
-// each step reads only what this wave wrote, in program order): decay table
-// gamma and log2 gamma, A = beta L o (K K^T), C = L o (Q K^T) (output chunk) and
-// (I + A)^-1. al_staged is this lane's staged alpha, of token lane % 32.
-template <int DK>
-__device__ __forceinline__ void build_tt(Smem<DK> &sm, float al_staged, int lane, int g, int l16,
-                                         bool out_chunk) {
-  constexpr int KS = DK / 32;
-  // Reads, arithmetic and writes of each step below are kept in separate
-  // groups: LDS reads are then issued back to back instead of one by one.
-  //
-  // ---- decays: gamma_t = alpha_0 ... alpha_t (product scan) and
-  // lg_t = log2 gamma_t (sum scan of log2 alpha, clamped at -126 so that a zero
-  // alpha stays finite); L[t][j] = alpha_{j+1} ... alpha_t = 2^(lg_t - lg_j).
-  {
-    const float lg2a = fmaxf(__log2f(al_staged), -126.f);
-    const float lg = scan32_add(lg2a);
-    const float gm = scan32_mul(al_staged);
-    if (lane < kCh) {
-      sm.lg[lane] = lg;
-      sm.gam[lane] = gm;
-    }
+// Decays of the chunk from this lane's staged alpha (token lane % 32):
+// gamma_t = alpha_0 ... alpha_t (product scan) and lg_t = log2 gamma_t (sum scan
+// of log2 alpha, each clamped at -126 so that a zero alpha stays finite), so
+// that L[t][j] = alpha_{j+1} ... alpha_t = 2^(lg_t - lg_j).
+struct Decay {
+  float lg, gm;
+};
+__device__ __forceinline__ Decay chunk_decay(float al_staged) {
+  Decay d;
+  d.lg = scan32_add(fmaxf(__log2f(al_staged), -126.f));
+  d.gm = scan32_mul(al_staged);
+  return d;
+}
+
+// 16 x 16 tiles (0,0), (1,0), (1,1) of a Gram matrix P Q^T of two 32-token row
+// blocks in LDS (exact bf16 products, fp32 sums); tile b holds rows
+// 16 ta + 4 g + i, column 16 tb + l16. One k-step's operands are live at a time.
+template <int DK, int W>
+__device__ __forceinline__ void gram3(const uint16_t (*p)[W], const uint16_t (*q)[W], int g,
+                                      int l16, f32x4 (&G)[3]) {
+#pragma unroll
+  for (int b = 0; b < 3; ++b) G[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < DK / 32; ++ks) {
+    const bf16x8 p0 = rd_row(p, l16, 32 * ks + 4 * g), p1 = rd_row(p, 16 + l16, 32 * ks + 4 * g);
+    const bf16x8 q0 = p == q ? p0 : rd_row(q, l16, 32 * ks + 4 * g);
+    const bf16x8 q1 = p == q ? p1 : rd_row(q, 16 + l16, 32 * ks + 4 * g);
+    G[0] = mfma(q0, p0, G[0]);
+    G[1] = mfma(q1, p0, G[1]);
+    G[2] = mfma(q1, p1, G[2]);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  // ---- Gram matrices K K^T and Q K^T (exact bf16 products, fp32 sums)
-  f32x4 Gm[3], Pm[3];  // tiles (0,0), (1,0), (1,1)
-  {
-    bf16x8 kr[KS][2], qr[KS][2];
+}
+
+// L[t][j] for the three tiles of gram3, zero above the diagonal
+__device__ __forceinline__ void decay_tiles(const float *lg, int g, int l16, float (&Lv)[3][4]) {
+  float lgv[2][4], lgc[2];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      kr[ks][0] = rd_row(sm.k, l16, 32 * ks + 4 * g);
-      kr[ks][1] = rd_row(sm.k, 16 + l16, 32 * ks + 4 * g);
-      if (out_chunk) {
-        qr[ks][0] = rd_row(sm.q, l16, 32 * ks + 4 * g);
-        qr[ks][1] = rd_row(sm.q, 16 + l16, 32 * ks + 4 * g);
-      }
-    }
+  for (int a = 0; a < 2; ++a) {
+    lgc[a] = lg[16 * a + l16];
 #pragma unroll
-    for (int b = 0; b < 3; ++b) Gm[b] = Pm[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      Gm[0] = mfma(kr[ks][0], kr[ks][0], Gm[0]);
-      Gm[1] = mfma(kr[ks][1], kr[ks][0], Gm[1]);
-      Gm[2] = mfma(kr[ks][1], kr[ks][1], Gm[2]);
-      if (out_chunk) {
-        Pm[0] = mfma(qr[ks][0], kr[ks][0], Pm[0]);
-        Pm[1] = mfma(qr[ks][1], kr[ks][0], Pm[1]);
-        Pm[2] = mfma(qr[ks][1], kr[ks][1], Pm[2]);
-      }
-    }
+    for (int i = 0; i < 4; ++i) lgv[a][i] = lg[16 * a + 4 * g + i];
   }
+#pragma unroll
+  for (int b = 0; b < 3; ++b)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ta = b == 0 ? 0 : 1, tb = b == 2 ? 1 : 0;
+      const int t = 16 * ta + 4 * g + i, j = 16 * tb + l16;
+      Lv[b][i] = (j <= t) ? exp2f(lgv[ta][i] - lgc[tb]) : 0.f;
+    }
+}
+
+// C = L o (Q K^T), lower triangle including the diagonal (output chunk only).
+// Built by another wave than A and its inverse, from its own decay scan (kept
+// in sm.lgc), so the two run side by side; it writes only sm.Cm and sm.lgc.
+template <int DK, int DV>
+__device__ __forceinline__ void build_c(Smem<DK, DV> &sm, float al_staged, int lane, int g, int l16) {
+  {
+    const Decay d = chunk_decay(al_staged);
+    if (lane < kCh) sm.lgc[lane] = d.lg;
+  }
+  f32x4 Pm[3];
+  gram3<DK>(sm.k, sm.q, g, l16, Pm);
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  // ---- A = beta L o (K K^T) strictly lower, C = L o (Q K^T) lower; tile b of
-  // (0,0), (1,0), (1,1) holds rows 16 ta + 4 g + i, column 16 tb + l16
-  {
-    float Lv[3][4], bv[2][4], lgv[2][4], lgc[2];
+  float Lv[3][4];
+  decay_tiles(sm.lgc, g, l16, Lv);
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      lgc[a] = sm.lg[16 * a + l16];
+  for (int b = 0; b < 4; ++b)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) lgv[a][i] = sm.lg[16 * a + 4 * g + i];
+    for (int i = 0; i < 4; ++i) {
+      const int ta = (b == 1 || b == 2) ? 1 : 0, tb = b >= 2 ? 1 : 0;
+      const int t = 16 * ta + 4 * g + i, j = 16 * tb + l16;
+      float c = 0.f;
+      if (b < 3) c = Lv[b < 3 ? b : 0][i] * Pm[b < 3 ? b : 0][i];
+      sm.Cm[t][j] = c;
     }
-#pragma unroll
-    for (int b = 0; b < 3; ++b)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ta = b == 0 ? 0 : 1, tb = b == 2 ? 1 : 0;
-        const int t = 16 * ta + 4 * g + i, j = 16 * tb + l16;
-        Lv[b][i] = (j <= t) ? exp2f(lgv[ta][i] - lgc[tb]) : 0.f;
-      }
+}
+
+// A = beta L o (K K^T) strictly lower, then (I + A)^-1 in sm.T, plus the decay vectors
+// gamma and lg, built by one wave (no workgroup barriers inside: each step reads
+// only what this wave wrote, in program order). al_staged is this lane's staged
+// alpha, of token lane % 32.
+template <int DK, int DV>
+__device__ __forceinline__ void build_tt(Smem<DK, DV> &sm, float al_staged, int lane, int g, int l16) {
+  {
+    const Decay d = chunk_decay(al_staged);
+    if (lane < kCh) {
+      sm.lg[lane] = d.lg;
+      sm.gam[lane] = d.gm;
+    }
+  }
+  f32x4 Gm[3];
+  gram3<DK>(sm.k, sm.k, g, l16, Gm);
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  {
+    float Lv[3][4], bv[2][4];
+    decay_tiles(sm.lg, g, l16, Lv);
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
       for (int i = 0; i < 4; ++i) bv[a][i] = sm.bet[16 * a + 4 * g + i];
-    float Av[4][4], Cv[4][4];
-#pragma unroll
-    for (int b = 0; b < 3; ++b)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ta = b == 0 ? 0 : 1, tb = b == 2 ? 1 : 0;
-        const int t = 16 * ta + 4 * g + i, j = 16 * tb + l16;
-        Av[b][i] = (j < t) ? bv[ta][i] * Lv[b][i] * Gm[b][i] : 0.f;
-        Cv[b][i] = (j <= t) ? Lv[b][i] * Pm[b][i] : 0.f;
-      }
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int ta = (b == 1 || b == 2) ? 1 : 0, tb = b >= 2 ? 1 : 0;
         const int t = 16 * ta + 4 * g + i, j = 16 * tb + l16;
-        sm.A[t][j] = b == 3 ? 0.f : Av[b][i];
-        if (out_chunk) sm.Cm[t][j] = b == 3 ? 0.f : Cv[b][i];
+        float v = 0.f;
+        if (b < 3 && j < t) v = bv[ta][i] * Lv[b < 3 ? b : 0][i] * Gm[b < 3 ? b : 0][i];
+        sm.T[t][j] = v;
       }
   }
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  // ---- (I + A)^-1 by recursive 2 x 2 blocking, T = [[T00, 0], [T10, T11]] with
-  // T10 = -T11 (A10 T00): 4 x 4 diagonal blocks by forward substitution, then
-  // 8 x 8 and 16 x 16 blocks on VALU, then the 32 x 32 level on MFMA. The
-  // strictly upper triangle of A (zero, never read) holds the A10 T00 products.
+  // ---- (I + A)^-1 in place, by recursive 2 x 2 blocking: T = [[T00, 0], [T10, T11]]
+  // with T10 = -T11 (A10 T00). 4 x 4 diagonal blocks by forward substitution, then
+  // 8 x 8 and 16 x 16 blocks on VALU, then the 32 x 32 level on MFMA. Each level
+  // overwrites the A10 block it has read with T10; the A10 T00 products of the
+  // VALU levels go to the (zero) upper-right block, which is cleared after use.
+  // Every step reads everything it needs before it writes (one wave, LDS
+  // accesses in program order).
   {
     // 4 x 4 diagonal blocks q = 0..7: lane = (q, column cc)
     const int q = (lane >> 2) & 7, cc = lane & 3, r0 = 4 * q;
-    const float a10 = sm.A[r0 + 1][r0], a20 = sm.A[r0 + 2][r0], a21 = sm.A[r0 + 2][r0 + 1];
-    const float a30 = sm.A[r0 + 3][r0], a31 = sm.A[r0 + 3][r0 + 1], a32 = sm.A[r0 + 3][r0 + 2];
+    const float a10 = sm.T[r0 + 1][r0], a20 = sm.T[r0 + 2][r0], a21 = sm.T[r0 + 2][r0 + 1];
+    const float a30 = sm.T[r0 + 3][r0], a31 = sm.T[r0 + 3][r0 + 1], a32 = sm.T[r0 + 3][r0 + 2];
     const float x0 = cc == 0 ? 1.f : 0.f;
     const float x1 = cc == 1 ? 1.f : (cc < 1 ? -a10 * x0 : 0.f);
     const float x2 = cc == 2 ? 1.f : (cc < 2 ? -(a20 * x0 + a21 * x1) : 0.f);
     const float x3 = cc == 3 ? 1.f : -(a30 * x0 + a31 * x1 + a32 * x2);
     if (lane < 32) {
-      sm.Ti[r0][r0 + cc] = x0;
-      sm.Ti[r0 + 1][r0 + cc] = x1;
-      sm.Ti[r0 + 2][r0 + cc] = x2;
-      sm.Ti[r0 + 3][r0 + cc] = x3;
+      sm.T[r0][r0 + cc] = x0;
+      sm.T[r0 + 1][r0 + cc] = x1;
+      sm.T[r0 + 2][r0 + cc] = x2;
+      sm.T[r0 + 3][r0 + cc] = x3;
     }
   }
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
@@ -475,25 +564,25 @@ __device__ __forceinline__ void build_tt(Smem<DK> &sm, float al_staged, int lane
     float av[4], tv[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      av[k] = sm.A[r0 + 4 + i][r0 + k];
-      tv[k] = sm.Ti[r0 + k][r0 + j];
+      av[k] = sm.T[r0 + 4 + i][r0 + k];
+      tv[k] = sm.T[r0 + k][r0 + j];
     }
     float m = 0.f;
 #pragma unroll
     for (int k = 0; k < 4; ++k) m = fmaf(av[k], tv[k], m);
-    sm.A[r0 + i][r0 + 4 + j] = m;
+    sm.T[r0 + i][r0 + 4 + j] = m;
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     float t11[4], mv[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      t11[k] = sm.Ti[r0 + 4 + i][r0 + 4 + k];
-      mv[k] = sm.A[r0 + k][r0 + 4 + j];
+      t11[k] = sm.T[r0 + 4 + i][r0 + 4 + k];
+      mv[k] = sm.T[r0 + k][r0 + 4 + j];
     }
     float t = 0.f;
 #pragma unroll
     for (int k = 0; k < 4; ++k) t = fmaf(t11[k], mv[k], t);
-    sm.Ti[r0 + 4 + i][r0 + j] = -t;
-    sm.Ti[r0 + i][r0 + 4 + j] = 0.f;
+    sm.T[r0 + 4 + i][r0 + j] = -t;
+    sm.T[r0 + i][r0 + 4 + j] = 0.f;
   }
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   {
@@ -503,9 +592,9 @@ __device__ __forceinline__ void build_tt(Smem<DK> &sm, float al_staged, int lane
     float av[8], tv[2][8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      av[k] = sm.A[r0 + 8 + i][r0 + k];
-      tv[0][k] = sm.Ti[r0 + k][r0 + j0];
-      tv[1][k] = sm.Ti[r0 + k][r0 + j0 + 4];
+      av[k] = sm.T[r0 + 8 + i][r0 + k];
+      tv[0][k] = sm.T[r0 + k][r0 + j0];
+      tv[1][k] = sm.T[r0 + k][r0 + j0 + 4];
     }
     float m0 = 0.f, m1 = 0.f;
 #pragma unroll
@@ -513,15 +602,15 @@ __device__ __forceinline__ void build_tt(Smem<DK> &sm, float al_staged, int lane
       m0 = fmaf(av[k], tv[0][k], m0);
       m1 = fmaf(av[k], tv[1][k], m1);
     }
-    sm.A[r0 + i][r0 + 8 + j0] = m0;
-    sm.A[r0 + i][r0 + 12 + j0] = m1;
+    sm.T[r0 + i][r0 + 8 + j0] = m0;
+    sm.T[r0 + i][r0 + 12 + j0] = m1;
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     float t11[8], mv[2][8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      t11[k] = sm.Ti[r0 + 8 + i][r0 + 8 + k];
-      mv[0][k] = sm.A[r0 + k][r0 + 8 + j0];
-      mv[1][k] = sm.A[r0 + k][r0 + 12 + j0];
+      t11[k] = sm.T[r0 + 8 + i][r0 + 8 + k];
+      mv[0][k] = sm.T[r0 + k][r0 + 8 + j0];
+      mv[1][k] = sm.T[r0 + k][r0 + 12 + j0];
     }
     float t0 = 0.f, t1 = 0.f;
 #pragma unroll
@@ -529,21 +618,21 @@ __device__ __forceinline__ void build_tt(Smem<DK> &sm, float al_staged, int lane
       t0 = fmaf(t11[k], mv[0][k], t0);
       t1 = fmaf(t11[k], mv[1][k], t1);
     }
-    sm.Ti[r0 + 8 + i][r0 + j0] = -t0;
-    sm.Ti[r0 + 8 + i][r0 + j0 + 4] = -t1;
-    sm.Ti[r0 + i][r0 + 8 + j0] = 0.f;
-    sm.Ti[r0 + i][r0 + 12 + j0] = 0.f;
+    sm.T[r0 + 8 + i][r0 + j0] = -t0;
+    sm.T[r0 + 8 + i][r0 + j0 + 4] = -t1;
+    sm.T[r0 + i][r0 + 8 + j0] = 0.f;
+    sm.T[r0 + i][r0 + 12 + j0] = 0.f;
   }
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   {
     // 16 x 16 products on MFMA with k = 4g + j (slots 4..7 zero), fp32
     // operands split into hi + lo bf16
     float xa[8], xb[8];
-    const float4 arow = *reinterpret_cast<const float4 *>(&sm.A[16 + l16][4 * g]);
-    const float4 trow = *reinterpret_cast<const float4 *>(&sm.Ti[16 + l16][16 + 4 * g]);
+    const float4 arow = *reinterpret_cast<const float4 *>(&sm.T[16 + l16][4 * g]);
+    const float4 trow = *reinterpret_cast<const float4 *>(&sm.T[16 + l16][16 + 4 * g]);
     float tcol[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) tcol[j] = sm.Ti[4 * g + j][l16];
+    for (int j = 0; j < 4; ++j) tcol[j] = sm.T[4 * g + j][l16];
     xa[0] = arow.x; xa[1] = arow.y; xa[2] = arow.z; xa[3] = arow.w;
 #pragma unroll
     for (int j = 0; j < 4; ++j) xb[j] = tcol[j];
@@ -566,8 +655,7 @@ __device__ __forceinline__ void build_tt(Smem<DK> &sm, float al_staged, int lane
     T1 = mfma(ah, bl, T1);
     T1 = mfma(al, bh, T1);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sm.Ti[16 + 4 * g + i][l16] = -T1[i];
-    *reinterpret_cast<float4 *>(&sm.Ti[l16][16 + 4 * g]) = float4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 4; ++i) sm.T[16 + 4 * g + i][l16] = -T1[i];
   }
   
 }
@@ -578,8 +666,8 @@ enum { kY = 1, kZ = 2 };
 // Y = K H and/or Z = Q H over d_k on MFMA, the state split into hi + lo bf16.
 // Both products share one split per k-step; a Z-only pass splits with
 // truncation so that it is never merged with (and kept alive from) a Y pass.
-template <int DK, int NT, int WHAT>
-__device__ __forceinline__ void contract(const Smem<DK> &sm,
+template <int DK, int DV, int NT, int WHAT>
+__device__ __forceinline__ void contract(const Smem<DK, DV> &sm,
                                          const typename Cols<NT>::F (&H)[DK / 16][4], int g,
                                          int l16, f32x4 (&Y)[2][NT], f32x4 (&Z)[2][NT]) {
   constexpr int KS = DK / 32;
@@ -624,20 +712,23 @@ __device__ __forceinline__ void contract(const Smem<DK> &sm,
   }
 }
 
-// X = beta (V - gamma Y), then W = (I + A)^-1 X (3-pass split product).
-template <int DK, int NT>
-__device__ __forceinline__ void solve_w(const Smem<DK> &sm, const f32x4 (&Y)[2][NT],
-                                        const typename Cols<NT>::U (&vv)[2][4], int g, int l16,
-                                        f32x4 (&Wm)[2][NT]) {
+// X = beta (V - gamma Y), then W = (I + A)^-1 X (3-pass split product); this
+// lane's v entries are rows 16 a + 4 g + i, columns colL .. colL + NT - 1.
+template <int DK, int DV, int NT>
+__device__ __forceinline__ void solve_w(const Smem<DK, DV> &sm, const f32x4 (&Y)[2][NT], int colL,
+                                        int g, int l16, f32x4 (&Wm)[2][NT]) {
+  typedef typename Cols<NT>::U U;
   bf16x8 xh[NT], xl[NT];
   {
     float be[2][4], ga[2][4];
+    U vv[2][4];
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         be[a][i] = sm.bet[16 * a + 4 * g + i];
         ga[a][i] = sm.gam[16 * a + 4 * g + i];
+        vv[a][i] = *reinterpret_cast<const U *>(&sm.v[16 * a + 4 * g + i][colL]);
       }
     f32x4 X[2][NT];
 #pragma unroll
@@ -652,7 +743,7 @@ __device__ __forceinline__ void solve_w(const Smem<DK> &sm, const f32x4 (&Y)[2][
   }
   float trow[2][8];
 #pragma unroll
-  for (int a = 0; a < 2; ++a) rd_frow(sm.Ti, 16 * a + l16, g, trow[a]);
+  for (int a = 0; a < 2; ++a) rd_frow(sm.T, 16 * a + l16, g, trow[a]);
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
     bf16x8 th, tl;
@@ -668,14 +759,22 @@ __device__ __forceinline__ void solve_w(const Smem<DK> &sm, const f32x4 (&Y)[2][
   }
 }
 
-// Draft outputs O = gamma Z + C W of chunk rows t (token t0 + t >= B, t < Treal);
-// out_base points at out[r][0][h][colL], rows D apart by tok_stride floats.
-template <int DK, int NT>
-__device__ __forceinline__ void emit_outputs(const Smem<DK> &sm, const f32x4 (&Z)[2][NT],
+// out[r][0..D-1][h][0..DV-1] of one (request, value head), rows HV DV floats apart
+__device__ __forceinline__ Rsrc out_rsrc(const VerifyArgs &va, int r, int h, int DV) {
+  const int HV = va.c.hv;
+  return make_rsrc(va.out + ((int64_t)r * va.draft * HV + h) * DV,
+                   ((va.draft - 1) * HV * DV + DV) * 4);
+}
+
+// Draft outputs O = gamma Z + C W of chunk rows t (token t0 + t >= B, t < Treal).
+// out holds out[r][0..D-1][h][*] (rows row_bytes apart); col_off = 4 colL.
+template <int DK, int DV, int NT>
+__device__ __forceinline__ void emit_outputs(const Smem<DK, DV> &sm, const f32x4 (&Z)[2][NT],
                                              const f32x4 (&Wm)[2][NT], int g, int l16, int t0,
-                                             int Treal, int B, float *out_base,
-                                             int64_t tok_stride) {
+                                             int Treal, int B, Rsrc out, uint32_t col_off,
+                                             uint32_t row_bytes) {
   typedef typename Cols<NT>::F F;
+  asm volatile("" : "+v"(B));  // recompute the row offsets here (see Stage::append)
   bf16x8 wh[NT], wl[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) tok_operand(Wm[0][nt], Wm[1][nt], wh[nt], wl[nt]);
@@ -705,19 +804,17 @@ __device__ __forceinline__ void emit_outputs(const Smem<DK> &sm, const f32x4 (&Z
     for (int i = 0; i < 4; ++i) {
       const int t = 16 * a + 4 * g + i;
       const int tok = t0 + t;
-      if (t < Treal && tok >= B) {
-        F o;
+      F o;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) o[nt] = O[nt][i];
-        *reinterpret_cast<F *>(out_base + (tok - B) * tok_stride) = o;
-      }
+      for (int nt = 0; nt < NT; ++nt) o[nt] = O[nt][i];
+      bstore(o, out, (t < Treal && tok >= B) ? (uint32_t)(tok - B) * row_bytes + col_off : kOOB);
     }
   }
 }
 
 // Fold the chunk into the state: H <- gamma_T H + K^T (L[T-1] o W).
-template <int DK, int NT>
-__device__ __forceinline__ void fold_state(const Smem<DK> &sm, const f32x4 (&Wm)[2][NT], int g,
+template <int DK, int DV, int NT>
+__device__ __forceinline__ void fold_state(const Smem<DK, DV> &sm, const f32x4 (&Wm)[2][NT], int g,
                                            int l16, typename Cols<NT>::F (&H)[DK / 16][4]) {
   constexpr int MT = DK / 16;
   const float gT = sm.gam[kCh - 1], lg31 = sm.lg[kCh - 1];
@@ -770,7 +867,7 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 2) void replay_chunked(Verif
   static_assert(DK % 32 == 0 && DV % (16 * NT) == 0 && (NT == 2 || NT == 4), "tile shape");
   static_assert(WAVES >= 1, "at least one wave");
   typedef typename Cols<NT>::F F;
-  __shared__ Smem<DK> sm;
+  __shared__ Smem<DK, DV> sm;
 
   const CacheView &c = VERIFY ? va.c : fa.c;
   const int HV = c.hv;
@@ -805,23 +902,20 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 2) void replay_chunked(Verif
   const Unit u{r, h, s, h / (HV / c.hk), head, n, T, C};
   const int nchunks = (T + kCh - 1) / kCh;
   const int T0 = T - kCh * (nchunks - 1);  // tokens in the first chunk (1..32)
-  float *st = c.state + ((int64_t)s * HV + h) * DK * DV;
+  const Rsrc st = make_rsrc(c.state + ((int64_t)s * HV + h) * DK * DV, DK * DV * 4);
+  const uint32_t st_off = (4 * g * DV + colL) * 4;
 
   // ---- first chunk's small inputs, then the whole state tile: waiting for the
   // former (loads complete in issue order) leaves the state loads in flight
-  const Bases bs = make_bases<DK, DV>(c, u, &va, VERIFY);
+  const Srcs sr = make_srcs<DK, DV>(c, u, &va, VERIFY);
   const int Ggrp = HV / c.hk;
   Stage<DK, DV, NT, VERIFY> sg;
-  sg.load(bs, u, 0, T0, VERIFY && nchunks == 1, colL, g);
+  sg.load(sr, u, 0, T0, VERIFY && nchunks == 1);
   __builtin_amdgcn_sched_barrier(0);
   // H[mt][i][nt] = state[16 mt + 4 g + i][colL + nt]: kept in the layout of the
   // loads so that nothing has to wait for them before it is used
   F H[MT][4];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      H[mt][i] = *reinterpret_cast<const F *>(st + (int64_t)(16 * mt + 4 * g + i) * DV + colL);
+  load_state<DK, DV, NT>(st, st_off, H);
   __builtin_amdgcn_sched_barrier(0);
 
   // One chunk; the first is peeled off the loop below so that the state loads
@@ -830,23 +924,28 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 2) void replay_chunked(Verif
     const int t0 = ch == 0 ? 0 : T0 + kCh * (ch - 1);
     const int Treal = ch == 0 ? T0 : kCh;
     const bool out_chunk = VERIFY && (ch + 1 == nchunks);  // holds the draft
-    if (ch > 0) sg.load(bs, u, t0, Treal, out_chunk, colL, g);
-    sg.store(sm, bs, u, t0, Treal, out_chunk, colL, g, Ggrp);
+    if (ch > 0) sg.load(sr, u, t0, Treal, out_chunk);
+    sg.store(sm, Treal, out_chunk);
     __syncthreads();
 
-    if (wave == 0) build_tt<DK>(sm, sg.al, lane, g, l16, out_chunk);
+    if (wave == 0) {
+      build_tt<DK, DV>(sm, sg.al, lane, g, l16);
+      if (WAVES == 1 && out_chunk) build_c<DK, DV>(sm, sg.al, lane, g, l16);
+    } else if (wave == 1 && out_chunk) {
+      build_c<DK, DV>(sm, sg.al, lane, g, l16);
+    }
 
     f32x4 Y[2][NT], Z[2][NT], Wm[2][NT];
-    contract<DK, NT, kY>(sm, H, g, l16, Y, Z);
+    contract<DK, DV, NT, kY>(sm, H, g, l16, Y, Z);
     __syncthreads();  // T x T matrices complete
-    solve_w<DK, NT>(sm, Y, sg.vv, g, l16, Wm);
+    solve_w<DK, DV, NT>(sm, Y, colL, g, l16, Wm);
     if (out_chunk) {
-      contract<DK, NT, kZ>(sm, H, g, l16, Y, Z);
-      emit_outputs<DK, NT>(sm, Z, Wm, g, l16, t0, Treal, u.B,
-                           va.out + ((int64_t)r * va.draft * HV + h) * DV + colL,
-                           (int64_t)HV * DV);
+      contract<DK, DV, NT, kZ>(sm, H, g, l16, Y, Z);
+      emit_outputs<DK, DV, NT>(sm, Z, Wm, g, l16, t0, Treal, u.B, out_rsrc(va, r, h, DV), colL * 4,
+                           HV * DV * 4);
+      sg.append(sm, sr, u, t0, Treal, h % Ggrp == 0);
     } else {
-      fold_state<DK, NT>(sm, Wm, g, l16, H);
+      fold_state<DK, DV, NT>(sm, Wm, g, l16, H);
     }
     __syncthreads();  // LDS is rewritten by the next chunk
   };
@@ -854,11 +953,7 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 2) void replay_chunked(Verif
   for (int ch = 1; ch < nchunks; ++ch) chunk(ch);
 
   if constexpr (!VERIFY) {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<F *>(st + (int64_t)(16 * mt + 4 * g + i) * DV + colL) = H[mt][i];
+    store_state<DK, DV, NT>(st, st_off, H);
     // The last workgroup of this slot to arrive moves the pointers. Every
     // workgroup's head/len loads were consumed (by the branches above) before
     // its arrival, so none can observe the update; no memory fence is needed
@@ -885,10 +980,11 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 2) void replay_chunked(Verif
 template <int DK, int DV, int NT, bool VERIFY>
 __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_single(VerifyArgs va,
                                                                           FlushArgs fa) {
+  constexpr int WAVES = DV / (16 * NT);
   constexpr int MT = DK / 16;
   static_assert(DK % 32 == 0 && DV % (16 * NT) == 0 && (NT == 2 || NT == 4), "tile shape");
   typedef typename Cols<NT>::F F;
-  __shared__ Smem<DK> sm;
+  __shared__ Smem<DK, DV> sm;
 
   const CacheView &c = VERIFY ? va.c : fa.c;
   const int HV = c.hv;
@@ -921,38 +1017,37 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_single(Verify
     T = n;
   }
   const Unit u{r, h, s, h / (HV / c.hk), head, n, T, C};
-  float *st = c.state + ((int64_t)s * HV + h) * DK * DV;
+  const Rsrc st = make_rsrc(c.state + ((int64_t)s * HV + h) * DK * DV, DK * DV * 4);
+  const uint32_t st_off = (4 * g * DV + colL) * 4;
 
-  const Bases bs = make_bases<DK, DV>(c, u, &va, VERIFY);
+  const Srcs sr = make_srcs<DK, DV>(c, u, &va, VERIFY);
   Stage<DK, DV, NT, VERIFY> sg;
-  sg.load(bs, u, 0, T, VERIFY, colL, g);
-  sg.store(sm, bs, u, 0, T, VERIFY, colL, g, HV / c.hk);
-  __syncthreads();
-
-  if (wave == 0) build_tt<DK>(sm, sg.al, lane, g, l16, VERIFY);
+  sg.load(sr, u, 0, T, VERIFY);
+  sg.store(sm, T, VERIFY);
   __builtin_amdgcn_sched_barrier(0);
   F H[MT][4];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      H[mt][i] = *reinterpret_cast<const F *>(st + (int64_t)(16 * mt + 4 * g + i) * DV + colL);
+  load_state<DK, DV, NT>(st, st_off, H);
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+
+  if (wave == 0) {
+    build_tt<DK, DV>(sm, sg.al, lane, g, l16);
+    if (WAVES == 1 && VERIFY) build_c<DK, DV>(sm, sg.al, lane, g, l16);
+  } else if (wave == 1 && VERIFY) {
+    build_c<DK, DV>(sm, sg.al, lane, g, l16);
+  }
   __syncthreads();  // T x T matrices complete
 
   f32x4 Y[2][NT], Z[2][NT], Wm[2][NT];
-  contract<DK, NT, VERIFY ? (kY | kZ) : kY>(sm, H, g, l16, Y, Z);
-  solve_w<DK, NT>(sm, Y, sg.vv, g, l16, Wm);
+  contract<DK, DV, NT, VERIFY ? (kY | kZ) : kY>(sm, H, g, l16, Y, Z);
+  solve_w<DK, DV, NT>(sm, Y, colL, g, l16, Wm);
   if constexpr (VERIFY) {
-    emit_outputs<DK, NT>(sm, Z, Wm, g, l16, 0, T, u.B,
-                         va.out + ((int64_t)r * va.draft * HV + h) * DV + colL,
-                         (int64_t)HV * DV);
+    emit_outputs<DK, DV, NT>(sm, Z, Wm, g, l16, 0, T, u.B, out_rsrc(va, r, h, DV), colL * 4,
+                         HV * DV * 4);
+    sg.append(sm, sr, u, 0, T, h % (HV / c.hk) == 0);
   } else {
-    fold_state<DK, NT>(sm, Wm, g, l16, H);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<F *>(st + (int64_t)(16 * mt + 4 * g + i) * DV + colL) = H[mt][i];
+    fold_state<DK, DV, NT>(sm, Wm, g, l16, H);
+    store_state<DK, DV, NT>(st, st_off, H);
     // The last workgroup of this slot to arrive moves the pointers. Every
     // workgroup's head/len loads were consumed (by the branches above) before
     // its arrival, so none can observe the update; no memory fence is needed

@@ -1,21 +1,27 @@
 """Benchmark of the GDN ReplaySSM verify / rollback / flush path on one MI355X.
 
-One step = the whole path over every GDN layer of the model for one batch:
-verify on all layers, then rollback on all layers, then flush on all layers
-(the order of a speculative decode step; "The inference stack behind OCRia",
-section "Making speculative verification cheaper": 32 concurrent requests,
-24 GDN layers). Each layer has its own cache (state + ring + pointers), so the
-24 states (1.5 GiB at 32 requests) do not fit in the 256 MB Infinity Cache and
-every verify streams its state from HBM.
+One step = the whole path over every GDN layer of the model for one batch
+("The inference stack behind OCRia", section "Making speculative verification
+cheaper": 32 concurrent requests, 24 GDN layers). Two orders of the same work
+are timed, each on its own caches built from the same seeded inputs:
 
-Timing: HIP events on the launch stream bracket the 24 verify launches, the 24
-rollback launches and the 24 flush launches of every timed step. The headline
-value is (verify time + flush time) per layer in microseconds, averaged over the
-timed steps. Algorithmic bytes come from the byte model below, evaluated with
-the actual buffer lengths of every call (tracked on the host from the known
-schedule).
+  fused     verify_flush on all layers (the periodic flush folded into the
+            verify of the next step), then rollback on all layers;
+  separate  verify on all layers, rollback on all layers, flush on all layers.
+
+Each layer has its own cache (state + ring + pointers), so the 24 states (1.5 GiB
+at 32 requests) do not fit in the 256 MB Infinity Cache and every call streams
+its state from HBM.
+
+Timing: HIP events on the launch stream bracket each group of 24 launches of
+every timed step. The headline value is the verify + flush time per layer in
+microseconds (the fused kernel's time, or verify + flush for the separate
+order), averaged over the timed steps. Algorithmic bytes come from the byte
+model below, evaluated with the actual buffer lengths of every call (tracked on
+the host from the known schedule).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+                    [--path both|fused|separate]
 """
 from __future__ import annotations
 
@@ -38,20 +44,21 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 
 def measured_traffic(kernel: str):
-    """HBM bytes per launch of `kernel` ("verify" / "flush") measured with rocprofv3
-    FETCH_SIZE / WRITE_SIZE (scaled by a copy of known size) and recorded in a
-    profiles/ summary, or None when no summary matches the current kernel source."""
+    """HBM bytes per launch of `kernel` ("verify", "flush" or "verify_flush")
+    measured with rocprofv3 FETCH_SIZE / WRITE_SIZE (scaled by a copy of known
+    size) and recorded in a profiles/ summary, or None when no summary matches
+    the current kernel source."""
     import glob
     import hashlib
     import re
     sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
     for path in sorted(glob.glob(os.path.join(PROFILES, "*.md"))):
         for line in open(path):
-            m = re.search(r"traffic source_sha=(\w+) verify_mb_per_launch=([\d.]+) "
-                          r"flush_mb_per_launch=([\d.]+)", line)
+            m = re.search(r"traffic source_sha=(\w+)((?: \w+_mb_per_launch=[\d.]+)+)", line)
             if m and m.group(1) == sha:
-                mb = float(m.group(2) if kernel == "verify" else m.group(3))
-                return int(mb * 1e6)
+                vals = dict(re.findall(r"(\w+)_mb_per_launch=([\d.]+)", m.group(2)))
+                if kernel in vals:
+                    return int(float(vals[kernel]) * 1e6)
     return None
 
 
@@ -71,6 +78,15 @@ def byte_model(wl, lens_at_verify, folded):
                + 2 * R * D * tok_draft + R * D * HV * dv * 4)
     f_bytes = sum(HV * dk * dv * 8 + int(n) * tok_ring for n in folded)
     return v_bytes, f_bytes
+
+
+def byte_model_fused(wl, lens_at_call, folded):
+    """Algorithmic HBM bytes of one layer's verify_flush call: the verify of the
+    byte model above with B_r = 0 for the folded slots, whose committed tokens
+    are read once by the fold and whose state is written once (HV*dk*dv*4 each)
+    but not read a second time."""
+    v_bytes, _ = byte_model(wl, lens_at_call, [])   # ring read of every slot's committed tokens
+    return v_bytes + len(folded) * wl.hv * wl.dk * wl.dv * 4
 
 
 def cpu_baseline(wl, seconds_budget=15.0):
@@ -112,6 +128,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="r32_hv32_hk16_d128_f16")
     ap.add_argument("--layers", type=int, default=None)
+    ap.add_argument("--path", choices=("both", "fused", "separate"), default="both")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="after the timed steps, copy a buffer of this many MiB once (a plain "
@@ -134,15 +151,12 @@ def main():
     wl = synth.WORKLOADS[args.workload]
     layers = args.layers or wl.layers
     stream = torch.cuda.current_stream()
+    paths = ("fused", "separate") if args.path == "both" else (args.path,)
 
-    rng = np.random.default_rng(synth.seed_for(wl.name, 0, 0))
-    caches = []
+    inits = []
     for L in range(layers):
-        lrng = np.random.default_rng(synth.seed_for(wl.name, L, 0))
-        init = synth.make_cache_init(wl, lrng)
-        caches.append(ReplayCache.from_numpy(init, wl.hv, wl.hk, wl.dk, wl.dv, wl.cap,
-                                             wl.in_dtype))
-    init_len = caches[0].len.cpu().numpy().astype(np.int64)
+        inits.append(synth.make_cache_init(wl, np.random.default_rng(synth.seed_for(wl.name, L, 0))))
+    init_len = inits[0]["len"].astype(np.int64)
     # two draft sets per layer, alternated: values do not change the work done
     drafts = []
     for L in range(layers):
@@ -154,69 +168,92 @@ def main():
     out = torch.empty((wl.num_reqs, wl.draft, wl.hv, wl.dv), dtype=torch.float32, device="cuda")
 
     total = args.warmup + args.steps
-    sched = []
-    lens = init_len.copy()  # identical across layers (same init lengths, same accepts)
-    for step in range(total):
-        slots = synth.make_slot_idx(wl, rng)
-        acc = synth.sample_accepted(wl, rng)
-        lv = lens[slots].copy()
-        lens[slots] += acc
-        due = lens[slots] >= max(wl.flush_min_len, 1)
-        folded = lens[slots][due].copy()
-        lens[slots[due]] = 0
-        sched.append(dict(slots=to_device(slots), acc=to_device(acc), lv=lv, folded=folded))
-    torch.cuda.synchronize()
-
+    rng = np.random.default_rng(synth.seed_for(wl.name, 0, 0))
+    steps = [(synth.make_slot_idx(wl, rng), synth.sample_accepted(wl, rng)) for _ in range(total)]
+    F = max(wl.flush_min_len, 1)
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
-    def run_step(step, marks):
-        sc = sched[step]
-        e = [ev() for _ in range(4)]
-        e[0].record(stream)
-        for L in range(layers):
-            d = drafts[L][step % 2]
-            caches[L].verify(sc["slots"], d["q"], d["k"], d["v"], d["alpha"], d["beta"], out=out)
-        e[1].record(stream)
-        for L in range(layers):
-            caches[L].rollback(sc["slots"], wl.draft, sc["acc"])
-        e[2].record(stream)
-        for L in range(layers):
-            caches[L].flush(sc["slots"], wl.flush_min_len)
-        e[3].record(stream)
-        marks.append(e)
+    def run_path(path):
+        caches = [ReplayCache.from_numpy(init, wl.hv, wl.hk, wl.dk, wl.dv, wl.cap, wl.in_dtype)
+                  for init in inits]
+        # the host's copy of the schedule (identical on every layer)
+        sched = []
+        lens = init_len.copy()
+        for slots, acc in steps:
+            lv = lens[slots].copy()
+            if path == "fused":
+                due = lv >= F
+                folded = lv[due].copy()
+                lens[slots] = np.where(due, 0, lv) + acc
+            else:
+                lens[slots] += acc
+                due = lens[slots] >= F
+                folded = lens[slots][due].copy()
+                lens[slots[due]] = 0
+            sched.append(dict(slots=to_device(slots), acc=to_device(acc), lv=lv, folded=folded))
+        torch.cuda.synchronize()
 
-    warm_marks, marks = [], []
-    for step in range(args.warmup):
-        run_step(step, warm_marks)
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for step in range(args.warmup, total):
-        run_step(step, marks)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
+        def run_step(step, marks):
+            sc = sched[step]
+            e = [ev() for _ in range(4)]
+            e[0].record(stream)
+            for L in range(layers):
+                d = drafts[L][step % 2]
+                if path == "fused":
+                    caches[L].verify_flush(sc["slots"], wl.flush_min_len, d["q"], d["k"], d["v"],
+                                           d["alpha"], d["beta"], out=out)
+                else:
+                    caches[L].verify(sc["slots"], d["q"], d["k"], d["v"], d["alpha"], d["beta"],
+                                     out=out)
+            e[1].record(stream)
+            for L in range(layers):
+                caches[L].rollback(sc["slots"], wl.draft, sc["acc"])
+            e[2].record(stream)
+            if path == "separate":
+                for L in range(layers):
+                    caches[L].flush(sc["slots"], wl.flush_min_len)
+            e[3].record(stream)
+            marks.append(e)
 
-    tv = tr = tf = 0.0
-    vb = fb = 0
-    for step in range(args.warmup, total):
-        e = marks[step - args.warmup]
-        tv += e[0].elapsed_time(e[1])
-        tr += e[1].elapsed_time(e[2])
-        tf += e[2].elapsed_time(e[3])
-        b_v, b_f = byte_model(wl, sched[step]["lv"], sched[step]["folded"])
-        vb += b_v * layers          # every layer sees the same lengths
-        fb += b_f * layers
-    K = args.steps
-    n_launch = K * layers
-    us_verify = tv * 1e3 / n_launch
-    us_rollback = tr * 1e3 / n_launch
-    us_flush = tf * 1e3 / n_launch
-    us_layer = us_verify + us_flush
-    bytes_layer = (vb + fb) / n_launch
-    gbps = bytes_layer / (us_layer * 1e-6) / 1e9
-    v_bytes = vb / n_launch
-    f_bytes = fb / n_launch
-    v_gbps = v_bytes / (us_verify * 1e-6) / 1e9
-    f_gbps = f_bytes / (us_flush * 1e-6) / 1e9 if us_flush > 0 else 0.0
+        warm_marks, marks = [], []
+        for step in range(args.warmup):
+            run_step(step, warm_marks)
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for step in range(args.warmup, total):
+            run_step(step, marks)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_start
+
+        tv = tr = tf = 0.0
+        vb = fb = 0
+        for step in range(args.warmup, total):
+            e = marks[step - args.warmup]
+            tv += e[0].elapsed_time(e[1])
+            tr += e[1].elapsed_time(e[2])
+            tf += e[2].elapsed_time(e[3])
+            if path == "fused":
+                b_v, b_f = byte_model_fused(wl, sched[step]["lv"], sched[step]["folded"]), 0
+            else:
+                b_v, b_f = byte_model(wl, sched[step]["lv"], sched[step]["folded"])
+            vb += b_v * layers          # every layer sees the same lengths
+            fb += b_f * layers
+        errs = [int(c.err.item()) for c in caches]
+        assert not any(errs), f"{path}: device error bits set: {errs}"
+        del caches
+        torch.cuda.synchronize()
+        n_launch = args.steps * layers
+        r = dict(wall=wall, us_verify=tv * 1e3 / n_launch, us_rollback=tr * 1e3 / n_launch,
+                 us_flush=tf * 1e3 / n_launch if path == "separate" else 0.0,
+                 v_bytes=vb / n_launch, f_bytes=fb / n_launch)
+        r["us_layer"] = r["us_verify"] + r["us_flush"]
+        r["bytes_layer"] = r["v_bytes"] + r["f_bytes"]
+        r["gbps"] = r["bytes_layer"] / (r["us_layer"] * 1e-6) / 1e9
+        r["v_gbps"] = r["v_bytes"] / (r["us_verify"] * 1e-6) / 1e9
+        r["f_gbps"] = r["f_bytes"] / (r["us_flush"] * 1e-6) / 1e9 if r["us_flush"] > 0 else 0.0
+        return r
+
+    res = {path: run_path(path) for path in paths}
     if args.copy_calib:
         nbytes = args.copy_calib << 20
         src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -225,20 +262,34 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    errs = [int(c.err.item()) for c in caches]
-    assert not any(errs), f"device error bits set: {errs}"
 
-    dominant = "verify" if us_verify >= us_flush else "flush"
-    dom_gbps, dom_bytes, dom_us = ((v_gbps, v_bytes, us_verify) if dominant == "verify"
-                                   else (f_gbps, f_bytes, us_flush))
+    head = res["fused"] if "fused" in res else res["separate"]
+    kernels = {}
+    if "fused" in res:
+        f = res["fused"]
+        kernels["verify_flush"] = {"us": round(f["us_verify"], 2), "bytes": int(f["v_bytes"]),
+                                   "gbps": round(f["v_gbps"], 1)}
+        kernels["rollback_fused_order"] = {"us": round(f["us_rollback"], 2)}
+    if "separate" in res:
+        sp = res["separate"]
+        kernels["verify"] = {"us": round(sp["us_verify"], 2), "bytes": int(sp["v_bytes"]),
+                             "gbps": round(sp["v_gbps"], 1)}
+        kernels["flush"] = {"us": round(sp["us_flush"], 2), "bytes": int(sp["f_bytes"]),
+                            "gbps": round(sp["f_gbps"], 1)}
+        kernels["rollback"] = {"us": round(sp["us_rollback"], 2)}
+    if "fused" in res:
+        dominant, dom = "verify_flush", kernels["verify_flush"]
+    else:
+        dominant = "verify" if kernels["verify"]["us"] >= kernels["flush"]["us"] else "flush"
+        dom = kernels[dominant]
     line = {
         "metric": METRIC,
-        "value": round(us_layer, 2),
+        "value": round(head["us_layer"], 2),
         "unit": "us/layer",
         "n_gpus": 1,
-        "steps": K,
+        "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall * 1e3 / K, 4),
+        "ms_per_step": round(head["wall"] * 1e3 / args.steps, 4),
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
@@ -247,23 +298,25 @@ def main():
         "config": {"workload": wl.name, "requests": wl.num_reqs, "v_heads": wl.hv,
                    "k_heads": wl.hk, "d_k": wl.dk, "d_v": wl.dv, "draft": wl.draft,
                    "ring_cap": wl.cap, "flush_min_len": wl.flush_min_len, "layers": layers,
-                   "inputs": wl.in_dtype, "state": "f32"},
-        "hbm_gbps": round(gbps, 1),
-        "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
-        "bytes_per_layer": int(bytes_layer),
-        "kernels": {
-            "verify": {"us": round(us_verify, 2), "bytes": int(v_bytes), "gbps": round(v_gbps, 1)},
-            "flush": {"us": round(us_flush, 2), "bytes": int(f_bytes), "gbps": round(f_gbps, 1)},
-            "rollback": {"us": round(us_rollback, 2)},
-        },
-        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(dom_gbps, 1),
+                   "inputs": wl.in_dtype, "state": "f32",
+                   "order": "fused" if "fused" in res else "separate"},
+        "hbm_gbps": round(head["gbps"], 1),
+        "hbm_frac": round(head["gbps"] / HBM_PEAK_GBPS, 4),
+        "bytes_per_layer": int(head["bytes_layer"]),
+        "kernels": kernels,
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": dom["gbps"],
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
+                     "frac": round(dom["gbps"] / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic(dominant),
-                     "bytes_per_launch": int(dom_bytes), "us_per_launch": round(dom_us, 2)},
+                     "bytes_per_launch": dom["bytes"], "us_per_launch": dom["us"]},
         "pages_context": {"b200_custom_kernel_us_per_layer": "23-24",
                           "b200_triton_us_per_layer": "72-80"},
     }
+    if "separate" in res:
+        sp = res["separate"]
+        line["separate_order"] = {"us_per_layer": round(sp["us_layer"], 2),
+                                  "hbm_gbps": round(sp["gbps"], 1),
+                                  "bytes_per_layer": int(sp["bytes_layer"])}
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(line), flush=True)

@@ -17,7 +17,7 @@ GDN_BF16, GDN_F32 = 0, 1
 GDN_DERR_CAPACITY, GDN_DERR_ACCEPT, GDN_DERR_SLOT, GDN_DERR_POINTER = 1, 2, 4, 8
 
 EXPORTED = ("gdn_replay_verify", "gdn_replay_rollback", "gdn_replay_flush",
-            "gdn_replay_strerror", "gdn_replay_version")
+            "gdn_replay_verify_flush", "gdn_replay_strerror", "gdn_replay_version")
 
 
 class GdnReplayCache(ctypes.Structure):
@@ -69,6 +69,8 @@ def load(path: str = LIB_PATH):
     lib.gdn_replay_rollback.restype = ctypes.c_int
     lib.gdn_replay_flush.argtypes = [P, I32, VP, I32, VP]
     lib.gdn_replay_flush.restype = ctypes.c_int
+    lib.gdn_replay_verify_flush.argtypes = [P, I32, VP, I32, I32, VP, VP, VP, VP, VP, VP, VP]
+    lib.gdn_replay_verify_flush.restype = ctypes.c_int
     lib.gdn_replay_strerror.argtypes = [ctypes.c_int]
     lib.gdn_replay_strerror.restype = ctypes.c_char_p
     lib.gdn_replay_version.argtypes = []
@@ -105,6 +107,12 @@ def flush_raw(cache: GdnReplayCache, num_reqs, slot_idx, min_len, stream) -> int
     return load().gdn_replay_flush(ctypes.byref(cache), num_reqs, slot_idx, min_len, stream)
 
 
+def verify_flush_raw(cache: GdnReplayCache, num_reqs, slot_idx, draft_len, min_len, q, k, v,
+                     alpha, beta, out, stream) -> int:
+    return load().gdn_replay_verify_flush(ctypes.byref(cache), num_reqs, slot_idx, draft_len,
+                                          min_len, q, k, v, alpha, beta, out, stream)
+
+
 def verify(cache, num_reqs, slot_idx, draft_len, q, k, v, alpha, beta, out, stream) -> None:
     _check("gdn_replay_verify",
            verify_raw(cache, num_reqs, slot_idx, draft_len, q, k, v, alpha, beta, out, stream))
@@ -117,6 +125,13 @@ def rollback(cache, num_reqs, slot_idx, draft_len, num_accepted, stream) -> None
 
 def flush(cache, num_reqs, slot_idx, min_len, stream) -> None:
     _check("gdn_replay_flush", flush_raw(cache, num_reqs, slot_idx, min_len, stream))
+
+
+def verify_flush(cache, num_reqs, slot_idx, draft_len, min_len, q, k, v, alpha, beta, out,
+                 stream) -> None:
+    _check("gdn_replay_verify_flush",
+           verify_flush_raw(cache, num_reqs, slot_idx, draft_len, min_len, q, k, v, alpha, beta,
+                            out, stream))
 
 
 def version() -> int:

@@ -1,4 +1,4 @@
-"""One layer's replay cache as torch device tensors, and the three calls on it.
+"""One layer's replay cache as torch device tensors, and the calls on it.
 
 Marshalling only: shapes, dtypes, devices and contiguity are checked here, the
 pointers are handed to libgdnreplay.so, and every step runs in its HIP kernels.
@@ -75,7 +75,8 @@ class ReplayCache:
         self.ring_beta = z((num_slots, hv, cap), torch.float32)
         self.head = z((num_slots,), torch.int32)
         self.len = z((num_slots,), torch.int32)
-        self.sync = z((num_slots,), torch.int32)
+        # slot counters, then the per-(slot, key head) counters of verify_flush
+        self.sync = z((num_slots * (1 + hk),), torch.int32)
         self.err = z((1,), torch.int32)
         self._struct = None
 
@@ -110,8 +111,8 @@ class ReplayCache:
                 p(self.sync), p(self.err))
         return self._struct
 
-    # -- the three calls -------------------------------------------------------
-    def verify(self, slot_idx, q, k, v, alpha, beta, out=None, stream=None) -> torch.Tensor:
+    # -- the calls ---------------------------------------------------------------
+    def _draft_args(self, slot_idx, q, k, v, alpha, beta, out):
         R = slot_idx.shape[0]
         D = alpha.shape[1] if alpha.dim() == 3 else 0
         tin = _TORCH_IN[self.in_dtype]
@@ -125,9 +126,22 @@ class ReplayCache:
         if out is None:
             out = torch.empty((R, D, self.hv, self.dv), dtype=torch.float32, device=dev)
         _need(out, "out", torch.float32, (R, D, self.hv, self.dv), dev)
+        return R, D, out
+
+    def verify(self, slot_idx, q, k, v, alpha, beta, out=None, stream=None) -> torch.Tensor:
+        R, D, out = self._draft_args(slot_idx, q, k, v, alpha, beta, out)
         binding.verify(self.struct(), R, slot_idx.data_ptr(), D, q.data_ptr(), k.data_ptr(),
                        v.data_ptr(), alpha.data_ptr(), beta.data_ptr(), out.data_ptr(),
                        _stream_handle(stream))
+        return out
+
+    def verify_flush(self, slot_idx, min_len: int, q, k, v, alpha, beta, out=None,
+                     stream=None) -> torch.Tensor:
+        """flush(min_len) then verify, in one pass (gdn_replay_verify_flush)."""
+        R, D, out = self._draft_args(slot_idx, q, k, v, alpha, beta, out)
+        binding.verify_flush(self.struct(), R, slot_idx.data_ptr(), D, int(min_len),
+                             q.data_ptr(), k.data_ptr(), v.data_ptr(), alpha.data_ptr(),
+                             beta.data_ptr(), out.data_ptr(), _stream_handle(stream))
         return out
 
     def rollback(self, slot_idx, draft_len: int, num_accepted, stream=None) -> None:

@@ -1,5 +1,5 @@
-// C-ABI entry points of libgdnreplay.so: synchronous host validation, then one
-// asynchronous launch on the caller's stream. No allocation, no host/device sync.
+// C-ABI entry points of libgdnreplay.so: synchronous host validation, then
+// asynchronous launches on the caller's stream. No allocation, no host/device sync.
 #include <stdint.h>
 
 #include "internal.h"
@@ -56,13 +56,10 @@ CacheView view_of(const gdn_replay_cache *c) {
   return v;
 }
 
-}  // namespace
-
-extern "C" {
-
-int gdn_replay_verify(const gdn_replay_cache *c, int32_t num_reqs, const int32_t *slot_idx,
-                      int32_t draft_len, const void *q, const void *k, const void *v,
-                      const float *alpha, const float *beta, float *out, hipStream_t stream) {
+// Validation and argument packing shared by verify and verify_flush.
+int verify_args(const gdn_replay_cache *c, int32_t num_reqs, const int32_t *slot_idx,
+                int32_t draft_len, const void *q, const void *k, const void *v, const float *alpha,
+                const float *beta, float *out, gdnr::VerifyArgs *a) {
   int st = check_cache(c);
   if (st != GDN_OK) return st;
   if (num_reqs < 0 || num_reqs > c->num_slots) return GDN_EINVAL;
@@ -72,22 +69,71 @@ int gdn_replay_verify(const gdn_replay_cache *c, int32_t num_reqs, const int32_t
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(alpha, 4) ||
       !aligned(beta, 4) || !aligned(out, 16) || !aligned(slot_idx, 4))
     return GDN_EINVAL;
-  gdnr::VerifyArgs a;
-  a.c = view_of(c);
-  a.num_reqs = num_reqs;
-  a.draft = draft_len;
-  a.slot_idx = slot_idx;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.alpha = alpha;
-  a.beta = beta;
-  a.out = out;
+  a->c = view_of(c);
+  a->num_reqs = num_reqs;
+  a->draft = draft_len;
+  a->slot_idx = slot_idx;
+  a->q = q;
+  a->k = k;
+  a->v = v;
+  a->alpha = alpha;
+  a->beta = beta;
+  a->out = out;
+  return GDN_OK;
+}
+
+int launch_verify(const gdn_replay_cache *c, const gdnr::VerifyArgs &a, hipStream_t stream) {
   const bool f32 = c->in_dtype == GDN_F32;
-  const hipError_t e = gdnr::chunked_supported(c->d_k, c->d_v, f32, draft_len)
+  const hipError_t e = gdnr::chunked_supported(c->d_k, c->d_v, f32, a.draft)
                            ? gdnr::launch_verify_chunked(a, stream)
                            : gdnr::launch_verify_recurrent(a, f32, stream);
   return e == hipSuccess ? GDN_OK : GDN_EHIP;
+}
+
+gdnr::FlushArgs flush_args(const gdn_replay_cache *c, int32_t num_reqs, const int32_t *slot_idx,
+                           int32_t min_len) {
+  gdnr::FlushArgs a;
+  a.c = view_of(c);
+  a.num_reqs = num_reqs;
+  a.min_len = min_len;
+  a.slot_idx = slot_idx;
+  return a;
+}
+
+int launch_flush(const gdn_replay_cache *c, const gdnr::FlushArgs &a, hipStream_t stream) {
+  const bool f32 = c->in_dtype == GDN_F32;
+  const hipError_t e = gdnr::chunked_supported(c->d_k, c->d_v, f32, 0)
+                           ? gdnr::launch_flush_chunked(a, stream)
+                           : gdnr::launch_flush_recurrent(a, f32, stream);
+  return e == hipSuccess ? GDN_OK : GDN_EHIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_replay_verify(const gdn_replay_cache *c, int32_t num_reqs, const int32_t *slot_idx,
+                      int32_t draft_len, const void *q, const void *k, const void *v,
+                      const float *alpha, const float *beta, float *out, hipStream_t stream) {
+  gdnr::VerifyArgs a;
+  const int st = verify_args(c, num_reqs, slot_idx, draft_len, q, k, v, alpha, beta, out, &a);
+  if (st != GDN_OK || num_reqs == 0) return st;
+  return launch_verify(c, a, stream);
+}
+
+int gdn_replay_verify_flush(const gdn_replay_cache *c, int32_t num_reqs, const int32_t *slot_idx,
+                            int32_t draft_len, int32_t min_len, const void *q, const void *k,
+                            const void *v, const float *alpha, const float *beta, float *out,
+                            hipStream_t stream) {
+  gdnr::VerifyArgs a;
+  const int st = verify_args(c, num_reqs, slot_idx, draft_len, q, k, v, alpha, beta, out, &a);
+  if (st != GDN_OK || num_reqs == 0) return st;
+  const bool f32 = c->in_dtype == GDN_F32;
+  if (gdnr::fused_supported(c->d_k, c->d_v, f32, draft_len, c->ring_cap))
+    return gdnr::launch_verify_flush_fused(a, min_len, stream) == hipSuccess ? GDN_OK : GDN_EHIP;
+  // Other shapes: the same result from the two calls back to back.
+  const int fs = launch_flush(c, flush_args(c, num_reqs, slot_idx, min_len), stream);
+  return fs != GDN_OK ? fs : launch_verify(c, a, stream);
 }
 
 int gdn_replay_rollback(const gdn_replay_cache *c, int32_t num_reqs, const int32_t *slot_idx,
@@ -115,16 +161,7 @@ int gdn_replay_flush(const gdn_replay_cache *c, int32_t num_reqs, const int32_t 
   if (num_reqs < 0 || num_reqs > c->num_slots) return GDN_EINVAL;
   if (num_reqs == 0) return GDN_OK;
   if (!slot_idx || !aligned(slot_idx, 4)) return GDN_EINVAL;
-  gdnr::FlushArgs a;
-  a.c = view_of(c);
-  a.num_reqs = num_reqs;
-  a.min_len = min_len;
-  a.slot_idx = slot_idx;
-  const bool f32 = c->in_dtype == GDN_F32;
-  const hipError_t e = gdnr::chunked_supported(c->d_k, c->d_v, f32, 0)
-                           ? gdnr::launch_flush_chunked(a, stream)
-                           : gdnr::launch_flush_recurrent(a, f32, stream);
-  return e == hipSuccess ? GDN_OK : GDN_EHIP;
+  return launch_flush(c, flush_args(c, num_reqs, slot_idx, min_len), stream);
 }
 
 const char *gdn_replay_strerror(int status) {

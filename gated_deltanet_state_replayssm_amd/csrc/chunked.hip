@@ -741,13 +741,12 @@ __device__ __forceinline__ void solve_w(const Smem<DK, DV> &sm, const f32x4 (&Y)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) tok_operand(X[0][nt], X[1][nt], xh[nt], xl[nt]);
   }
-  float trow[2][8];
-#pragma unroll
-  for (int a = 0; a < 2; ++a) rd_frow(sm.T, 16 * a + l16, g, trow[a]);
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
+    float trow[8];
+    rd_frow(sm.T, 16 * a + l16, g, trow);
     bf16x8 th, tl;
-    split8(trow[a], th, tl);
+    split8(trow, th, tl);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -1064,6 +1063,121 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_single(Verify
   }
 }
 
+// Flush fused into verify, ring capacity <= 32. A slot with len >= max(min_len,
+// 1) first folds its len committed tokens into the checkpoint, writes it back
+// and moves its pointers (head += len, len = 0), then verifies the draft from
+// the new checkpoint; other slots verify as replay_single does. One state read
+// serves both, and a due slot's state is written once.
+//
+// The draft is appended at (new head + j) mod C, which may wrap onto committed
+// key rows that the other value heads of the same key head are still reading
+// for their fold. So each workgroup of a due slot counts itself in at
+// sync[num_slots + s HK + kh] once its fold inputs are staged, and the last
+// one of the key head's group appends k and q (the others have read by then).
+template <int DK, int DV, int NT>
+__global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyArgs va,
+                                                                         int min_len) {
+  constexpr int WAVES = DV / (16 * NT);
+  constexpr int MT = DK / 16;
+  static_assert(DK % 32 == 0 && DV % (16 * NT) == 0 && (NT == 2 || NT == 4), "tile shape");
+  typedef typename Cols<NT>::F F;
+  __shared__ Smem<DK, DV> sm;
+  __shared__ int group_rank;
+
+  const CacheView &c = va.c;
+  const int HV = c.hv, G = HV / c.hk;
+  const int r = blockIdx.x / HV, h = blockIdx.x % HV;
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+  const int g = lane >> 4, l16 = lane & 15;
+  const int colL = wave * 16 * NT + NT * l16;
+  const bool lead = (h == 0 && tid == 0);
+
+  const int s = va.slot_idx[r];
+  if (s < 0 || s >= c.num_slots) {
+    if (lead) raise_err(c.err, GDN_DERR_SLOT);
+    return;
+  }
+  const int C = c.cap;
+  const int head = c.head[s], n = c.len[s];
+  if (head < 0 || head >= C || n < 0 || n > C) {
+    if (lead) raise_err(c.err, GDN_DERR_POINTER);
+    return;
+  }
+  const bool due = n >= max(min_len, 1);
+  if (!due && n + va.draft > C) {
+    if (lead) raise_err(c.err, GDN_DERR_CAPACITY);
+    return;
+  }
+  const int kh = h / G;
+  const Rsrc st = make_rsrc(c.state + ((int64_t)s * HV + h) * DK * DV, DK * DV * 4);
+  const uint32_t st_off = (4 * g * DV + colL) * 4;
+  int32_t *group_ctr = c.sync + c.num_slots + (int64_t)s * c.hk + kh;
+
+  F H[MT][4];
+  int hd = head, B = n;  // ring start and committed count of the verify below
+  if (due) {
+    // ---- flush: fold the n committed tokens
+    const Unit uf{r, h, s, kh, head, n, n, C};
+    const Srcs sf = make_srcs<DK, DV>(c, uf, nullptr, false);
+    Stage<DK, DV, NT, false> sgf;
+    sgf.load(sf, uf, 0, n, false);
+    sgf.store(sm, n, false);
+    __builtin_amdgcn_sched_barrier(0);
+    load_state<DK, DV, NT>(st, st_off, H);
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();  // the committed rows are read (and staged)
+    if (tid == 0) group_rank = atomicAdd(group_ctr, 1);
+    if (wave == 0) build_tt<DK, DV>(sm, sgf.al, lane, g, l16);
+    __syncthreads();
+    f32x4 Y[2][NT], Z[2][NT], Wm[2][NT];
+    contract<DK, DV, NT, kY>(sm, H, g, l16, Y, Z);
+    solve_w<DK, DV, NT>(sm, Y, colL, g, l16, Wm);
+    fold_state<DK, DV, NT>(sm, Wm, g, l16, H);
+    store_state<DK, DV, NT>(st, st_off, H);
+    hd = head + n - (head + n >= C ? C : 0);
+    B = 0;
+    __syncthreads();  // LDS is staged again below
+  }
+
+  // ---- verify the draft from checkpoint H plus B committed tokens at hd
+  const Unit u{r, h, s, kh, hd, B, B + va.draft, C};
+  const Srcs sr = make_srcs<DK, DV>(c, u, &va, true);
+  Stage<DK, DV, NT, true> sg;
+  sg.load(sr, u, 0, u.T, true);
+  sg.store(sm, u.T, true);
+  if (!due) {
+    __builtin_amdgcn_sched_barrier(0);
+    load_state<DK, DV, NT>(st, st_off, H);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __syncthreads();
+  if (wave == 0) {
+    build_tt<DK, DV>(sm, sg.al, lane, g, l16);
+    if (WAVES == 1) build_c<DK, DV>(sm, sg.al, lane, g, l16);
+  } else if (wave == 1) {
+    build_c<DK, DV>(sm, sg.al, lane, g, l16);
+  }
+  __syncthreads();  // T x T matrices complete
+
+  f32x4 Y[2][NT], Z[2][NT], Wm[2][NT];
+  contract<DK, DV, NT, kY | kZ>(sm, H, g, l16, Y, Z);
+  solve_w<DK, DV, NT>(sm, Y, colL, g, l16, Wm);
+  emit_outputs<DK, DV, NT>(sm, Z, Wm, g, l16, 0, u.T, u.B, out_rsrc(va, r, h, DV), colL * 4,
+                           HV * DV * 4);
+  const bool kq_writer = due ? group_rank == G - 1 : h % G == 0;
+  sg.append(sm, sr, u, 0, u.T, kq_writer);
+  if (due && tid == 0) {
+    if (kq_writer) *group_ctr = 0;  // every member has counted in
+    // Last workgroup of the slot moves the pointers (see replay_single).
+    const int prev = atomicAdd(&c.sync[s], 1);
+    if (prev == HV - 1) {
+      c.head[s] = hd;
+      c.len[s] = 0;
+      c.sync[s] = 0;
+    }
+  }
+}
+
 template <int DK, int DV, bool VERIFY>
 hipError_t launch_t(const VerifyArgs &va, const FlushArgs &fa, int num_reqs, int hv, int cap,
                     hipStream_t stream) {
@@ -1077,6 +1191,25 @@ hipError_t launch_t(const VerifyArgs &va, const FlushArgs &fa, int num_reqs, int
 }
 
 }  // namespace
+
+hipError_t launch_verify_flush_fused(const VerifyArgs &a, int min_len, hipStream_t stream) {
+  constexpr int NT = 2;
+  const dim3 grid(a.num_reqs * a.c.hv);
+  if (a.c.dk == 128) {
+    hipLaunchKernelGGL((replay_fused<128, 128, NT>), grid, dim3(64 * (128 / (16 * NT))), 0, stream,
+                       a, min_len);
+  } else if (a.c.dk == 64) {
+    hipLaunchKernelGGL((replay_fused<64, 64, NT>), grid, dim3(64 * (64 / (16 * NT))), 0, stream,
+                       a, min_len);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+bool fused_supported(int dk, int dv, bool in_f32, int draft, int cap) {
+  return chunked_supported(dk, dv, in_f32, draft) && cap <= kCh;
+}
 
 bool chunked_supported(int dk, int dv, bool in_f32, int draft) {
   return !in_f32 && dk == dv && (dk == 64 || dk == 128) && draft <= kCh;

@@ -24,7 +24,8 @@
  * a call returns and holds no global state; calls are reentrant.
  *
  * Ordering: every call only enqueues work on `stream` (no host/device
- * synchronisation). Stream order gives verify -> rollback -> flush.
+ * synchronisation). Stream order gives verify -> rollback -> flush, or
+ * verify_flush -> rollback with the flush folded into the next step's verify.
  *
  * Errors: host-side validation is synchronous: a non-zero gdn_status is
  * returned and nothing is enqueued. Contract violations that only the device
@@ -42,7 +43,7 @@
 extern "C" {
 #endif
 
-#define GDN_REPLAY_VERSION 1
+#define GDN_REPLAY_VERSION 2
 
 typedef enum {
   GDN_OK = 0,
@@ -77,9 +78,12 @@ enum {
  *   head       [num_slots] int32: ring position of the first committed token.
  *   len        [num_slots] int32: committed tokens not yet in the checkpoint.
  *              The committed tokens sit at (head + t) mod C, t < len.
- *   sync       [num_slots] int32 arrival counters used by flush to move the
- *              pointers after every workgroup of a slot has read them. Must be
- *              zero when created; every completed flush leaves it zero.
+ *   sync       int32 arrival counters, zero when created; every completed call
+ *              leaves them zero. sync[s] (s < num_slots) lets flush move the
+ *              pointers after every workgroup of slot s has read them. Calls of
+ *              gdn_replay_verify_flush also use sync[num_slots + s * HK + kh],
+ *              so give it num_slots * (1 + HK) entries if that call is used,
+ *              num_slots entries otherwise.
  *   err        [1] int32 sticky error word, or NULL to drop device errors.
  *
  * Value head h reads key head h / (HV / HK) (consecutive grouping, HV % HK == 0).
@@ -161,6 +165,29 @@ int gdn_replay_rollback(const gdn_replay_cache *c, int32_t num_reqs, const int32
  */
 int gdn_replay_flush(const gdn_replay_cache *c, int32_t num_reqs, const int32_t *slot_idx,
                      int32_t min_len, hipStream_t stream);
+
+/*
+ * gdn_replay_verify_flush — gdn_replay_flush(min_len) followed by
+ * gdn_replay_verify, in one pass over the state: the periodic flush ("Making
+ * speculative verification cheaper", as above) is folded into the next
+ * verify, so the state of a due slot is read once and written once.
+ *
+ * For request i with slot s = slot_idx[i]: if len[s] >= max(min_len, 1), fold the
+ * len[s] committed tokens into state[s], head[s] = (head[s] + len[s]) mod C and
+ * len[s] = 0 (exactly as gdn_replay_flush); then verify the draft exactly as
+ * gdn_replay_verify, from the resulting checkpoint, pointers and ring. Arguments
+ * as for gdn_replay_verify plus min_len; sync must hold num_slots * (1 + HK)
+ * counters (see gdn_replay_cache). Ring capacity <= 32 with bf16 inputs and
+ * d_k = d_v in {64, 128} runs as one kernel; other shapes run the two calls back
+ * to back on the stream.
+ * Device errors: slot out of range -> SLOT; head or len out of range -> POINTER;
+ * a slot that is not due with len + D > C -> CAPACITY. The request is skipped
+ * with no writes at all (no flush either).
+ */
+int gdn_replay_verify_flush(const gdn_replay_cache *c, int32_t num_reqs, const int32_t *slot_idx,
+                            int32_t draft_len, int32_t min_len, const void *q, const void *k,
+                            const void *v, const float *alpha, const float *beta, float *out,
+                            hipStream_t stream);
 
 /* Human-readable text of a gdn_status (static storage). */
 const char *gdn_replay_strerror(int status);

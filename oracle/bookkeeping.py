@@ -12,6 +12,7 @@ committed tokens not yet folded into the checkpoint), capacity C.
                 (head + len + j) mod C, j < D. Pointers unchanged.
   rollback(a):  needs 0 <= a <= D and len + a <= C; len += a.
   flush(m):     if len >= max(m, 1): head = (head + len) mod C, len = 0.
+  verify_flush(D, m): flush(m), then verify(D).
 Violations set CAPACITY=1 / ACCEPT=2 / SLOT=4 / POINTER=8 (head outside [0, C)
 or len outside [0, C]) and leave the slot untouched.
 """
@@ -78,3 +79,8 @@ class RingPointers:
                 self.head[s] = (self.head[s] + n) % self.cap
                 self.len[s] = 0
         return folded
+
+    def verify_flush(self, slots, draft_len: int, min_len: int):
+        """flush(min_len) then verify(draft_len): (folded, written) of the two."""
+        folded = self.flush(slots, min_len)
+        return folded, self.verify(slots, draft_len)

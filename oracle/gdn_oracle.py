@@ -244,6 +244,14 @@ class ReplayOracle:
             self.head[s] = (int(self.head[s]) + n) % self.cap
             self.len[s] = 0
 
+    def verify_flush(self, slot_idx, min_len: int, q, k, v, alpha, beta) -> np.ndarray:
+        """The periodic flush folded into the next verify: flush(min_len), then
+        verify from the resulting checkpoint, pointers and ring. A slot that is
+        not due and has len + D > C is skipped by verify (CAPACITY) after a flush
+        that did not touch it, so the call writes nothing for it."""
+        self.flush(slot_idx, min_len)
+        return self.verify(slot_idx, q, k, v, alpha, beta)
+
     # -- views in the library's layouts -----------------------------------------
     def state_abi(self) -> np.ndarray:
         """Checkpoint as [slots][HV][d_k][d_v] (H = S^T), float64."""

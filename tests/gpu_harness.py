@@ -93,6 +93,43 @@ class Pair:
         self._check_common(host)
         return out
 
+    def _check_flushed(self, host, before, slot_idx, sel, min_len, len_before):
+        ref_state = self.orc.state_abi()
+        flushed = [int(slot_idx[i]) for i in sel
+                   if 0 <= slot_idx[i] < self.wl.num_slots and
+                   len_before[slot_idx[i]] >= max(min_len, 1) and self.orc.len[slot_idx[i]] == 0]
+        if flushed:
+            e = rel_err(host["state"][flushed], ref_state[flushed])
+            self.worst["state"] = max(self.worst["state"], e)
+            assert e <= TOL, f"flushed states: rel err {e:.3e} > {TOL}"
+            self.flushed_count += len(flushed)
+        others = [s for s in range(self.wl.num_slots) if s not in set(flushed)
+                  and (self.oracle_slots is None or s in self.oracle_slots)]
+        assert np.array_equal(host["state"][others].view(np.uint32),
+                              before[others].view(np.uint32)), "unflushed slot state changed"
+
+    def verify_flush(self, slot_idx, min_len, dr, label=""):
+        say(f"  verify_flush {label} R={len(slot_idx)} D={dr['alpha'].shape[1]} min_len={min_len}")
+        before = self.gpu.state.cpu().numpy()
+        len_before = self.orc.len.copy()
+        dev = {k: to_device(v) for k, v in dr.items()}
+        out = self.gpu.verify_flush(to_device(slot_idx), min_len, dev["q"], dev["k"], dev["v"],
+                                    dev["alpha"], dev["beta"])
+        torch.cuda.synchronize()
+        sel = self._sel(slot_idx)
+        ref = self.orc.verify_flush(slot_idx[sel], min_len,
+                                    *(dr[x][sel] for x in ("q", "k", "v", "alpha", "beta")))
+        got = out.cpu().numpy()[sel]
+        ok = ~np.isnan(ref).any(axis=(1, 2, 3))
+        if ok.any():
+            e = rel_err(got[ok], ref[ok])
+            self.worst["out"] = max(self.worst["out"], e)
+            assert e <= TOL, f"verify_flush outputs: rel err {e:.3e} > {TOL}"
+        host = self.gpu.to_numpy()
+        self._check_common(host)
+        self._check_flushed(host, before, slot_idx, sel, min_len, len_before)
+        return out
+
     def rollback(self, slot_idx, draft_len, acc, label=""):
         say(f"  rollback {label}")
         before = self.gpu.state.clone()
@@ -113,24 +150,13 @@ class Pair:
         self.orc.flush(slot_idx[sel], min_len)
         host = self.gpu.to_numpy()
         self._check_common(host)
-        ref_state = self.orc.state_abi()
-        flushed = [int(slot_idx[i]) for i in sel
-                   if 0 <= slot_idx[i] < self.wl.num_slots and
-                   len_before[slot_idx[i]] >= max(min_len, 1) and self.orc.len[slot_idx[i]] == 0]
-        if flushed:
-            e = rel_err(host["state"][flushed], ref_state[flushed])
-            self.worst["state"] = max(self.worst["state"], e)
-            assert e <= TOL, f"flushed states: rel err {e:.3e} > {TOL}"
-            self.flushed_count += len(flushed)
-        others = [s for s in range(self.wl.num_slots) if s not in set(flushed)
-                  and (self.oracle_slots is None or s in self.oracle_slots)]
-        assert np.array_equal(host["state"][others].view(np.uint32),
-                              before[others].view(np.uint32)), "unflushed slot state changed"
+        self._check_flushed(host, before, slot_idx, sel, min_len, len_before)
 
 
 def run_schedule(wl: synth.Workload, steps: int, seed: int, layers: int = 1, with_q=True,
-                 oracle_slots=None, label=""):
-    """verify -> rollback -> flush for `steps` steps over `layers` independent caches."""
+                 oracle_slots=None, label="", fused=False):
+    """verify -> rollback -> flush for `steps` steps over `layers` independent caches
+    (fused: verify_flush -> rollback, the flush folded into the next verify)."""
     rng = np.random.default_rng(seed)
     pairs = []
     for L in range(layers):
@@ -141,9 +167,13 @@ def run_schedule(wl: synth.Workload, steps: int, seed: int, layers: int = 1, wit
         acc = synth.sample_accepted(wl, rng)
         for L, p in enumerate(pairs):
             dr = synth.make_draft(wl, rng)
-            p.verify(slots, dr, f"{label} L{L} step{step}")
+            if fused:
+                p.verify_flush(slots, wl.flush_min_len, dr, f"{label} L{L} step{step}")
+            else:
+                p.verify(slots, dr, f"{label} L{L} step{step}")
         for L, p in enumerate(pairs):
             p.rollback(slots, wl.draft, acc, f"{label} L{L} step{step}")
-        for L, p in enumerate(pairs):
-            p.flush(slots, wl.flush_min_len, f"{label} L{L} step{step}")
+        if not fused:
+            for L, p in enumerate(pairs):
+                p.flush(slots, wl.flush_min_len, f"{label} L{L} step{step}")
     return pairs

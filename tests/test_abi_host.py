@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert b.version() == 1
+    assert b.version() == 2
     for st in (b.GDN_OK, b.GDN_EINVAL, b.GDN_EUNSUPPORTED, b.GDN_EHIP):
         assert b.load().gdn_replay_strerror(st)
     assert b.load().gdn_replay_strerror(12345) == b"unknown status"
@@ -52,11 +52,20 @@ def _verify(c, num_reqs=2, draft=4, **ptrs):
                         p["out"], None)
 
 
+def _verify_flush(c, num_reqs=2, draft=4, min_len=1, **ptrs):
+    p = dict(slot=FAKE, q=FAKE, k=FAKE, v=FAKE, a=FAKE, be=FAKE, out=FAKE)
+    p.update(ptrs)
+    return b.verify_flush_raw(c, num_reqs, p["slot"], draft, min_len, p["q"], p["k"], p["v"],
+                              p["a"], p["be"], p["out"], None)
+
+
 def test_null_cache_rejected():
     lib = b.load()
     assert lib.gdn_replay_verify(None, 1, FAKE, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == b.GDN_EINVAL
     assert lib.gdn_replay_rollback(None, 1, FAKE, 1, FAKE, None) == b.GDN_EINVAL
     assert lib.gdn_replay_flush(None, 1, FAKE, 1, None) == b.GDN_EINVAL
+    assert lib.gdn_replay_verify_flush(None, 1, FAKE, 1, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                       None) == b.GDN_EINVAL
 
 
 @pytest.mark.parametrize("over,status", [
@@ -82,6 +91,7 @@ def test_cache_validation(over, status):
     assert _verify(c) == status
     assert b.rollback_raw(c, 2, FAKE, 4, FAKE, None) == status
     assert b.flush_raw(c, 2, FAKE, 1, None) == status
+    assert _verify_flush(c) == status
 
 
 def test_call_validation():
@@ -98,6 +108,10 @@ def test_call_validation():
     assert b.rollback_raw(c, 2, FAKE, 4, None, None) == b.GDN_EINVAL
     assert b.flush_raw(c, -3, FAKE, 1, None) == b.GDN_EINVAL
     assert b.flush_raw(c, 2, None, 1, None) == b.GDN_EINVAL
+    for kw in (dict(num_reqs=-1), dict(num_reqs=5), dict(draft=0), dict(draft=9),
+               dict(k=None), dict(be=None), dict(out=FAKE + 4),
+               dict(slot=None)):
+        assert _verify_flush(c, **kw) == b.GDN_EINVAL, kw
 
 
 def test_zero_requests_is_a_noop_without_launch():
@@ -105,6 +119,7 @@ def test_zero_requests_is_a_noop_without_launch():
     assert _verify(c, num_reqs=0, q=None, k=None) == b.GDN_OK
     assert b.rollback_raw(c, 0, None, 4, None, None) == b.GDN_OK
     assert b.flush_raw(c, 0, None, 1, None) == b.GDN_OK
+    assert _verify_flush(c, num_reqs=0, q=None, out=None) == b.GDN_OK
 
 
 def test_struct_layout_matches_header():

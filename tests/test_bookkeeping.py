@@ -115,3 +115,19 @@ def test_committed_window_holds_accepted_tokens_in_order():
             for t, rec in enumerate(hist[s]):
                 pos = (int(orc.head[s]) + t) % wl.cap
                 assert np.array_equal(orc.ring_k[s, :, pos], rec)
+
+
+def test_verify_flush_is_flush_then_verify_on_the_model():
+    """The fused call's pointer rule on the integer model: a due slot is folded
+    (head += len, len = 0) and the draft lands right behind the new head; a slot
+    that is not due and has len + D > C is rejected without any change."""
+    m = bk.RingPointers([3, 5, 0, 7], [6, 2, 7, 1], 8)
+    folded, written = m.verify_flush([0, 1, 2, 3], 2, 6)
+    assert folded == {0: 6, 2: 7}
+    assert m.head == [1, 5, 7, 7] and m.len == [0, 2, 0, 1]
+    assert written == {0: [1, 2], 1: [7, 0], 2: [7, 0], 3: [0, 1]}
+    assert m.err == 0
+    m2 = bk.RingPointers([0], [7], 8)
+    folded, written = m2.verify_flush([0], 2, 8)    # not due, 7 + 2 > 8
+    assert folded == {} and written == {} and m2.err == 1
+    assert m2.head == [0] and m2.len == [7]

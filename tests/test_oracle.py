@@ -271,8 +271,9 @@ def test_contraction_bound():
         S = S1
 
 
-def _run_schedule(wl, mode, steps, seed, flush_min_len, collect=True):
-    """Random verify/rollback/flush schedule; returns (oracle, accepted outputs per slot)."""
+def _run_schedule(wl, mode, steps, seed, flush_min_len, collect=True, fused=False):
+    """Random verify/rollback/flush schedule (fused: verify_flush/rollback, the
+    flush folded into the next verify); returns (oracle, accepted outputs per slot)."""
     rng = np.random.default_rng(seed)
     init = synth.make_cache_init(wl, rng)
     orc = go.ReplayOracle(init, wl.hv, wl.hk, wl.dk, wl.dv, wl.cap, mode=mode)
@@ -282,9 +283,14 @@ def _run_schedule(wl, mode, steps, seed, flush_min_len, collect=True):
         slots = synth.make_slot_idx(wl, rng)
         dr = synth.make_draft(wl, rng)
         acc = synth.sample_accepted(wl, rng)
-        out = orc.verify(slots, dr["q"], dr["k"], dr["v"], dr["alpha"], dr["beta"])
+        if fused:
+            out = orc.verify_flush(slots, flush_min_len, dr["q"], dr["k"], dr["v"], dr["alpha"],
+                                   dr["beta"])
+        else:
+            out = orc.verify(slots, dr["q"], dr["k"], dr["v"], dr["alpha"], dr["beta"])
         orc.rollback(slots, wl.draft, acc)
-        orc.flush(slots, flush_min_len)
+        if not fused:
+            orc.flush(slots, flush_min_len)
         for i, s in enumerate(slots):
             for j in range(acc[i]):
                 accepted[s].append(out[i, j])
@@ -292,11 +298,16 @@ def _run_schedule(wl, mode, steps, seed, flush_min_len, collect=True):
     return orc, init, accepted, stream
 
 
-def test_replay_equals_sequential_recurrence():
+@pytest.mark.parametrize("fused", [False, True])
+def test_replay_equals_sequential_recurrence(fused):
     """P8: accepted outputs over many steps with flushes = one plain sequential
-    run over each slot's committed token stream from the initial checkpoint."""
+    run over each slot's committed token stream from the initial checkpoint
+    (also with the flush folded into the next verify)."""
     wl = synth.Workload("t", 3, 4, 4, 2, 8, 6, 12, 4, synth.F32, 5, 1, "uniform", "uniform:0:4")
-    orc, init, accepted, stream = _run_schedule(wl, "replay", 12, 11, wl.flush_min_len)
+    orc, init, accepted, stream = _run_schedule(wl, "replay", 12, 11, wl.flush_min_len,
+                                                fused=fused)
+    if fused:
+        assert (orc.len < wl.flush_min_len + wl.draft).all()
     G = wl.hv // wl.hk
     for s in range(wl.num_slots):
         S = np.swapaxes(init["state"][s].astype(np.float64), -1, -2)

@@ -24,7 +24,8 @@ PIN_TESTS = [
     lambda: pins.test_scalar_recurrence_closed_form(),
     lambda: pins.test_state_layout_is_transpose(),
     lambda: pins.test_linearity_in_state_and_values(),
-    lambda: pins.test_replay_equals_sequential_recurrence(),
+    lambda: pins.test_replay_equals_sequential_recurrence(False),
+    lambda: pins.test_replay_equals_sequential_recurrence(True),
     lambda: pins.test_rollback_prefix_equals_recurrence_over_prefix(),
     lambda: pins.test_flush_then_verify_equals_verify_without_flush(),
     lambda: pins.test_gva_head_grouping(),

@@ -75,8 +75,8 @@ class ReplayCache:
         self.ring_beta = z((num_slots, hv, cap), torch.float32)
         self.head = z((num_slots,), torch.int32)
         self.len = z((num_slots,), torch.int32)
-        # slot counters, then the per-(slot, key head) counters of verify_flush
-        self.sync = z((num_slots * (1 + hk),), torch.int32)
+        # slot counters, then the per-(slot, key head) and grid counters of verify_flush
+        self.sync = z((num_slots * (1 + hk) + 1,), torch.int32)
         self.err = z((1,), torch.int32)
         self._struct = None
 

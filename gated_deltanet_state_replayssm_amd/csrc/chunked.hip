@@ -1063,11 +1063,67 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_single(Verify
   }
 }
 
+// Request of rank q in the order [due requests..., other requests...], where a
+// request is due when its slot is valid and len >= mn; every lane of the wave
+// returns the same value. Up to 64 requests take one load per lane and one
+// ballot; more are counted in rounds of 64. The order depends only on slot_idx
+// and len, which the fused kernel leaves unchanged until its last workgroup.
+__device__ __forceinline__ int nth_bit(uint64_t m, int n) {
+  for (int t = 0; t < n; ++t) m &= m - 1;
+  return __builtin_ctzll(m);
+}
+
+__device__ int ordered_request(const VerifyArgs &va, int mn, int q, int lane) {
+  const int R = va.num_reqs;
+  const CacheView &c = va.c;
+  auto due_mask = [&](int j) -> uint64_t {
+    const int i = 64 * j + lane;
+    bool d = false;
+    if (i < R) {
+      const int si = va.slot_idx[i];
+      d = si >= 0 && si < c.num_slots && c.len[si] >= mn;
+    }
+    return __ballot(d);
+  };
+  auto lanes = [&](int j) -> uint64_t {
+    const int m = min(64, R - 64 * j);
+    return m == 64 ? ~0ull : ((1ull << m) - 1);
+  };
+  if (R <= 64) {
+    const uint64_t dm = due_mask(0);
+    const int nd = __popcll(dm);
+    return q < nd ? nth_bit(dm, q) : nth_bit(~dm & lanes(0), q - nd);
+  }
+  const int chunks = (R + 63) / 64;
+  int nd = 0;
+  for (int j = 0; j < chunks; ++j) nd += __popcll(due_mask(j));
+  const bool want_due = q < nd;
+  int left = want_due ? q : q - nd;
+  for (int j = 0; j < chunks; ++j) {
+    uint64_t m = due_mask(j);
+    if (!want_due) m = ~m & lanes(j);
+    const int cnt = __popcll(m);
+    if (left < cnt) return 64 * j + nth_bit(m, left);
+    left -= cnt;
+  }
+  return q;  // not reached: the two classes cover every request
+}
+
 // Flush fused into verify, ring capacity <= 32. A slot with len >= max(min_len,
-// 1) first folds its len committed tokens into the checkpoint, writes it back
-// and moves its pointers (head += len, len = 0), then verifies the draft from
-// the new checkpoint; other slots verify as replay_single does. One state read
-// serves both, and a due slot's state is written once.
+// 1) first folds its len committed tokens into the checkpoint and writes it
+// back, then verifies the draft from the new checkpoint; other slots verify as
+// replay_single does. One state read serves both, and a due slot's state is
+// written once.
+//
+// Work order: units of due requests (about twice the work) come first, so that
+// the dispatch, which spreads consecutive workgroups over the CUs, gives every
+// CU a similar share of them. Every workgroup derives the order from each
+// request's len, so len must not change while a workgroup may still read it:
+// the pointers of the due slots (head += len, len = 0) are moved by the last
+// workgroup of the grid to finish. It is found in two levels, so that no
+// counter sees more than one arrival per workgroup of a request group: the
+// HV workgroups of request rank q count in at sync[q], the last of them at
+// sync[num_slots * (1 + HK)].
 //
 // The draft is appended at (new head + j) mod C, which may wrap onto committed
 // key rows that the other value heads of the same key head are still reading
@@ -1082,30 +1138,61 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyA
   static_assert(DK % 32 == 0 && DV % (16 * NT) == 0 && (NT == 2 || NT == 4), "tile shape");
   typedef typename Cols<NT>::F F;
   __shared__ Smem<DK, DV> sm;
-  __shared__ int group_rank;
+  __shared__ int group_rank, grid_rank;
 
   const CacheView &c = va.c;
   const int HV = c.hv, G = HV / c.hk;
-  const int r = blockIdx.x / HV, h = blockIdx.x % HV;
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
   const int g = lane >> 4, l16 = lane & 15;
   const int colL = wave * 16 * NT + NT * l16;
+  const int mn = max(min_len, 1);
+  const int r = ordered_request(va, mn, blockIdx.x / HV, lane), h = blockIdx.x % HV;
   const bool lead = (h == 0 && tid == 0);
+  int32_t *grid_ctr = c.sync + (int64_t)c.num_slots * (1 + c.hk);
+  int32_t *rank_ctr = c.sync + blockIdx.x / HV;
+
+  // Every workgroup counts itself in at its end (after a barrier, so that all
+  // its waves have read the pointers); the last one moves the due slots' pointers.
+  auto finish = [&]() {
+    __syncthreads();
+    if (tid == 0) {
+      int last = 0;
+      if (atomicAdd(rank_ctr, 1) == HV - 1) {
+        *rank_ctr = 0;
+        last = atomicAdd(grid_ctr, 1) == va.num_reqs - 1;
+      }
+      grid_rank = last;
+    }
+    __syncthreads();
+    if (!grid_rank) return;
+    for (int i = tid; i < va.num_reqs; i += blockDim.x) {
+      const int si = va.slot_idx[i];
+      if (si < 0 || si >= c.num_slots) continue;
+      const int hs = c.head[si], ns = c.len[si];
+      if (hs < 0 || hs >= c.cap || ns < mn || ns > c.cap) continue;
+      c.head[si] = hs + ns - (hs + ns >= c.cap ? c.cap : 0);
+      c.len[si] = 0;
+    }
+    if (tid == 0) *grid_ctr = 0;
+  };
 
   const int s = va.slot_idx[r];
   if (s < 0 || s >= c.num_slots) {
     if (lead) raise_err(c.err, GDN_DERR_SLOT);
+    finish();
     return;
   }
   const int C = c.cap;
   const int head = c.head[s], n = c.len[s];
   if (head < 0 || head >= C || n < 0 || n > C) {
     if (lead) raise_err(c.err, GDN_DERR_POINTER);
+    finish();
     return;
   }
-  const bool due = n >= max(min_len, 1);
+  const bool due = n >= mn;
   if (!due && n + va.draft > C) {
     if (lead) raise_err(c.err, GDN_DERR_CAPACITY);
+    finish();
     return;
   }
   const int kh = h / G;
@@ -1166,16 +1253,8 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyA
                            HV * DV * 4);
   const bool kq_writer = due ? group_rank == G - 1 : h % G == 0;
   sg.append(sm, sr, u, 0, u.T, kq_writer);
-  if (due && tid == 0) {
-    if (kq_writer) *group_ctr = 0;  // every member has counted in
-    // Last workgroup of the slot moves the pointers (see replay_single).
-    const int prev = atomicAdd(&c.sync[s], 1);
-    if (prev == HV - 1) {
-      c.head[s] = hd;
-      c.len[s] = 0;
-      c.sync[s] = 0;
-    }
-  }
+  if (due && kq_writer && tid == 0) *group_ctr = 0;  // every member has counted in
+  finish();
 }
 
 template <int DK, int DV, bool VERIFY>

@@ -44,7 +44,7 @@ bool chunked_supported(int dk, int dv, bool in_f32, int draft);
 hipError_t launch_verify_chunked(const VerifyArgs &a, hipStream_t stream);
 hipError_t launch_flush_chunked(const FlushArgs &a, hipStream_t stream);
 // Flush fused into verify in one kernel (chunked shapes, ring capacity <= 32);
-// needs sync sized [num_slots * (1 + HK)].
+// needs sync sized [num_slots * (1 + HK) + 1].
 bool fused_supported(int dk, int dv, bool in_f32, int draft, int cap);
 hipError_t launch_verify_flush_fused(const VerifyArgs &a, int min_len, hipStream_t stream);
 // Token-by-token fp32 kernels (every built shape, bf16 or fp32 inputs):

@@ -81,9 +81,10 @@ enum {
  *   sync       int32 arrival counters, zero when created; every completed call
  *              leaves them zero. sync[s] (s < num_slots) lets flush move the
  *              pointers after every workgroup of slot s has read them. Calls of
- *              gdn_replay_verify_flush also use sync[num_slots + s * HK + kh],
- *              so give it num_slots * (1 + HK) entries if that call is used,
- *              num_slots entries otherwise.
+ *              gdn_replay_verify_flush also use sync[num_slots + s * HK + kh]
+ *              and sync[num_slots * (1 + HK)], so give it
+ *              num_slots * (1 + HK) + 1 entries if that call is used, num_slots
+ *              entries otherwise.
  *   err        [1] int32 sticky error word, or NULL to drop device errors.
  *
  * Value head h reads key head h / (HV / HK) (consecutive grouping, HV % HK == 0).
@@ -176,7 +177,7 @@ int gdn_replay_flush(const gdn_replay_cache *c, int32_t num_reqs, const int32_t 
  * len[s] committed tokens into state[s], head[s] = (head[s] + len[s]) mod C and
  * len[s] = 0 (exactly as gdn_replay_flush); then verify the draft exactly as
  * gdn_replay_verify, from the resulting checkpoint, pointers and ring. Arguments
- * as for gdn_replay_verify plus min_len; sync must hold num_slots * (1 + HK)
+ * as for gdn_replay_verify plus min_len; sync must hold num_slots * (1 + HK) + 1
  * counters (see gdn_replay_cache). Ring capacity <= 32 with bf16 inputs and
  * d_k = d_v in {64, 128} runs as one kernel; other shapes run the two calls back
  * to back on the stream.

@@ -125,3 +125,15 @@ def test_fused_equals_flush_then_verify_bitwise():
             x, y = x.view(torch.int16), y.view(torch.int16)
         assert torch.equal(x, y), name
     assert not a.sync.any()
+
+
+def test_fused_stress_batch_sampled():
+    """128 requests: more workgroups than fit on the GPU at once, and the due
+    ordering counted in rounds of 64 requests."""
+    wl = W["r128_hv32_hk16_d128_f16"]
+    say("case fused r128_hv32_hk16_d128_f16, sampled")
+    rng = np.random.default_rng(24)
+    sample = rng.choice(wl.num_slots, 5, replace=False)
+    pairs = run_schedule(wl, 4, synth.seed_for(wl.name, 0, 1), oracle_slots=sample,
+                         label="c4f", fused=True)
+    say(f"  worst {pairs[0].worst}")

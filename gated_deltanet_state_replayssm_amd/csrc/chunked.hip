@@ -286,9 +286,9 @@ struct RowAt {
 // holds the whole draft) stages the queries; a folded chunk stages the
 // transposed keys instead. append() copies the draft rows from LDS into the
 // ring once the chunk is done.
-template <int DK, int DV, int NT, bool VERIFY>
+template <int DK, int DV, int NT, bool VERIFY, int STAGERS = 64 * (DV / (16 * NT))>
 struct Stage {
-  static constexpr int THREADS = 64 * (DV / (16 * NT));
+  static constexpr int THREADS = STAGERS;
   static constexpr int PK = DK / 8, PV = DV / 8;  // 16-byte pieces per k / v row
   static constexpr int IK = kCh * PK / THREADS, IV = kCh * PV / THREADS;
   static_assert(kCh * PK % THREADS == 0 && kCh * PV % THREADS == 0, "pieces per thread");
@@ -971,11 +971,10 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 2) void replay_chunked(Verif
 
 
 // Ring capacity <= 32, so every replay is a single chunk (T = len [+ D] <= 32).
-// Waves 1.. issue their state loads as soon as the inputs are staged, while
-// wave 0 builds the T x T matrices and only then loads its own state columns:
-// the state is never live next to the matrix-building temporaries, which lets
-// four workgroups share a CU. Verify takes Y = K H and Z = Q H in one pass, so
-// its state registers die right after it.
+// Waves 2 and 3 load their state columns first; waves 0 and 1 stage the
+// chunk's inputs, load theirs, then build the T x T matrices (wave 0: A and its
+// inverse; wave 1: C) while the state streams in. Verify takes Y = K H and
+// Z = Q H in one pass, so its state registers die right after it.
 template <int DK, int DV, int NT, bool VERIFY>
 __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_single(VerifyArgs va,
                                                                           FlushArgs fa) {
@@ -1020,13 +1019,22 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_single(Verify
   const uint32_t st_off = (4 * g * DV + colL) * 4;
 
   const Srcs sr = make_srcs<DK, DV>(c, u, &va, VERIFY);
-  Stage<DK, DV, NT, VERIFY> sg;
-  sg.load(sr, u, 0, T, VERIFY);
-  sg.store(sm, T, VERIFY);
-  __builtin_amdgcn_sched_barrier(0);
+  // Waves SW.. issue their state loads first; waves 0..SW-1 stage the chunk's
+  // inputs, then load their state columns (loads complete in issue order, so a
+  // wave that must wait for its staged inputs must not have its state loads
+  // ahead of them).
+  constexpr int SW = WAVES >= 4 ? 2 : WAVES;
+  Stage<DK, DV, NT, VERIFY, 64 * SW> sg;
   F H[MT][4];
-  load_state<DK, DV, NT>(st, st_off, H);
-  __builtin_amdgcn_sched_barrier(0);
+  if (wave >= SW) {
+    load_state<DK, DV, NT>(st, st_off, H);
+  } else {
+    sg.load(sr, u, 0, T, VERIFY);
+    sg.store(sm, T, VERIFY);
+    __builtin_amdgcn_sched_barrier(0);
+    load_state<DK, DV, NT>(st, st_off, H);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   __syncthreads();
 
   if (wave == 0) {
@@ -1043,7 +1051,7 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_single(Verify
   if constexpr (VERIFY) {
     emit_outputs<DK, DV, NT>(sm, Z, Wm, g, l16, 0, T, u.B, out_rsrc(va, r, h, DV), colL * 4,
                          HV * DV * 4);
-    sg.append(sm, sr, u, 0, T, h % (HV / c.hk) == 0);
+    if (wave < SW) sg.append(sm, sr, u, 0, T, h % (HV / c.hk) == 0);
   } else {
     fold_state<DK, DV, NT>(sm, Wm, g, l16, H);
     store_state<DK, DV, NT>(st, st_off, H);

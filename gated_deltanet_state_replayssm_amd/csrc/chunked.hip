@@ -1072,18 +1072,46 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_single(Verify
 }
 
 // Request of rank q in the order [due requests..., other requests...], where a
-// request is due when its slot is valid and len >= mn; every lane of the wave
-// returns the same value. Up to 64 requests take one load per lane and one
-// ballot; more are counted in rounds of 64. The order depends only on slot_idx
-// and len, which the fused kernel leaves unchanged until its last workgroup.
+// request is due when its slot is valid and len >= mn, with its slot and that
+// slot's pointers (head and len are meaningful only for a valid slot); every
+// lane of the wave returns the same values. Up to 64 requests take one pass:
+// each lane loads one request's slot and pointers, a ballot orders them, and the
+// chosen lane's values are read across the wave, so the state address is known
+// after two dependent loads. More requests are counted in rounds of 64 and the
+// chosen one's slot and pointers are loaded again. The order depends only on
+// slot_idx and len, which the fused kernel leaves unchanged until its last
+// workgroup.
 __device__ __forceinline__ int nth_bit(uint64_t m, int n) {
   for (int t = 0; t < n; ++t) m &= m - 1;
   return __builtin_ctzll(m);
 }
 
-__device__ int ordered_request(const VerifyArgs &va, int mn, int q, int lane) {
+struct Req {
+  int r, s, head, len;
+};
+
+__device__ Req ordered_request(const VerifyArgs &va, int mn, int q, int lane) {
   const int R = va.num_reqs;
   const CacheView &c = va.c;
+  auto lanes = [&](int j) -> uint64_t {
+    const int m = min(64, R - 64 * j);
+    return m == 64 ? ~0ull : ((1ull << m) - 1);
+  };
+  if (R <= 64) {
+    int si = -1, hi = 0, ni = 0;
+    if (lane < R) {
+      si = va.slot_idx[lane];
+      if (si >= 0 && si < c.num_slots) {
+        hi = c.head[si];
+        ni = c.len[si];
+      }
+    }
+    const uint64_t dm = __ballot(si >= 0 && si < c.num_slots && ni >= mn);
+    const int nd = __popcll(dm);
+    const int r = q < nd ? nth_bit(dm, q) : nth_bit(~dm & lanes(0), q - nd);
+    return Req{r, __builtin_amdgcn_readlane(si, r), __builtin_amdgcn_readlane(hi, r),
+               __builtin_amdgcn_readlane(ni, r)};
+  }
   auto due_mask = [&](int j) -> uint64_t {
     const int i = 64 * j + lane;
     bool d = false;
@@ -1093,28 +1121,28 @@ __device__ int ordered_request(const VerifyArgs &va, int mn, int q, int lane) {
     }
     return __ballot(d);
   };
-  auto lanes = [&](int j) -> uint64_t {
-    const int m = min(64, R - 64 * j);
-    return m == 64 ? ~0ull : ((1ull << m) - 1);
-  };
-  if (R <= 64) {
-    const uint64_t dm = due_mask(0);
-    const int nd = __popcll(dm);
-    return q < nd ? nth_bit(dm, q) : nth_bit(~dm & lanes(0), q - nd);
-  }
   const int chunks = (R + 63) / 64;
   int nd = 0;
   for (int j = 0; j < chunks; ++j) nd += __popcll(due_mask(j));
   const bool want_due = q < nd;
   int left = want_due ? q : q - nd;
+  int r = q;  // replaced below: the two classes cover every request
   for (int j = 0; j < chunks; ++j) {
     uint64_t m = due_mask(j);
     if (!want_due) m = ~m & lanes(j);
     const int cnt = __popcll(m);
-    if (left < cnt) return 64 * j + nth_bit(m, left);
+    if (left < cnt) {
+      r = 64 * j + nth_bit(m, left);
+      break;
+    }
     left -= cnt;
   }
-  return q;  // not reached: the two classes cover every request
+  Req o{r, va.slot_idx[r], 0, 0};
+  if (o.s >= 0 && o.s < c.num_slots) {
+    o.head = c.head[o.s];
+    o.len = c.len[o.s];
+  }
+  return o;
 }
 
 // Flush fused into verify, ring capacity <= 32. A slot with len >= max(min_len,
@@ -1152,9 +1180,22 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyA
   const int HV = c.hv, G = HV / c.hk;
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
   const int g = lane >> 4, l16 = lane & 15;
-  const int colL = wave * 16 * NT + NT * l16;
+  // This lane's first state column and its byte offset in the state tile, taken
+  // from an opaque copy of the thread index at each use, so that they are
+  // recomputed there instead of being held in registers through the kernel.
+  auto col_of = [&]() {
+    int t = tid;
+    asm volatile("" : "+v"(t));
+    return (t / 64) * 16 * NT + NT * (t & 15);
+  };
+  auto st_off_of = [&]() {
+    int t = tid;
+    asm volatile("" : "+v"(t));
+    return (uint32_t)((4 * ((t & 63) >> 4) * DV + (t / 64) * 16 * NT + NT * (t & 15)) * 4);
+  };
   const int mn = max(min_len, 1);
-  const int r = ordered_request(va, mn, blockIdx.x / HV, lane), h = blockIdx.x % HV;
+  const Req rq = ordered_request(va, mn, blockIdx.x / HV, lane);
+  const int r = rq.r, h = blockIdx.x % HV;
   const bool lead = (h == 0 && tid == 0);
   int32_t *grid_ctr = c.sync + (int64_t)c.num_slots * (1 + c.hk);
   int32_t *rank_ctr = c.sync + blockIdx.x / HV;
@@ -1184,14 +1225,14 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyA
     if (tid == 0) *grid_ctr = 0;
   };
 
-  const int s = va.slot_idx[r];
+  const int s = rq.s;
   if (s < 0 || s >= c.num_slots) {
     if (lead) raise_err(c.err, GDN_DERR_SLOT);
     finish();
     return;
   }
   const int C = c.cap;
-  const int head = c.head[s], n = c.len[s];
+  const int head = rq.head, n = rq.len;
   if (head < 0 || head >= C || n < 0 || n > C) {
     if (lead) raise_err(c.err, GDN_DERR_POINTER);
     finish();
@@ -1205,62 +1246,87 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyA
   }
   const int kh = h / G;
   const Rsrc st = make_rsrc(c.state + ((int64_t)s * HV + h) * DK * DV, DK * DV * 4);
-  const uint32_t st_off = (4 * g * DV + colL) * 4;
   int32_t *group_ctr = c.sync + c.num_slots + (int64_t)s * c.hk + kh;
 
+  // Waves SW.. issue their state loads first; waves 0..SW-1 stage the inputs of
+  // the first replay, then load their state columns (loads complete in issue
+  // order, so a wave that waits for staged inputs must not have state loads
+  // ahead of them).
+  constexpr int SW = WAVES >= 4 ? 2 : WAVES;
   F H[MT][4];
   int hd = head, B = n;  // ring start and committed count of the verify below
   if (due) {
     // ---- flush: fold the n committed tokens
     const Unit uf{r, h, s, kh, head, n, n, C};
-    const Srcs sf = make_srcs<DK, DV>(c, uf, nullptr, false);
-    Stage<DK, DV, NT, false> sgf;
-    sgf.load(sf, uf, 0, n, false);
-    sgf.store(sm, n, false);
-    __builtin_amdgcn_sched_barrier(0);
-    load_state<DK, DV, NT>(st, st_off, H);
-    __builtin_amdgcn_sched_barrier(0);
+    Stage<DK, DV, NT, false, 64 * SW> sgf;
+    if (wave >= SW) {
+      load_state<DK, DV, NT>(st, st_off_of(), H);
+    } else {
+      const Srcs sf = make_srcs<DK, DV>(c, uf, nullptr, false);
+      sgf.load(sf, uf, 0, n, false);
+      sgf.store(sm, n, false);
+      __builtin_amdgcn_sched_barrier(0);
+      load_state<DK, DV, NT>(st, st_off_of(), H);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     __syncthreads();  // the committed rows are read (and staged)
     if (tid == 0) group_rank = atomicAdd(group_ctr, 1);
     if (wave == 0) build_tt<DK, DV>(sm, sgf.al, lane, g, l16);
     __syncthreads();
     f32x4 Y[2][NT], Z[2][NT], Wm[2][NT];
     contract<DK, DV, NT, kY>(sm, H, g, l16, Y, Z);
-    solve_w<DK, DV, NT>(sm, Y, colL, g, l16, Wm);
+    solve_w<DK, DV, NT>(sm, Y, col_of(), g, l16, Wm);
     fold_state<DK, DV, NT>(sm, Wm, g, l16, H);
-    store_state<DK, DV, NT>(st, st_off, H);
+    store_state<DK, DV, NT>(st, st_off_of(), H);
     hd = head + n - (head + n >= C ? C : 0);
     B = 0;
     __syncthreads();  // LDS is staged again below
   }
 
-  // ---- verify the draft from checkpoint H plus B committed tokens at hd
+  // ---- verify the draft from checkpoint H plus B committed tokens at hd. A due
+  // slot's state is live here, so all waves stage (fewer rows each); otherwise
+  // waves 0..SW-1 stage while the others' state loads stream in.
   const Unit u{r, h, s, kh, hd, B, B + va.draft, C};
   const Srcs sr = make_srcs<DK, DV>(c, u, &va, true);
-  Stage<DK, DV, NT, true> sg;
-  sg.load(sr, u, 0, u.T, true);
-  sg.store(sm, u.T, true);
-  if (!due) {
-    __builtin_amdgcn_sched_barrier(0);
-    load_state<DK, DV, NT>(st, st_off, H);
-    __builtin_amdgcn_sched_barrier(0);
+  Stage<DK, DV, NT, true> sga;
+  Stage<DK, DV, NT, true, 64 * SW> sgs;
+  float al;  // this lane's staged alpha (token lane % 32)
+  if (due) {
+    sga.load(sr, u, 0, u.T, true);
+    sga.store(sm, u.T, true);
+    al = sga.al;
+  } else {
+    if (wave >= SW) {
+      load_state<DK, DV, NT>(st, st_off_of(), H);
+      al = 1.f;
+    } else {
+      sgs.load(sr, u, 0, u.T, true);
+      sgs.store(sm, u.T, true);
+      al = sgs.al;
+      __builtin_amdgcn_sched_barrier(0);
+      load_state<DK, DV, NT>(st, st_off_of(), H);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
   __syncthreads();
   if (wave == 0) {
-    build_tt<DK, DV>(sm, sg.al, lane, g, l16);
-    if (WAVES == 1) build_c<DK, DV>(sm, sg.al, lane, g, l16);
+    build_tt<DK, DV>(sm, al, lane, g, l16);
+    if (WAVES == 1) build_c<DK, DV>(sm, al, lane, g, l16);
   } else if (wave == 1) {
-    build_c<DK, DV>(sm, sg.al, lane, g, l16);
+    build_c<DK, DV>(sm, al, lane, g, l16);
   }
   __syncthreads();  // T x T matrices complete
 
   f32x4 Y[2][NT], Z[2][NT], Wm[2][NT];
   contract<DK, DV, NT, kY | kZ>(sm, H, g, l16, Y, Z);
-  solve_w<DK, DV, NT>(sm, Y, colL, g, l16, Wm);
-  emit_outputs<DK, DV, NT>(sm, Z, Wm, g, l16, 0, u.T, u.B, out_rsrc(va, r, h, DV), colL * 4,
+  solve_w<DK, DV, NT>(sm, Y, col_of(), g, l16, Wm);
+  emit_outputs<DK, DV, NT>(sm, Z, Wm, g, l16, 0, u.T, u.B, out_rsrc(va, r, h, DV), col_of() * 4,
                            HV * DV * 4);
   const bool kq_writer = due ? group_rank == G - 1 : h % G == 0;
-  sg.append(sm, sr, u, 0, u.T, kq_writer);
+  if (due)
+    sga.append(sm, sr, u, 0, u.T, kq_writer);
+  else if (wave < SW)
+    sgs.append(sm, sr, u, 0, u.T, kq_writer);
   if (due && kq_writer && tid == 0) *group_ctr = 0;  // every member has counted in
   finish();
 }

@@ -22,6 +22,7 @@ the host from the known schedule).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
                     [--path both|fused|separate]
+    python bench.py --sweep [--steps K] [--warmup W]   (replay cost vs buffer length)
 """
 from __future__ import annotations
 
@@ -121,6 +122,87 @@ def cpu_baseline(wl, seconds_budget=15.0):
                       f"{spent:.1f} s timed"}
 
 
+def sweep(args, workload="r32_hv32_hk16_d128_f64", buffer_lens=(0, 8, 16, 32, 48, 63),
+          fold_lens=(16, 32, 64, 79)):
+    """Replay cost against the committed-buffer length (32 requests, ring capacity
+    80, D = 16, 24 layer caches): (i) verify with every request's buffer at B,
+    (ii) flush alone folding n tokens of every slot. HIP events around each
+    group of 24 launches (verify) or each launch (flush, whose pointers are
+    reset by a fill before every call); bytes from the byte model."""
+    import torch
+
+    from gated_deltanet_state_replayssm_amd import synth
+    from gated_deltanet_state_replayssm_amd.cache import ReplayCache, to_device
+
+    wl = synth.WORKLOADS[workload]
+    layers = args.layers or wl.layers
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    slots = to_device(np.arange(wl.num_reqs, dtype=np.int32))
+    out = torch.empty((wl.num_reqs, wl.draft, wl.hv, wl.dv), dtype=torch.float32, device="cuda")
+    d = {k: to_device(v) for k, v in
+         synth.make_draft(wl, np.random.default_rng(synth.seed_for(wl.name, 0, 77))).items()}
+
+    def caches_with(n):
+        cs = []
+        for L in range(layers):
+            rng = np.random.default_rng(synth.seed_for(wl.name, L, 0))
+            init = synth.make_cache_init(wl, rng, init_len=np.full(wl.num_slots, n, np.int32))
+            cs.append(ReplayCache.from_numpy(init, wl.hv, wl.hk, wl.dk, wl.dv, wl.cap,
+                                             wl.in_dtype))
+        torch.cuda.synchronize()
+        return cs
+
+    def emit(kind, n, us, nbytes):
+        print(json.dumps({
+            "metric": f"GDN replay {kind} us/layer at fixed length", "kind": kind,
+            "length": int(n), "value": round(us, 2), "unit": "us/layer",
+            "hbm_gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "bytes_per_layer": int(nbytes), "steps": args.steps, "warmup": args.warmup,
+            "config": {"workload": wl.name, "requests": wl.num_reqs, "v_heads": wl.hv,
+                       "k_heads": wl.hk, "d_k": wl.dk, "d_v": wl.dv, "draft": wl.draft,
+                       "ring_cap": wl.cap, "layers": layers, "inputs": wl.in_dtype}}),
+            flush=True)
+
+    for B in buffer_lens:
+        caches = caches_with(B)
+        marks = []
+        for step in range(args.warmup + args.steps):
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            for c in caches:   # verify leaves state and pointers as they are
+                c.verify(slots, d["q"], d["k"], d["v"], d["alpha"], d["beta"], out=out)
+            e1.record(stream)
+            if step >= args.warmup:
+                marks.append((e0, e1))
+        torch.cuda.synchronize()
+        assert not any(int(c.err.item()) for c in caches)
+        us = sum(a.elapsed_time(b) for a, b in marks) * 1e3 / (len(marks) * layers)
+        v_bytes, _ = byte_model(wl, np.full(wl.num_reqs, B), [])
+        emit("verify", B, us, v_bytes)
+        del caches
+
+    for n in fold_lens:
+        caches = caches_with(n)
+        marks = []
+        for step in range(args.warmup + args.steps):
+            for c in caches:
+                c.len.fill_(n)   # every slot folds n tokens again (head moves on)
+                e0, e1 = ev(), ev()
+                e0.record(stream)
+                c.flush(slots, 1)
+                e1.record(stream)
+                if step >= args.warmup:
+                    marks.append((e0, e1))
+        torch.cuda.synchronize()
+        assert not any(int(c.err.item()) for c in caches)
+        us = sum(a.elapsed_time(b) for a, b in marks) * 1e3 / len(marks)
+        _, f_bytes = byte_model(wl, np.zeros(wl.num_reqs), [n] * wl.num_reqs)
+        emit("flush", n, us, f_bytes)
+        del caches
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -130,6 +212,10 @@ def main():
     ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--path", choices=("both", "fused", "separate"), default="both")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the step benchmark: verify at fixed committed-buffer "
+                         "lengths and flush alone at fixed fold lengths (ring capacity 80 "
+                         "workload), one JSON line per point")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="after the timed steps, copy a buffer of this many MiB once (a plain "
                          "copy kernel of known size that scales the HBM byte counters)")
@@ -148,6 +234,9 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.sweep:
+        sweep(args)
+        return
     wl = synth.WORKLOADS[args.workload]
     layers = args.layers or wl.layers
     stream = torch.cuda.current_stream()
@@ -238,12 +327,14 @@ def main():
                 b_v, b_f = byte_model(wl, sched[step]["lv"], sched[step]["folded"])
             vb += b_v * layers          # every layer sees the same lengths
             fb += b_f * layers
+        graph_ms = graph_leg(caches, sched) if path == "fused" else None
         errs = [int(c.err.item()) for c in caches]
         assert not any(errs), f"{path}: device error bits set: {errs}"
         del caches
         torch.cuda.synchronize()
         n_launch = args.steps * layers
-        r = dict(wall=wall, us_verify=tv * 1e3 / n_launch, us_rollback=tr * 1e3 / n_launch,
+        r = dict(wall=wall, graph_ms=graph_ms, us_verify=tv * 1e3 / n_launch,
+                 us_rollback=tr * 1e3 / n_launch,
                  us_flush=tf * 1e3 / n_launch if path == "separate" else 0.0,
                  v_bytes=vb / n_launch, f_bytes=fb / n_launch)
         r["us_layer"] = r["us_verify"] + r["us_flush"]
@@ -252,6 +343,38 @@ def main():
         r["v_gbps"] = r["v_bytes"] / (r["us_verify"] * 1e-6) / 1e9
         r["f_gbps"] = r["f_bytes"] / (r["us_flush"] * 1e-6) / 1e9 if r["us_flush"] > 0 else 0.0
         return r
+
+    def graph_leg(caches, sched):
+        """Secondary figure: one whole step (verify_flush then rollback on every
+        layer) captured once in a HIP graph and replayed for the timed steps'
+        schedules, whose slot permutation and accept counts are copied into the
+        graph's input buffers before each replay. Returns ms per replayed step
+        (HIP events around each replay)."""
+        slots_buf = sched[0]["slots"].clone()
+        acc_buf = sched[0]["acc"].clone()
+        d = drafts
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for L in range(layers):
+                dd = d[L][0]
+                caches[L].verify_flush(slots_buf, wl.flush_min_len, dd["q"], dd["k"], dd["v"],
+                                       dd["alpha"], dd["beta"], out=out)
+            for L in range(layers):
+                caches[L].rollback(slots_buf, wl.draft, acc_buf)
+        torch.cuda.synchronize()
+        times = []
+        for step in range(args.warmup, total):
+            slots_buf.copy_(sched[step]["slots"])
+            acc_buf.copy_(sched[step]["acc"])
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            times.append((e0, e1))
+        torch.cuda.synchronize()
+        ms = sum(a.elapsed_time(b) for a, b in times) / len(times)
+        del g
+        return ms
 
     res = {path: run_path(path) for path in paths}
     if args.copy_calib:
@@ -312,6 +435,12 @@ def main():
         "pages_context": {"b200_custom_kernel_us_per_layer": "23-24",
                           "b200_triton_us_per_layer": "72-80"},
     }
+    if "fused" in res and res["fused"]["graph_ms"] is not None:
+        gm = res["fused"]["graph_ms"]
+        line["graph_step"] = {"ms_per_step": round(gm, 4),
+                              "us_per_layer": round(gm * 1e3 / layers, 2),
+                              "what": "verify_flush + rollback on every layer, one HIP graph "
+                                      "replay per step, HIP events around each replay"}
     if "separate" in res:
         sp = res["separate"]
         line["separate_order"] = {"us_per_layer": round(sp["us_layer"], 2),

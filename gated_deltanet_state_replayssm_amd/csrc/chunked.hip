@@ -260,6 +260,15 @@ __device__ __forceinline__ Srcs make_srcs(const CacheView &c, const Unit &u, con
   return b;
 }
 
+// The thread index through an empty volatile asm: values derived from it are
+// recomputed after each call instead of being hoisted out of loops and held in
+// registers (the chunk loop's body is register-bound).
+__device__ __forceinline__ int opaque_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 // Where chunk row t (token t0 + t of the stream: B committed ring tokens, then
 // the draft when verifying) lives: its ring slot (head + token) mod C and its
 // draft index. Byte offsets for rows of the given sizes; kOOB where absent.
@@ -298,7 +307,7 @@ struct Stage {
 
   __device__ __forceinline__ void load(const Srcs &sr, const Unit &u, int t0, int Treal,
                                        bool out_chunk) {
-    const int tid = threadIdx.x;
+    const int tid = opaque_tid();
 #pragma unroll
     for (int it = 0; it < IK; ++it) {
       const int p = tid + it * THREADS, t = p / PK, part = p % PK;
@@ -334,7 +343,7 @@ struct Stage {
   }
 
   __device__ __forceinline__ void store(Smem<DK, DV> &sm, int Treal, bool out_chunk) {
-    const int tid = threadIdx.x;
+    const int tid = opaque_tid();
 #pragma unroll
     for (int it = 0; it < IK; ++it) {
       const int p = tid + it * THREADS, t = p / PK, part = p % PK;
@@ -366,7 +375,7 @@ struct Stage {
   // from LDS (one workgroup per key head writes k and q).
   __device__ __forceinline__ void append(const Smem<DK, DV> &sm, const Srcs &sr, const Unit &u,
                                          int t0, int Treal, bool kq_writer) const {
-    const int tid = threadIdx.x;
+    const int tid = opaque_tid();
     // Recompute the row offsets here rather than keep those of the loads alive
     // in registers through the whole kernel: the copy of the unit is opaque to
     // the compiler, so it cannot reuse them.
@@ -848,23 +857,26 @@ __device__ __forceinline__ void fold_state(const Smem<DK, DV> &sm, const f32x4 (
   }
 }
 
-// One workgroup per (request, value head). VERIFY: outputs of the draft, state
-// untouched. !VERIFY (flush): fold all committed tokens, write the state back,
-// move the pointers. Chunks are cut from the end of the token stream so the
-// last one (verify's output chunk) holds the whole draft (D <= 32).
+// One workgroup per (request, value head), any ring capacity. VERIFY: outputs of
+// the draft, state untouched. !VERIFY (flush): fold all committed tokens, write
+// the state back, move the pointers. The token stream (B committed ring tokens,
+// then the draft when verifying) is cut into chunks of 32 from its end, so the
+// last chunk (verify's output chunk) holds the whole draft (D <= 32); every other
+// chunk is folded into the state held in registers.
 //
-// Per chunk: all threads stage the chunk's inputs; wave 0 builds the T x T
-// matrices (decay table, Gram matrices, (I + A)^-1) using only wave-local LDS
-// ordering while every wave computes Y = K H; after one barrier every wave
-// forms X, W and either the draft outputs or the fold of its state columns.
+// Chunk 0 is staged by waves 0..SW-1 while waves SW.. load their state columns
+// (as in replay_single); later chunks are staged by all waves. Per chunk: wave 0
+// builds the decays, A and (I + A)^-1, wave 1 the output chunk's C, one barrier,
+// then every wave contracts its state columns and forms W and either the
+// outputs or the fold. The chunk loop is not unrolled: its body is the
+// register-bound part, and one copy of it keeps the kernel at 4 workgroups per CU.
 template <int DK, int DV, int NT, bool VERIFY>
-__global__ __launch_bounds__(64 * (DV / (16 * NT)), 2) void replay_chunked(VerifyArgs va,
+__global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_chunked(VerifyArgs va,
                                                                            FlushArgs fa) {
   constexpr int WAVES = DV / (16 * NT);
-  constexpr int MT = DK / 16;   // 16-row tiles of the state
-  constexpr int KS = DK / 32;   // k-steps of a contraction over d_k
+  constexpr int MT = DK / 16;
   static_assert(DK % 32 == 0 && DV % (16 * NT) == 0 && (NT == 2 || NT == 4), "tile shape");
-  static_assert(WAVES >= 1, "at least one wave");
+  static_assert(WAVES >= 2, "the T x T matrices are built by waves 0 and 1");
   typedef typename Cols<NT>::F F;
   __shared__ Smem<DK, DV> sm;
 
@@ -873,8 +885,19 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 2) void replay_chunked(Verif
   const int r = blockIdx.x / HV, h = blockIdx.x % HV;
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
   const int g = lane >> 4, l16 = lane & 15;
-  const int colL = wave * 16 * NT + NT * l16;  // this lane's first state column
   const bool lead = (h == 0 && tid == 0);
+  // this lane's first state column and its byte offset in the state tile,
+  // recomputed where used from an opaque copy of the thread index
+  auto col_of = [&]() {
+    int t = tid;
+    asm volatile("" : "+v"(t));
+    return (t / 64) * 16 * NT + NT * (t & 15);
+  };
+  auto st_off_of = [&]() {
+    int t = tid;
+    asm volatile("" : "+v"(t));
+    return (uint32_t)((4 * ((t & 63) >> 4) * DV + (t / 64) * 16 * NT + NT * (t & 15)) * 4);
+  };
 
   const int s = VERIFY ? va.slot_idx[r] : fa.slot_idx[r];
   if (s < 0 || s >= c.num_slots) {
@@ -902,57 +925,83 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 2) void replay_chunked(Verif
   const int nchunks = (T + kCh - 1) / kCh;
   const int T0 = T - kCh * (nchunks - 1);  // tokens in the first chunk (1..32)
   const Rsrc st = make_rsrc(c.state + ((int64_t)s * HV + h) * DK * DV, DK * DV * 4);
-  const uint32_t st_off = (4 * g * DV + colL) * 4;
-
-  // ---- first chunk's small inputs, then the whole state tile: waiting for the
-  // former (loads complete in issue order) leaves the state loads in flight
   const Srcs sr = make_srcs<DK, DV>(c, u, &va, VERIFY);
-  const int Ggrp = HV / c.hk;
-  Stage<DK, DV, NT, VERIFY> sg;
-  sg.load(sr, u, 0, T0, VERIFY && nchunks == 1);
-  __builtin_amdgcn_sched_barrier(0);
-  // H[mt][i][nt] = state[16 mt + 4 g + i][colL + nt]: kept in the layout of the
-  // loads so that nothing has to wait for them before it is used
-  F H[MT][4];
-  load_state<DK, DV, NT>(st, st_off, H);
-  __builtin_amdgcn_sched_barrier(0);
+  const bool kq_writer = h % (HV / c.hk) == 0;
 
-  // One chunk; the first is peeled off the loop below so that the state loads
-  // can still be in flight while its inputs are staged and its matrices built.
-  auto chunk = [&](int ch) {
+  constexpr int SW = WAVES >= 4 ? 2 : WAVES;
+  F H[MT][4];
+  float al;  // staged alpha of token lane % 32 of the current chunk (waves 0 and 1)
+  {
+    Stage<DK, DV, NT, VERIFY, 64 * SW> sg0;
+    const bool out0 = VERIFY && nchunks == 1;
+    if (wave >= SW) {
+      load_state<DK, DV, NT>(st, st_off_of(), H);
+      al = 1.f;
+    } else {
+      sg0.load(sr, u, 0, T0, out0);
+      sg0.store(sm, T0, out0);
+      al = sg0.al;
+      __builtin_amdgcn_sched_barrier(0);
+      load_state<DK, DV, NT>(st, st_off_of(), H);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+  }
+
+  // every chunk but verify's last: fold into the state
+  const int nfold = VERIFY ? nchunks - 1 : nchunks;
+#pragma nounroll
+  for (int ch = 0; ch < nfold; ++ch) {
+    const int lane = opaque_tid() % 64, g = lane >> 4, l16 = lane & 15;
     const int t0 = ch == 0 ? 0 : T0 + kCh * (ch - 1);
     const int Treal = ch == 0 ? T0 : kCh;
-    const bool out_chunk = VERIFY && (ch + 1 == nchunks);  // holds the draft
-    if (ch > 0) sg.load(sr, u, t0, Treal, out_chunk);
-    sg.store(sm, Treal, out_chunk);
-    __syncthreads();
-
-    if (wave == 0) {
-      build_tt<DK, DV>(sm, sg.al, lane, g, l16);
-      if (WAVES == 1 && out_chunk) build_c<DK, DV>(sm, sg.al, lane, g, l16);
-    } else if (wave == 1 && out_chunk) {
-      build_c<DK, DV>(sm, sg.al, lane, g, l16);
+    if (ch > 0) {
+      Stage<DK, DV, NT, VERIFY> sg;
+      sg.load(sr, u, t0, Treal, false);
+      sg.store(sm, Treal, false);
+      al = sg.al;
+      __syncthreads();
     }
-
+    if (wave == 0) build_tt<DK, DV>(sm, al, lane, g, l16);
+    __syncthreads();  // T x T matrices complete
     f32x4 Y[2][NT], Z[2][NT], Wm[2][NT];
     contract<DK, DV, NT, kY>(sm, H, g, l16, Y, Z);
-    __syncthreads();  // T x T matrices complete
-    solve_w<DK, DV, NT>(sm, Y, colL, g, l16, Wm);
-    if (out_chunk) {
-      contract<DK, DV, NT, kZ>(sm, H, g, l16, Y, Z);
-      emit_outputs<DK, DV, NT>(sm, Z, Wm, g, l16, t0, Treal, u.B, out_rsrc(va, r, h, DV), colL * 4,
-                           HV * DV * 4);
-      sg.append(sm, sr, u, t0, Treal, h % Ggrp == 0);
-    } else {
-      fold_state<DK, DV, NT>(sm, Wm, g, l16, H);
-    }
+    solve_w<DK, DV, NT>(sm, Y, col_of(), g, l16, Wm);
+    fold_state<DK, DV, NT>(sm, Wm, g, l16, H);
     __syncthreads();  // LDS is rewritten by the next chunk
-  };
-  chunk(0);
-  for (int ch = 1; ch < nchunks; ++ch) chunk(ch);
+  }
+
+  if constexpr (VERIFY) {
+    // the output chunk: the draft and the committed tokens before it
+    const int t0 = nchunks == 1 ? 0 : T0 + kCh * (nchunks - 2);
+    const int Treal = nchunks == 1 ? T0 : kCh;
+    if (nchunks > 1) {
+      Stage<DK, DV, NT, VERIFY> sg;
+      sg.load(sr, u, t0, Treal, true);
+      sg.store(sm, Treal, true);
+      al = sg.al;
+      __syncthreads();
+    }
+    if (wave == 0)
+      build_tt<DK, DV>(sm, al, lane, g, l16);
+    else if (wave == 1)
+      build_c<DK, DV>(sm, al, lane, g, l16);
+    __syncthreads();  // T x T matrices complete
+    f32x4 Y[2][NT], Z[2][NT], Wm[2][NT];
+    contract<DK, DV, NT, kY | kZ>(sm, H, g, l16, Y, Z);
+    solve_w<DK, DV, NT>(sm, Y, col_of(), g, l16, Wm);
+    emit_outputs<DK, DV, NT>(sm, Z, Wm, g, l16, t0, Treal, u.B, out_rsrc(va, r, h, DV),
+                             col_of() * 4, HV * DV * 4);
+    // the draft rows, from LDS; the thread mapping is that of the stage type
+    if (nchunks == 1) {
+      if (wave < SW) Stage<DK, DV, NT, VERIFY, 64 * SW>{}.append(sm, sr, u, t0, Treal, kq_writer);
+    } else {
+      Stage<DK, DV, NT, VERIFY>{}.append(sm, sr, u, t0, Treal, kq_writer);
+    }
+  }
 
   if constexpr (!VERIFY) {
-    store_state<DK, DV, NT>(st, st_off, H);
+    store_state<DK, DV, NT>(st, st_off_of(), H);
     // The last workgroup of this slot to arrive moves the pointers. Every
     // workgroup's head/len loads were consumed (by the branches above) before
     // its arrival, so none can observe the update; no memory fence is needed

@@ -95,6 +95,24 @@ def test_flush_heavy_long_buffers():
         p.flush(slots, 1, f"B={B}")
 
 
+@pytest.mark.parametrize("d", [128, 64])
+def test_long_rings_many_chunks(d):
+    """Ring capacity 256 with a 32-token draft: replays of up to 8 chunks, with
+    chunk boundaries inside the committed tokens and right before the draft."""
+    C, D = 256, 32
+    wl = synth.Workload("lr", 2, 2, 4, 2, d, d, C, D, synth.BF16, 1, 1, "fixed:7",
+                        "fixed:0")
+    rng = np.random.default_rng(41 + d)
+    for B in (0, 1, 31, 32, 33, 100, 224):
+        say(f"case long ring d={d} C={C} D={D} B={B}")
+        init = synth.make_cache_init(wl, rng, init_len=[B] * wl.num_slots)
+        p = Pair(wl, init)
+        slots = synth.make_slot_idx(wl, rng)
+        p.verify(slots, synth.make_draft(wl, rng), f"B={B}")
+        p.rollback(slots, wl.draft, synth.sample_accepted(wl, rng), f"B={B}")
+        p.flush(slots, 1, f"B={B}")
+
+
 def test_stress_batch_sampled():
     wl = W["r128_hv32_hk16_d128_f16"]
     say("case r128_hv32_hk16_d128_f16, sampled")

@@ -75,6 +75,7 @@ class Workload:
     layers: int
     accept: str         # "fixed:<a>", "uniform", "clipnormal:<mu>:<sd>", "uniform_forced"
     init_len: str       # "fixed:<b>", "uniform:<lo>:<hi>"
+    draft_lens: str = "fixed"  # "fixed" (every request drafts `draft`) or "uniform:<lo>:<hi>"
 
     @property
     def in_bytes(self) -> int:
@@ -98,6 +99,13 @@ WORKLOADS = {
     "r128_hv32_hk16_d128_f16": Workload("r128_hv32_hk16_d128_f16", 128, 128, 32, 16, 128,
                                         128, 32, 16, BF16, 16, 24, "uniform_forced",
                                         "fixed:0"),
+    # plain decode (no speculation): one token per request and step, always kept
+    "r32_hv32_hk16_d128_d1": Workload("r32_hv32_hk16_d128_d1", 32, 32, 32, 16, 128, 128, 32,
+                                      1, BF16, 16, 24, "fixed:1", "fixed:0"),
+    # per-request draft lengths U{1..16} (adaptive speculation), accept clipped to each
+    "r32_hv32_hk16_d128_varlen": Workload("r32_hv32_hk16_d128_varlen", 32, 32, 32, 16, 128,
+                                          128, 32, 16, BF16, 16, 24, "clipnormal:12:3",
+                                          "fixed:0", "uniform:1:16"),
 }
 
 # index used in the per-workload seed formula
@@ -170,25 +178,41 @@ def make_slot_idx(wl: Workload, rng: np.random.Generator, num_reqs=None) -> np.n
     return rng.permutation(wl.num_slots)[:R].astype(np.int32)
 
 
-def sample_accepted(wl: Workload, rng: np.random.Generator, num_reqs=None, draft=None):
+def sample_draft_lens(wl: Workload, rng: np.random.Generator, num_reqs=None):
+    """Per-request draft lengths, or None when every request drafts wl.draft."""
+    R = wl.num_reqs if num_reqs is None else num_reqs
+    kind, *args = wl.draft_lens.split(":")
+    if kind == "fixed":
+        return None
+    if kind == "uniform":
+        lo, hi = int(args[0]), int(args[1])
+        return rng.integers(lo, hi + 1, R).astype(np.int32)
+    raise ValueError(wl.draft_lens)
+
+
+def sample_accepted(wl: Workload, rng: np.random.Generator, num_reqs=None, draft=None,
+                    draft_lens=None):
+    """Accepted counts a_i in [0, D_i] (D_i = draft_lens[i] when given)."""
     R = wl.num_reqs if num_reqs is None else num_reqs
     D = wl.draft if draft is None else draft
+    if draft_lens is not None:
+        D = np.asarray(draft_lens, dtype=np.int64)
     kind, *args = wl.accept.split(":")
     if kind == "fixed":
-        a = np.full(R, int(args[0]))
+        a = np.minimum(np.full(R, int(args[0])), D)
     elif kind == "uniform":
-        a = rng.integers(0, D + 1, R)
+        a = rng.integers(0, np.asarray(D) + 1, R)
     elif kind == "uniform_forced":
-        a = rng.integers(0, D + 1, R)
+        a = rng.integers(0, np.asarray(D) + 1, R)
         if R >= 2:
             i, j = rng.choice(R, 2, replace=False)
-            a[i], a[j] = 0, D
+            a[i], a[j] = 0, np.broadcast_to(D, (R,))[j]
     elif kind == "clipnormal":
         mu, sd = float(args[0]), float(args[1])
         a = np.clip(np.rint(rng.normal(mu, sd, R)), 0, D)
     else:
         raise ValueError(wl.accept)
-    return a.astype(np.int32)
+    return np.asarray(a).astype(np.int32)
 
 
 def canonical(workload: str) -> Workload:

@@ -49,8 +49,14 @@ Readings taken where the pages are silent (each listed in the design notes)
 * contract violations skip the request and OR a bit into a sticky error word:
   CAPACITY (len + D > C at verify, len + a > C at rollback), ACCEPT
   (a outside [0, D]), SLOT (slot index outside [0, num_slots)), POINTER
-  (head outside [0, C) or len outside [0, C]).
+  (head outside [0, C) or len outside [0, C]), DRAFT (a per-request draft
+  length outside [0, D_max]).
 * a buffered token's q is never read.
+* per-request draft lengths: request i drafts D_i <= D_max tokens, the first
+  D_i rows of its D_max-row block; D_i = 1 is plain (non-speculative) decode
+  and D_i = 0 leaves the request without a draft (nothing appended, no outputs,
+  its flush still happens in verify_flush). Rows past D_i are neither read nor
+  written.
 """
 from __future__ import annotations
 
@@ -60,6 +66,17 @@ ERR_CAPACITY = 1
 ERR_ACCEPT = 2
 ERR_SLOT = 4
 ERR_POINTER = 8
+ERR_DRAFT = 16
+
+
+def per_request_lengths(draft_lens, num_reqs: int, d_max: int) -> np.ndarray:
+    """Draft length of every request: d_max for all, or the given per-request
+    values (checked against [0, d_max] by the calls)."""
+    if draft_lens is None:
+        return np.full(num_reqs, d_max, dtype=np.int64)
+    out = np.asarray(draft_lens, dtype=np.int64).reshape(-1)
+    assert out.shape[0] == num_reqs
+    return out
 
 
 def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
@@ -164,19 +181,25 @@ class ReplayOracle:
         return True
 
     # -- the three calls ------------------------------------------------------
-    def verify(self, slot_idx, q, k, v, alpha, beta) -> np.ndarray:
-        """Outputs of the draft block [R, D, HV, dv] (NaN rows for skipped requests).
+    def verify(self, slot_idx, q, k, v, alpha, beta, draft_lens=None) -> np.ndarray:
+        """Outputs of the draft block [R, D, HV, dv] (NaN rows for skipped requests
+        and for rows past a request's draft length).
 
         out[i, j, h] = S q_j for the state after draft token j of request i,
         starting from the state after the committed tokens. The draft is
         appended to the ring; checkpoint, head and len are not changed."""
         slot_idx = np.asarray(slot_idx)
-        R, D = np.asarray(alpha).shape[:2]
+        R, Dmax = np.asarray(alpha).shape[:2]
+        Ds = per_request_lengths(draft_lens, R, Dmax)
         assert len(set(int(s) for s in slot_idx)) == len(slot_idx), "slots must be unique"
-        out = np.full((R, D, self.hv, self.dv), np.nan)
+        out = np.full((R, Dmax, self.hv, self.dv), np.nan)
         for i in range(R):
             s = int(slot_idx[i])
             if not self._slot_ok(s):
+                continue
+            D = int(Ds[i])
+            if D < 0 or D > Dmax:
+                self.err |= ERR_DRAFT
                 continue
             n = int(self.len[s])
             if n + D > self.cap:
@@ -207,13 +230,19 @@ class ReplayOracle:
                 self.S_live[s] = S                      # live state moved speculatively
         return out
 
-    def rollback(self, slot_idx, draft_len: int, num_accepted) -> None:
-        """Commit the first a tokens of the last appended draft: len += a."""
-        for s, a in zip(np.asarray(slot_idx), np.asarray(num_accepted)):
-            s, a = int(s), int(a)
+    def rollback(self, slot_idx, draft_len: int, num_accepted, draft_lens=None) -> None:
+        """Commit the first a tokens of the last appended draft: len += a, with
+        0 <= a <= the request's draft length."""
+        slot_idx = np.asarray(slot_idx)
+        Ds = per_request_lengths(draft_lens, len(slot_idx), draft_len)
+        for s, a, D in zip(slot_idx, np.asarray(num_accepted), Ds):
+            s, a, D = int(s), int(a), int(D)
             if not self._slot_ok(s):
                 continue
-            if a < 0 or a > draft_len:
+            if D < 0 or D > draft_len:
+                self.err |= ERR_DRAFT
+                continue
+            if a < 0 or a > D:
                 self.err |= ERR_ACCEPT
                 continue
             n = int(self.len[s])
@@ -244,13 +273,24 @@ class ReplayOracle:
             self.head[s] = (int(self.head[s]) + n) % self.cap
             self.len[s] = 0
 
-    def verify_flush(self, slot_idx, min_len: int, q, k, v, alpha, beta) -> np.ndarray:
+    def verify_flush(self, slot_idx, min_len: int, q, k, v, alpha, beta,
+                     draft_lens=None) -> np.ndarray:
         """The periodic flush folded into the next verify: flush(min_len), then
         verify from the resulting checkpoint, pointers and ring. A slot that is
         not due and has len + D > C is skipped by verify (CAPACITY) after a flush
-        that did not touch it, so the call writes nothing for it."""
-        self.flush(slot_idx, min_len)
-        return self.verify(slot_idx, q, k, v, alpha, beta)
+        that did not touch it, so the call writes nothing for it. A request whose
+        draft length is outside [0, D_max] is skipped entirely (DRAFT, no flush)."""
+        slot_idx = np.asarray(slot_idx)
+        R, Dmax = np.asarray(alpha).shape[:2]
+        Ds = per_request_lengths(draft_lens, R, Dmax)
+        # checks in the order slot, pointers, draft length: a request with a bad
+        # length is flushed by nobody; verify then flags it (DRAFT) and skips it
+        slot_ok = np.array([0 <= int(s) < self.num_slots
+                            and 0 <= self.head[int(s)] < self.cap
+                            and 0 <= self.len[int(s)] <= self.cap for s in slot_idx], dtype=bool)
+        bad = slot_ok & ((Ds < 0) | (Ds > Dmax))
+        self.flush(slot_idx[~bad], min_len)
+        return self.verify(slot_idx, q, k, v, alpha, beta, draft_lens=Ds)
 
     # -- views in the library's layouts -----------------------------------------
     def state_abi(self) -> np.ndarray:

@@ -131,3 +131,43 @@ def test_verify_flush_is_flush_then_verify_on_the_model():
     folded, written = m2.verify_flush([0], 2, 8)    # not due, 7 + 2 > 8
     assert folded == {} and written == {} and m2.err == 1
     assert m2.head == [0] and m2.len == [7]
+
+
+def test_integer_model_matches_oracle_with_per_request_draft_lengths():
+    """Per-request draft lengths (including 0 and out-of-range values): the
+    integer model and the oracle agree on pointers and error bits, through
+    both the separate and the fused order."""
+    wl = synth.Workload("t", 4, 6, 2, 1, 4, 4, 12, 5, synth.F32, 6, 1, "uniform", "uniform:0:7")
+    rng = np.random.default_rng(23)
+    init = synth.make_cache_init(wl, rng)
+    orc = go.ReplayOracle(init, 2, 1, 4, 4, wl.cap, mode="replay")
+    m = bk.RingPointers(init["head"], init["len"], wl.cap)
+    for step in range(80):
+        slots = synth.make_slot_idx(wl, rng)
+        dmax = int(rng.integers(1, wl.draft + 1))
+        dl = rng.integers(-1, dmax + 2, len(slots)).astype(np.int32)   # includes invalid
+        dr = synth.make_draft(wl, rng, draft=dmax)
+        fl = int(rng.integers(0, 9))
+        if step % 2:
+            orc.verify_flush(slots, fl, dr["q"], dr["k"], dr["v"], dr["alpha"], dr["beta"],
+                             draft_lens=dl)
+            m.verify_flush(slots, list(dl), fl, dmax)
+        else:
+            orc.verify(slots, dr["q"], dr["k"], dr["v"], dr["alpha"], dr["beta"], draft_lens=dl)
+            m.verify(slots, list(dl), dmax)
+        acc = rng.integers(-1, dmax + 2, len(slots))
+        orc.rollback(slots, dmax, acc, draft_lens=dl)
+        m.rollback(slots, list(dl), acc, dmax)
+        if step % 2 == 0:
+            orc.flush(slots, fl)
+            m.flush(slots, fl)
+        assert list(orc.head) == m.head and list(orc.len) == m.len and orc.err == m.err
+    assert orc.err & bk.ERR_DRAFT
+
+
+def test_per_request_written_positions():
+    m = bk.RingPointers([3, 10, 0], [2, 1, 5], 12)
+    w = m.verify([0, 1, 2], [4, 3, 0], 4)
+    assert w == {0: [5, 6, 7, 8], 1: [11, 0, 1], 2: []} and m.err == 0
+    w = m.verify([0, 1], [5, -1], 4)
+    assert w == {} and m.err == bk.ERR_DRAFT

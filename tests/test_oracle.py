@@ -273,7 +273,8 @@ def test_contraction_bound():
 
 def _run_schedule(wl, mode, steps, seed, flush_min_len, collect=True, fused=False):
     """Random verify/rollback/flush schedule (fused: verify_flush/rollback, the
-    flush folded into the next verify); returns (oracle, accepted outputs per slot)."""
+    flush folded into the next verify; per-request draft lengths when the
+    workload draws them); returns (oracle, accepted outputs per slot)."""
     rng = np.random.default_rng(seed)
     init = synth.make_cache_init(wl, rng)
     orc = go.ReplayOracle(init, wl.hv, wl.hk, wl.dk, wl.dv, wl.cap, mode=mode)
@@ -282,13 +283,15 @@ def _run_schedule(wl, mode, steps, seed, flush_min_len, collect=True, fused=Fals
     for _ in range(steps):
         slots = synth.make_slot_idx(wl, rng)
         dr = synth.make_draft(wl, rng)
-        acc = synth.sample_accepted(wl, rng)
+        dl = synth.sample_draft_lens(wl, rng)
+        acc = synth.sample_accepted(wl, rng, draft_lens=dl)
         if fused:
             out = orc.verify_flush(slots, flush_min_len, dr["q"], dr["k"], dr["v"], dr["alpha"],
-                                   dr["beta"])
+                                   dr["beta"], draft_lens=dl)
         else:
-            out = orc.verify(slots, dr["q"], dr["k"], dr["v"], dr["alpha"], dr["beta"])
-        orc.rollback(slots, wl.draft, acc)
+            out = orc.verify(slots, dr["q"], dr["k"], dr["v"], dr["alpha"], dr["beta"],
+                             draft_lens=dl)
+        orc.rollback(slots, wl.draft, acc, draft_lens=dl)
         if not fused:
             orc.flush(slots, flush_min_len)
         for i, s in enumerate(slots):
@@ -299,13 +302,23 @@ def _run_schedule(wl, mode, steps, seed, flush_min_len, collect=True, fused=Fals
 
 
 @pytest.mark.parametrize("fused", [False, True])
-def test_replay_equals_sequential_recurrence(fused):
+@pytest.mark.parametrize("drafts", ["fixed", "varlen", "decode"])
+def test_replay_equals_sequential_recurrence(fused, drafts):
     """P8: accepted outputs over many steps with flushes = one plain sequential
     run over each slot's committed token stream from the initial checkpoint
-    (also with the flush folded into the next verify)."""
-    wl = synth.Workload("t", 3, 4, 4, 2, 8, 6, 12, 4, synth.F32, 5, 1, "uniform", "uniform:0:4")
+    (also with the flush folded into the next verify, with per-request draft
+    lengths 0..D, and as plain decode: D = 1 with every token kept)."""
+    if drafts == "decode":
+        wl = synth.Workload("t", 3, 4, 4, 2, 8, 6, 12, 1, synth.F32, 5, 1, "fixed:1",
+                            "uniform:0:4")
+    else:
+        wl = synth.Workload("t", 3, 4, 4, 2, 8, 6, 12, 4, synth.F32, 5, 1, "uniform",
+                            "uniform:0:4", "uniform:0:4" if drafts == "varlen" else "fixed")
     orc, init, accepted, stream = _run_schedule(wl, "replay", 12, 11, wl.flush_min_len,
                                                 fused=fused)
+    assert orc.err == 0
+    if drafts == "decode":
+        assert all(len(stream[s]) > 0 for s in range(wl.num_slots) if len(accepted[s]))
     if fused:
         assert (orc.len < wl.flush_min_len + wl.draft).all()
     G = wl.hv // wl.hk
@@ -326,9 +339,12 @@ def test_replay_equals_sequential_recurrence(fused):
             np.testing.assert_allclose(o, np.einsum("hij,hj->hi", S, q), rtol=0, atol=1e-11)
 
 
-def test_snapshot_mode_equals_replay_mode():
-    """P9: explicit snapshot/restore on rejection == pointer-only replay, bitwise."""
-    wl = synth.Workload("t", 3, 5, 4, 2, 8, 8, 16, 5, synth.F32, 4, 1, "uniform", "uniform:0:6")
+@pytest.mark.parametrize("drafts", ["fixed", "uniform:0:5"])
+def test_snapshot_mode_equals_replay_mode(drafts):
+    """P9: explicit snapshot/restore on rejection == pointer-only replay, bitwise
+    (also with per-request draft lengths)."""
+    wl = synth.Workload("t", 3, 5, 4, 2, 8, 8, 16, 5, synth.F32, 4, 1, "uniform", "uniform:0:6",
+                        drafts)
     o1, *_ = _run_schedule(wl, "snapshot", 10, 12, 4)
     o2, *_ = _run_schedule(wl, "replay", 10, 12, 4)
     assert np.array_equal(o1.S_ckpt, o2.S_ckpt)
@@ -401,6 +417,78 @@ def test_error_bits_and_skips():
     assert orc.err == go.ERR_CAPACITY | go.ERR_ACCEPT and orc.len[0] == 5
     orc.flush([3], 1)
     assert orc.err == 7 and orc.len[0] == 5
+
+
+def _clone(orc):
+    c = go.ReplayOracle.__new__(go.ReplayOracle)
+    c.__dict__ = {k: (v.copy() if isinstance(v, np.ndarray) else
+                      ({kk: vv.copy() for kk, vv in v.items()} if isinstance(v, dict) else v))
+                  for k, v in orc.__dict__.items()}
+    return c
+
+
+def test_varlen_equals_one_request_at_a_time():
+    """Per-request draft lengths: one varlen call = every request verified alone
+    with its own fixed draft length (its first D_i rows); rows past D_i stay
+    unwritten and the ring past the appended rows is unchanged."""
+    wl = synth.Workload("t", 4, 6, 4, 2, 8, 8, 16, 6, synth.BF16, 1, 1, "uniform", "uniform:0:8")
+    rng = np.random.default_rng(21)
+    init = synth.make_cache_init(wl, rng)
+    dr = synth.make_draft(wl, rng)
+    slots = synth.make_slot_idx(wl, rng)
+    dl = np.array([0, 1, 6, 3], np.int32)
+    a = go.ReplayOracle(init, wl.hv, wl.hk, wl.dk, wl.dv, wl.cap, mode="replay")
+    b = _clone(a)
+    out = a.verify(slots, dr["q"], dr["k"], dr["v"], dr["alpha"], dr["beta"], draft_lens=dl)
+    for i, s in enumerate(slots):
+        D = int(dl[i])
+        assert np.isnan(out[i, D:]).all()
+        if D == 0:
+            continue
+        sub = {x: dr[x][i:i + 1, :D] for x in dr}
+        o = b.verify([s], sub["q"], sub["k"], sub["v"], sub["alpha"], sub["beta"])
+        np.testing.assert_array_equal(out[i, :D], o[0])
+    for x in ("ring_q", "ring_k", "ring_v", "ring_alpha", "ring_beta"):
+        assert np.array_equal(getattr(a, x), getattr(b, x)), x
+    assert a.err == b.err == 0
+    # rollback bounds follow each request's own length
+    a.rollback(slots, wl.draft, np.array([0, 1, 6, 3]), draft_lens=dl)
+    assert a.err == 0 and (a.len[slots] == init["len"][slots] + [0, 1, 6, 3]).all()
+    a.rollback(slots[:2], wl.draft, np.array([1, 2]), draft_lens=dl[:2])
+    assert a.err == go.ERR_ACCEPT
+
+
+def test_varlen_draft_errors_and_empty_drafts():
+    """A length outside [0, D_max] sets DRAFT and leaves the request untouched
+    (verify_flush does not flush it either); D_i = 0 appends nothing, emits
+    nothing and still lets verify_flush fold a due slot."""
+    wl = synth.Workload("t", 4, 4, 2, 1, 8, 8, 16, 4, synth.F32, 1, 1, "uniform", "fixed:6")
+    rng = np.random.default_rng(22)
+    init = synth.make_cache_init(wl, rng)
+    dr = synth.make_draft(wl, rng)
+    slots = np.arange(4, dtype=np.int32)
+    orc = go.ReplayOracle(init, wl.hv, wl.hk, wl.dk, wl.dv, wl.cap, mode="replay")
+    before = _clone(orc)
+    out = orc.verify_flush(slots, 6, dr["q"], dr["k"], dr["v"], dr["alpha"], dr["beta"],
+                           draft_lens=np.array([-1, 5, 0, 4], np.int32))
+    assert orc.err == go.ERR_DRAFT
+    assert np.isnan(out[0]).all() and np.isnan(out[1]).all() and np.isnan(out[2]).all()
+    assert not np.isnan(out[3]).any()
+    # bad lengths: no flush, no append
+    for s in (0, 1):
+        assert orc.len[s] == 6 and orc.head[s] == before.head[s]
+        assert np.array_equal(orc.S_ckpt[s], before.S_ckpt[s])
+        assert np.array_equal(orc.ring_k[s], before.ring_k[s])
+    # empty draft: folded (due), nothing appended
+    assert orc.len[2] == 0 and orc.head[2] == (before.head[2] + 6) % wl.cap
+    assert np.array_equal(orc.ring_k[2], before.ring_k[2])
+    ref = _clone(before)
+    ref.flush([2], 6)
+    assert np.array_equal(orc.S_ckpt[2], ref.S_ckpt[2])
+    # rollback of a bad length: DRAFT, untouched
+    orc.err = 0
+    orc.rollback(slots, 4, np.array([0, 0, 0, 2]), draft_lens=np.array([7, 0, 0, 4]))
+    assert orc.err == go.ERR_DRAFT and orc.len[3] == 2 and orc.len[0] == 6
 
 
 # ---------------------------------------------------------------------------

@@ -24,8 +24,10 @@ PIN_TESTS = [
     lambda: pins.test_scalar_recurrence_closed_form(),
     lambda: pins.test_state_layout_is_transpose(),
     lambda: pins.test_linearity_in_state_and_values(),
-    lambda: pins.test_replay_equals_sequential_recurrence(False),
-    lambda: pins.test_replay_equals_sequential_recurrence(True),
+    lambda: pins.test_replay_equals_sequential_recurrence(False, "fixed"),
+    lambda: pins.test_replay_equals_sequential_recurrence(True, "fixed"),
+    lambda: pins.test_replay_equals_sequential_recurrence(False, "varlen"),
+    lambda: pins.test_replay_equals_sequential_recurrence(True, "decode"),
     lambda: pins.test_rollback_prefix_equals_recurrence_over_prefix(),
     lambda: pins.test_flush_then_verify_equals_verify_without_flush(),
     lambda: pins.test_gva_head_grouping(),
@@ -92,9 +94,9 @@ def _flush_bad_head(self, slot_idx, min_len):
 _orig_verify = go.ReplayOracle.verify
 
 
-def _verify_output_before_update(self, slot_idx, q, k, v, alpha, beta):
+def _verify_output_before_update(self, slot_idx, q, k, v, alpha, beta, draft_lens=None):
     # emits S_{t-1} q_t: shift each request's outputs by one token
-    out = _orig_verify(self, slot_idx, q, k, v, alpha, beta)
+    out = _orig_verify(self, slot_idx, q, k, v, alpha, beta, draft_lens)
     return np.concatenate([out[:, :1] * 0.0 + out[:, :1], out[:, :-1]], axis=1)
 
 

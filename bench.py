@@ -63,31 +63,43 @@ def measured_traffic(kernel: str):
     return None
 
 
-def byte_model(wl, lens_at_verify, folded):
+def byte_model(wl, lens_at_verify, folded, drafts=None):
     """Algorithmic HBM bytes of one layer's verify and flush calls.
 
-    verify: state read R*HV*dk*dv*4; committed ring read sum_r B_r*(HK*dk*ib +
-    HV*dv*ib + HV*8); draft read and ring append R*D*(2*HK*dk*ib + HV*dv*ib +
-    HV*8) each (q is appended too); out write R*D*HV*dv*4.
+    verify: state read R*HV*dk*dv*4 (requests with a draft); committed ring read
+    sum_r B_r*(HK*dk*ib + HV*dv*ib + HV*8); draft read and ring append
+    sum_r D_r*(2*HK*dk*ib + HV*dv*ib + HV*8) each (q is appended too); out write
+    sum_r D_r*HV*dv*4. drafts: per-request D_r (default D for every request).
     flush: for each folded slot, state read + write HV*dk*dv*8 and ring read
     n*(HK*dk*ib + HV*dv*ib + HV*8)."""
     ib = wl.in_bytes
-    R, D, HV, HK, dk, dv = wl.num_reqs, wl.draft, wl.hv, wl.hk, wl.dk, wl.dv
+    R, HV, HK, dk, dv = wl.num_reqs, wl.hv, wl.hk, wl.dk, wl.dv
+    Ds = np.full(R, wl.draft) if drafts is None else np.asarray(drafts)
+    with_draft = Ds > 0
     tok_ring = HK * dk * ib + HV * dv * ib + HV * 8
     tok_draft = 2 * HK * dk * ib + HV * dv * ib + HV * 8
-    v_bytes = (R * HV * dk * dv * 4 + int(np.sum(lens_at_verify)) * tok_ring
-               + 2 * R * D * tok_draft + R * D * HV * dv * 4)
+    v_bytes = (int(with_draft.sum()) * HV * dk * dv * 4
+               + int(np.sum(np.asarray(lens_at_verify)[with_draft])) * tok_ring
+               + int(Ds.sum()) * (2 * tok_draft + HV * dv * 4))
     f_bytes = sum(HV * dk * dv * 8 + int(n) * tok_ring for n in folded)
     return v_bytes, f_bytes
 
 
-def byte_model_fused(wl, lens_at_call, folded):
+def byte_model_fused(wl, lens_at_call, folded, drafts=None):
     """Algorithmic HBM bytes of one layer's verify_flush call: the verify of the
     byte model above with B_r = 0 for the folded slots, whose committed tokens
     are read once by the fold and whose state is written once (HV*dk*dv*4 each)
-    but not read a second time."""
-    v_bytes, _ = byte_model(wl, lens_at_call, [])   # ring read of every slot's committed tokens
-    return v_bytes + len(folded) * wl.hv * wl.dk * wl.dv * 4
+    but not read a second time (a folded slot without a draft reads its state
+    for the fold only)."""
+    Ds = np.full(wl.num_reqs, wl.draft) if drafts is None else np.asarray(drafts)
+    lens = np.asarray(lens_at_call)
+    due = lens >= max(wl.flush_min_len, 1)
+    v_bytes, _ = byte_model(wl, np.where(due & (Ds == 0), 0, lens), [], Ds)
+    fold_only = int((due & (Ds == 0)).sum())
+    tok_ring = wl.hk * wl.dk * wl.in_bytes + wl.hv * wl.dv * wl.in_bytes + wl.hv * 8
+    fold_only_ring = int(lens[due & (Ds == 0)].sum()) * tok_ring
+    return (v_bytes + len(folded) * wl.hv * wl.dk * wl.dv * 4
+            + fold_only * wl.hv * wl.dk * wl.dv * 4 + fold_only_ring)
 
 
 def cpu_baseline(wl, seconds_budget=15.0):
@@ -258,7 +270,11 @@ def main():
 
     total = args.warmup + args.steps
     rng = np.random.default_rng(synth.seed_for(wl.name, 0, 0))
-    steps = [(synth.make_slot_idx(wl, rng), synth.sample_accepted(wl, rng)) for _ in range(total)]
+    steps = []
+    for _ in range(total):
+        slots = synth.make_slot_idx(wl, rng)
+        lens = synth.sample_draft_lens(wl, rng)   # None: every request drafts wl.draft
+        steps.append((slots, synth.sample_accepted(wl, rng, draft_lens=lens), lens))
     F = max(wl.flush_min_len, 1)
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
@@ -268,7 +284,7 @@ def main():
         # the host's copy of the schedule (identical on every layer)
         sched = []
         lens = init_len.copy()
-        for slots, acc in steps:
+        for slots, acc, dl in steps:
             lv = lens[slots].copy()
             if path == "fused":
                 due = lv >= F
@@ -279,7 +295,8 @@ def main():
                 due = lens[slots] >= F
                 folded = lens[slots][due].copy()
                 lens[slots[due]] = 0
-            sched.append(dict(slots=to_device(slots), acc=to_device(acc), lv=lv, folded=folded))
+            sched.append(dict(slots=to_device(slots), acc=to_device(acc), lv=lv, folded=folded,
+                              dl=None if dl is None else to_device(dl), drafts=dl))
         torch.cuda.synchronize()
 
         def run_step(step, marks):
@@ -290,13 +307,13 @@ def main():
                 d = drafts[L][step % 2]
                 if path == "fused":
                     caches[L].verify_flush(sc["slots"], wl.flush_min_len, d["q"], d["k"], d["v"],
-                                           d["alpha"], d["beta"], out=out)
+                                           d["alpha"], d["beta"], out=out, draft_lens=sc["dl"])
                 else:
                     caches[L].verify(sc["slots"], d["q"], d["k"], d["v"], d["alpha"], d["beta"],
-                                     out=out)
+                                     out=out, draft_lens=sc["dl"])
             e[1].record(stream)
             for L in range(layers):
-                caches[L].rollback(sc["slots"], wl.draft, sc["acc"])
+                caches[L].rollback(sc["slots"], wl.draft, sc["acc"], draft_lens=sc["dl"])
             e[2].record(stream)
             if path == "separate":
                 for L in range(layers):
@@ -321,10 +338,11 @@ def main():
             tv += e[0].elapsed_time(e[1])
             tr += e[1].elapsed_time(e[2])
             tf += e[2].elapsed_time(e[3])
+            sc = sched[step]
             if path == "fused":
-                b_v, b_f = byte_model_fused(wl, sched[step]["lv"], sched[step]["folded"]), 0
+                b_v, b_f = byte_model_fused(wl, sc["lv"], sc["folded"], sc["drafts"]), 0
             else:
-                b_v, b_f = byte_model(wl, sched[step]["lv"], sched[step]["folded"])
+                b_v, b_f = byte_model(wl, sc["lv"], sc["folded"], sc["drafts"])
             vb += b_v * layers          # every layer sees the same lengths
             fb += b_f * layers
         graph_ms = graph_leg(caches, sched) if path == "fused" else None
@@ -352,20 +370,23 @@ def main():
         (HIP events around each replay)."""
         slots_buf = sched[0]["slots"].clone()
         acc_buf = sched[0]["acc"].clone()
+        dl_buf = None if sched[0]["dl"] is None else sched[0]["dl"].clone()
         d = drafts
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for L in range(layers):
                 dd = d[L][0]
                 caches[L].verify_flush(slots_buf, wl.flush_min_len, dd["q"], dd["k"], dd["v"],
-                                       dd["alpha"], dd["beta"], out=out)
+                                       dd["alpha"], dd["beta"], out=out, draft_lens=dl_buf)
             for L in range(layers):
-                caches[L].rollback(slots_buf, wl.draft, acc_buf)
+                caches[L].rollback(slots_buf, wl.draft, acc_buf, draft_lens=dl_buf)
         torch.cuda.synchronize()
         times = []
         for step in range(args.warmup, total):
             slots_buf.copy_(sched[step]["slots"])
             acc_buf.copy_(sched[step]["acc"])
+            if dl_buf is not None:
+                dl_buf.copy_(sched[step]["dl"])
             e0, e1 = ev(), ev()
             e0.record(stream)
             g.replay()
@@ -421,6 +442,7 @@ def main():
         "config": {"workload": wl.name, "requests": wl.num_reqs, "v_heads": wl.hv,
                    "k_heads": wl.hk, "d_k": wl.dk, "d_v": wl.dv, "draft": wl.draft,
                    "ring_cap": wl.cap, "flush_min_len": wl.flush_min_len, "layers": layers,
+                   "draft_lens": wl.draft_lens,
                    "inputs": wl.in_dtype, "state": "f32",
                    "order": "fused" if "fused" in res else "separate"},
         "hbm_gbps": round(head["gbps"], 1),

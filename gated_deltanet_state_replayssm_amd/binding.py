@@ -15,9 +15,12 @@ LIB_PATH = os.path.join(PKG, "libgdnreplay.so")
 GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EHIP = 0, -1, -2, -3
 GDN_BF16, GDN_F32 = 0, 1
 GDN_DERR_CAPACITY, GDN_DERR_ACCEPT, GDN_DERR_SLOT, GDN_DERR_POINTER = 1, 2, 4, 8
+GDN_DERR_DRAFT = 16
 
 EXPORTED = ("gdn_replay_verify", "gdn_replay_rollback", "gdn_replay_flush",
-            "gdn_replay_verify_flush", "gdn_replay_strerror", "gdn_replay_version")
+            "gdn_replay_verify_flush", "gdn_replay_verify_varlen",
+            "gdn_replay_verify_flush_varlen", "gdn_replay_rollback_varlen",
+            "gdn_replay_strerror", "gdn_replay_version")
 
 
 class GdnReplayCache(ctypes.Structure):
@@ -71,6 +74,13 @@ def load(path: str = LIB_PATH):
     lib.gdn_replay_flush.restype = ctypes.c_int
     lib.gdn_replay_verify_flush.argtypes = [P, I32, VP, I32, I32, VP, VP, VP, VP, VP, VP, VP]
     lib.gdn_replay_verify_flush.restype = ctypes.c_int
+    lib.gdn_replay_verify_varlen.argtypes = [P, I32, VP, VP, I32, VP, VP, VP, VP, VP, VP, VP]
+    lib.gdn_replay_verify_varlen.restype = ctypes.c_int
+    lib.gdn_replay_verify_flush_varlen.argtypes = [P, I32, VP, VP, I32, I32, VP, VP, VP, VP, VP,
+                                                   VP, VP]
+    lib.gdn_replay_verify_flush_varlen.restype = ctypes.c_int
+    lib.gdn_replay_rollback_varlen.argtypes = [P, I32, VP, VP, I32, VP, VP]
+    lib.gdn_replay_rollback_varlen.restype = ctypes.c_int
     lib.gdn_replay_strerror.argtypes = [ctypes.c_int]
     lib.gdn_replay_strerror.restype = ctypes.c_char_p
     lib.gdn_replay_version.argtypes = []
@@ -113,6 +123,25 @@ def verify_flush_raw(cache: GdnReplayCache, num_reqs, slot_idx, draft_len, min_l
                                           min_len, q, k, v, alpha, beta, out, stream)
 
 
+def verify_varlen_raw(cache: GdnReplayCache, num_reqs, slot_idx, draft_lens, max_draft, q, k, v,
+                      alpha, beta, out, stream) -> int:
+    return load().gdn_replay_verify_varlen(ctypes.byref(cache), num_reqs, slot_idx, draft_lens,
+                                           max_draft, q, k, v, alpha, beta, out, stream)
+
+
+def verify_flush_varlen_raw(cache: GdnReplayCache, num_reqs, slot_idx, draft_lens, max_draft,
+                            min_len, q, k, v, alpha, beta, out, stream) -> int:
+    return load().gdn_replay_verify_flush_varlen(ctypes.byref(cache), num_reqs, slot_idx,
+                                                 draft_lens, max_draft, min_len, q, k, v, alpha,
+                                                 beta, out, stream)
+
+
+def rollback_varlen_raw(cache: GdnReplayCache, num_reqs, slot_idx, draft_lens, max_draft,
+                        num_accepted, stream) -> int:
+    return load().gdn_replay_rollback_varlen(ctypes.byref(cache), num_reqs, slot_idx, draft_lens,
+                                             max_draft, num_accepted, stream)
+
+
 def verify(cache, num_reqs, slot_idx, draft_len, q, k, v, alpha, beta, out, stream) -> None:
     _check("gdn_replay_verify",
            verify_raw(cache, num_reqs, slot_idx, draft_len, q, k, v, alpha, beta, out, stream))
@@ -132,6 +161,27 @@ def verify_flush(cache, num_reqs, slot_idx, draft_len, min_len, q, k, v, alpha, 
     _check("gdn_replay_verify_flush",
            verify_flush_raw(cache, num_reqs, slot_idx, draft_len, min_len, q, k, v, alpha, beta,
                             out, stream))
+
+
+def verify_varlen(cache, num_reqs, slot_idx, draft_lens, max_draft, q, k, v, alpha, beta, out,
+                  stream) -> None:
+    _check("gdn_replay_verify_varlen",
+           verify_varlen_raw(cache, num_reqs, slot_idx, draft_lens, max_draft, q, k, v, alpha,
+                             beta, out, stream))
+
+
+def verify_flush_varlen(cache, num_reqs, slot_idx, draft_lens, max_draft, min_len, q, k, v, alpha,
+                        beta, out, stream) -> None:
+    _check("gdn_replay_verify_flush_varlen",
+           verify_flush_varlen_raw(cache, num_reqs, slot_idx, draft_lens, max_draft, min_len, q, k,
+                                   v, alpha, beta, out, stream))
+
+
+def rollback_varlen(cache, num_reqs, slot_idx, draft_lens, max_draft, num_accepted,
+                    stream) -> None:
+    _check("gdn_replay_rollback_varlen",
+           rollback_varlen_raw(cache, num_reqs, slot_idx, draft_lens, max_draft, num_accepted,
+                               stream))
 
 
 def version() -> int:

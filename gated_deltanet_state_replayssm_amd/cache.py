@@ -128,28 +128,51 @@ class ReplayCache:
         _need(out, "out", torch.float32, (R, D, self.hv, self.dv), dev)
         return R, D, out
 
-    def verify(self, slot_idx, q, k, v, alpha, beta, out=None, stream=None) -> torch.Tensor:
+    def _lens(self, draft_lens, R):
+        if draft_lens is not None:
+            _need(draft_lens, "draft_lens", torch.int32, (R,), self.device)
+        return draft_lens
+
+    def verify(self, slot_idx, q, k, v, alpha, beta, out=None, stream=None,
+               draft_lens=None) -> torch.Tensor:
+        """Outputs of the draft block. draft_lens ([R] int32, device): per-request
+        draft lengths in [0, D] (the *_varlen entry point); rows past a request's
+        length are left untouched."""
         R, D, out = self._draft_args(slot_idx, q, k, v, alpha, beta, out)
-        binding.verify(self.struct(), R, slot_idx.data_ptr(), D, q.data_ptr(), k.data_ptr(),
-                       v.data_ptr(), alpha.data_ptr(), beta.data_ptr(), out.data_ptr(),
-                       _stream_handle(stream))
+        args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), alpha.data_ptr(), beta.data_ptr(),
+                out.data_ptr(), _stream_handle(stream))
+        if self._lens(draft_lens, R) is None:
+            binding.verify(self.struct(), R, slot_idx.data_ptr(), D, *args)
+        else:
+            binding.verify_varlen(self.struct(), R, slot_idx.data_ptr(), draft_lens.data_ptr(), D,
+                                  *args)
         return out
 
     def verify_flush(self, slot_idx, min_len: int, q, k, v, alpha, beta, out=None,
-                     stream=None) -> torch.Tensor:
+                     stream=None, draft_lens=None) -> torch.Tensor:
         """flush(min_len) then verify, in one pass (gdn_replay_verify_flush)."""
         R, D, out = self._draft_args(slot_idx, q, k, v, alpha, beta, out)
-        binding.verify_flush(self.struct(), R, slot_idx.data_ptr(), D, int(min_len),
-                             q.data_ptr(), k.data_ptr(), v.data_ptr(), alpha.data_ptr(),
-                             beta.data_ptr(), out.data_ptr(), _stream_handle(stream))
+        args = (int(min_len), q.data_ptr(), k.data_ptr(), v.data_ptr(), alpha.data_ptr(),
+                beta.data_ptr(), out.data_ptr(), _stream_handle(stream))
+        if self._lens(draft_lens, R) is None:
+            binding.verify_flush(self.struct(), R, slot_idx.data_ptr(), D, *args)
+        else:
+            binding.verify_flush_varlen(self.struct(), R, slot_idx.data_ptr(),
+                                        draft_lens.data_ptr(), D, *args)
         return out
 
-    def rollback(self, slot_idx, draft_len: int, num_accepted, stream=None) -> None:
+    def rollback(self, slot_idx, draft_len: int, num_accepted, stream=None,
+                 draft_lens=None) -> None:
         R = slot_idx.shape[0]
         _need(slot_idx, "slot_idx", torch.int32, (R,), self.device)
         _need(num_accepted, "num_accepted", torch.int32, (R,), self.device)
-        binding.rollback(self.struct(), R, slot_idx.data_ptr(), int(draft_len),
-                         num_accepted.data_ptr(), _stream_handle(stream))
+        if self._lens(draft_lens, R) is None:
+            binding.rollback(self.struct(), R, slot_idx.data_ptr(), int(draft_len),
+                             num_accepted.data_ptr(), _stream_handle(stream))
+        else:
+            binding.rollback_varlen(self.struct(), R, slot_idx.data_ptr(), draft_lens.data_ptr(),
+                                    int(draft_len), num_accepted.data_ptr(),
+                                    _stream_handle(stream))
 
     def flush(self, slot_idx, min_len: int, stream=None) -> None:
         R = slot_idx.shape[0]

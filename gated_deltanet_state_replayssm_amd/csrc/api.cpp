@@ -56,16 +56,19 @@ CacheView view_of(const gdn_replay_cache *c) {
   return v;
 }
 
-// Validation and argument packing shared by verify and verify_flush.
+// Validation and argument packing shared by verify and verify_flush (varlen:
+// draft_lens non-null, draft_len is the maximum).
 int verify_args(const gdn_replay_cache *c, int32_t num_reqs, const int32_t *slot_idx,
                 int32_t draft_len, const void *q, const void *k, const void *v, const float *alpha,
-                const float *beta, float *out, gdnr::VerifyArgs *a) {
+                const float *beta, float *out, gdnr::VerifyArgs *a, bool varlen = false,
+                const int32_t *draft_lens = nullptr) {
   int st = check_cache(c);
   if (st != GDN_OK) return st;
   if (num_reqs < 0 || num_reqs > c->num_slots) return GDN_EINVAL;
   if (draft_len < 1 || draft_len > c->ring_cap) return GDN_EINVAL;
   if (num_reqs == 0) return GDN_OK;
   if (!slot_idx || !q || !k || !v || !alpha || !beta || !out) return GDN_EINVAL;
+  if (varlen && (!draft_lens || !aligned(draft_lens, 4))) return GDN_EINVAL;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(alpha, 4) ||
       !aligned(beta, 4) || !aligned(out, 16) || !aligned(slot_idx, 4))
     return GDN_EINVAL;
@@ -73,6 +76,7 @@ int verify_args(const gdn_replay_cache *c, int32_t num_reqs, const int32_t *slot
   a->num_reqs = num_reqs;
   a->draft = draft_len;
   a->slot_idx = slot_idx;
+  a->draft_lens = varlen ? draft_lens : nullptr;
   a->q = q;
   a->k = k;
   a->v = v;
@@ -97,6 +101,8 @@ gdnr::FlushArgs flush_args(const gdn_replay_cache *c, int32_t num_reqs, const in
   a.num_reqs = num_reqs;
   a.min_len = min_len;
   a.slot_idx = slot_idx;
+  a.draft_lens = nullptr;
+  a.max_draft = 0;
   return a;
 }
 
@@ -121,23 +127,45 @@ int gdn_replay_verify(const gdn_replay_cache *c, int32_t num_reqs, const int32_t
   return launch_verify(c, a, stream);
 }
 
-int gdn_replay_verify_flush(const gdn_replay_cache *c, int32_t num_reqs, const int32_t *slot_idx,
-                            int32_t draft_len, int32_t min_len, const void *q, const void *k,
-                            const void *v, const float *alpha, const float *beta, float *out,
-                            hipStream_t stream) {
+int gdn_replay_verify_varlen(const gdn_replay_cache *c, int32_t num_reqs, const int32_t *slot_idx,
+                             const int32_t *draft_lens, int32_t max_draft, const void *q,
+                             const void *k, const void *v, const float *alpha, const float *beta,
+                             float *out, hipStream_t stream) {
   gdnr::VerifyArgs a;
-  const int st = verify_args(c, num_reqs, slot_idx, draft_len, q, k, v, alpha, beta, out, &a);
+  const int st = verify_args(c, num_reqs, slot_idx, max_draft, q, k, v, alpha, beta, out, &a,
+                             true, draft_lens);
+  if (st != GDN_OK || num_reqs == 0) return st;
+  return launch_verify(c, a, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int verify_flush_impl(const gdn_replay_cache *c, int32_t num_reqs, const int32_t *slot_idx,
+                      int32_t draft_len, int32_t min_len, const void *q, const void *k,
+                      const void *v, const float *alpha, const float *beta, float *out,
+                      hipStream_t stream, bool varlen, const int32_t *draft_lens) {
+  gdnr::VerifyArgs a;
+  const int st = verify_args(c, num_reqs, slot_idx, draft_len, q, k, v, alpha, beta, out, &a,
+                             varlen, draft_lens);
   if (st != GDN_OK || num_reqs == 0) return st;
   const bool f32 = c->in_dtype == GDN_F32;
   if (gdnr::fused_supported(c->d_k, c->d_v, f32, draft_len, c->ring_cap))
     return gdnr::launch_verify_flush_fused(a, min_len, stream) == hipSuccess ? GDN_OK : GDN_EHIP;
-  // Other shapes: the same result from the two calls back to back.
-  const int fs = launch_flush(c, flush_args(c, num_reqs, slot_idx, min_len), stream);
+  // Other shapes: the same result from the two calls back to back. With
+  // per-request lengths a request whose length is out of range must not be
+  // flushed, so the flush checks the lengths too.
+  gdnr::FlushArgs fa = flush_args(c, num_reqs, slot_idx, min_len);
+  fa.draft_lens = a.draft_lens;
+  fa.max_draft = draft_len;
+  const int fs = launch_flush(c, fa, stream);
   return fs != GDN_OK ? fs : launch_verify(c, a, stream);
 }
 
-int gdn_replay_rollback(const gdn_replay_cache *c, int32_t num_reqs, const int32_t *slot_idx,
-                        int32_t draft_len, const int32_t *num_accepted, hipStream_t stream) {
+int rollback_impl(const gdn_replay_cache *c, int32_t num_reqs, const int32_t *slot_idx,
+                  int32_t draft_len, const int32_t *num_accepted, hipStream_t stream, bool varlen,
+                  const int32_t *draft_lens) {
   int st = check_cache(c);
   if (st != GDN_OK) return st;
   if (num_reqs < 0 || num_reqs > c->num_slots) return GDN_EINVAL;
@@ -145,13 +173,47 @@ int gdn_replay_rollback(const gdn_replay_cache *c, int32_t num_reqs, const int32
   if (num_reqs == 0) return GDN_OK;
   if (!slot_idx || !num_accepted) return GDN_EINVAL;
   if (!aligned(slot_idx, 4) || !aligned(num_accepted, 4)) return GDN_EINVAL;
+  if (varlen && (!draft_lens || !aligned(draft_lens, 4))) return GDN_EINVAL;
   gdnr::RollbackArgs a;
   a.c = view_of(c);
   a.num_reqs = num_reqs;
   a.draft = draft_len;
   a.slot_idx = slot_idx;
+  a.draft_lens = varlen ? draft_lens : nullptr;
   a.num_accepted = num_accepted;
   return gdnr::launch_rollback(a, stream) == hipSuccess ? GDN_OK : GDN_EHIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_replay_verify_flush(const gdn_replay_cache *c, int32_t num_reqs, const int32_t *slot_idx,
+                            int32_t draft_len, int32_t min_len, const void *q, const void *k,
+                            const void *v, const float *alpha, const float *beta, float *out,
+                            hipStream_t stream) {
+  return verify_flush_impl(c, num_reqs, slot_idx, draft_len, min_len, q, k, v, alpha, beta, out,
+                           stream, false, nullptr);
+}
+
+int gdn_replay_verify_flush_varlen(const gdn_replay_cache *c, int32_t num_reqs,
+                                   const int32_t *slot_idx, const int32_t *draft_lens,
+                                   int32_t max_draft, int32_t min_len, const void *q,
+                                   const void *k, const void *v, const float *alpha,
+                                   const float *beta, float *out, hipStream_t stream) {
+  return verify_flush_impl(c, num_reqs, slot_idx, max_draft, min_len, q, k, v, alpha, beta, out,
+                           stream, true, draft_lens);
+}
+
+int gdn_replay_rollback(const gdn_replay_cache *c, int32_t num_reqs, const int32_t *slot_idx,
+                        int32_t draft_len, const int32_t *num_accepted, hipStream_t stream) {
+  return rollback_impl(c, num_reqs, slot_idx, draft_len, num_accepted, stream, false, nullptr);
+}
+
+int gdn_replay_rollback_varlen(const gdn_replay_cache *c, int32_t num_reqs,
+                               const int32_t *slot_idx, const int32_t *draft_lens,
+                               int32_t max_draft, const int32_t *num_accepted, hipStream_t stream) {
+  return rollback_impl(c, num_reqs, slot_idx, max_draft, num_accepted, stream, true, draft_lens);
 }
 
 int gdn_replay_flush(const gdn_replay_cache *c, int32_t num_reqs, const int32_t *slot_idx,

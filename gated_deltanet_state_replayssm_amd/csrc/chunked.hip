@@ -245,8 +245,10 @@ __device__ __forceinline__ Srcs make_srcs(const CacheView &c, const Unit &u, con
   b.dv_row = HV * DV * 2;
   b.dab_row = HV * 4;
   if (verify) {
-    const int D = va->draft;
-    const int64_t d0 = (int64_t)u.r * D;
+    // this request's draft length; rows are va->draft apart. A fused verify of a
+    // due slot without a draft stages zero rows: resources of one row then.
+    const int D = max(u.T - u.B, 1);
+    const int64_t d0 = (int64_t)u.r * va->draft;
     const uint32_t kq_bytes = (D - 1) * b.dk_row + DK * 2;
     b.dk = make_rsrc(static_cast<const uint16_t *>(va->k) + (d0 * HK + u.kh) * DK, kq_bytes);
     b.dq = make_rsrc(static_cast<const uint16_t *>(va->q) + (d0 * HK + u.kh) * DK, kq_bytes);
@@ -767,11 +769,11 @@ __device__ __forceinline__ void solve_w(const Smem<DK, DV> &sm, const f32x4 (&Y)
   }
 }
 
-// out[r][0..D-1][h][0..DV-1] of one (request, value head), rows HV DV floats apart
-__device__ __forceinline__ Rsrc out_rsrc(const VerifyArgs &va, int r, int h, int DV) {
+// out[r][0..D-1][h][0..DV-1] of one (request, value head), rows HV DV floats apart;
+// D >= 1 is the request's draft length (request r's rows start at r * va.draft)
+__device__ __forceinline__ Rsrc out_rsrc(const VerifyArgs &va, int r, int h, int DV, int D) {
   const int HV = va.c.hv;
-  return make_rsrc(va.out + ((int64_t)r * va.draft * HV + h) * DV,
-                   ((va.draft - 1) * HV * DV + DV) * 4);
+  return make_rsrc(va.out + ((int64_t)r * va.draft * HV + h) * DV, ((D - 1) * HV * DV + DV) * 4);
 }
 
 // Draft outputs O = gamma Z + C W of chunk rows t (token t0 + t >= B, t < Treal).
@@ -870,7 +872,7 @@ __device__ __forceinline__ void fold_state(const Smem<DK, DV> &sm, const f32x4 (
 // then every wave contracts its state columns and forms W and either the
 // outputs or the fold. The chunk loop is not unrolled: its body is the
 // register-bound part, and one copy of it keeps the kernel at 4 workgroups per CU.
-template <int DK, int DV, int NT, bool VERIFY>
+template <int DK, int DV, int NT, bool VERIFY, bool VARLEN>
 __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_chunked(VerifyArgs va,
                                                                            FlushArgs fa) {
   constexpr int WAVES = DV / (16 * NT);
@@ -883,8 +885,8 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_chunked(Verif
   const CacheView &c = VERIFY ? va.c : fa.c;
   const int HV = c.hv;
   const int r = blockIdx.x / HV, h = blockIdx.x % HV;
-  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
-  const int g = lane >> 4, l16 = lane & 15;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int g = (tid >> 4) & 3, l16 = tid & 15;  // bit fields of the thread index: cheap to recompute
   const bool lead = (h == 0 && tid == 0);
   // this lane's first state column and its byte offset in the state tile,
   // recomputed where used from an opaque copy of the thread index
@@ -912,13 +914,25 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_chunked(Verif
   }
   int T;
   if constexpr (VERIFY) {
-    if (n + va.draft > C) {
+    // this request's draft length (per-request lengths: a separate instantiation)
+    const int D = VARLEN ? request_draft(va.draft_lens, r, va.draft) : va.draft;
+    if (VARLEN && D < 0) {
+      if (lead) raise_err(c.err, GDN_DERR_DRAFT);
+      return;
+    }
+    if (VARLEN && D == 0) return;  // no draft: nothing to emit or append
+    if (n + D > C) {
       if (lead) raise_err(c.err, GDN_DERR_CAPACITY);
       return;
     }
-    T = n + va.draft;
+    T = n + D;
+    // opaque past the checks: value facts drawn from them made the register
+    // allocation of the chunk loop spill
+    asm volatile("" : "+s"(T));
   } else {
     if (n < max(fa.min_len, 1)) return;  // not due: nothing is written
+    // verify_flush run as two calls: a request with a bad draft length is not flushed
+    if (fa.draft_lens && request_draft(fa.draft_lens, r, fa.max_draft) < 0) return;
     T = n;
   }
   const Unit u{r, h, s, h / (HV / c.hk), head, n, T, C};
@@ -990,7 +1004,7 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_chunked(Verif
     f32x4 Y[2][NT], Z[2][NT], Wm[2][NT];
     contract<DK, DV, NT, kY | kZ>(sm, H, g, l16, Y, Z);
     solve_w<DK, DV, NT>(sm, Y, col_of(), g, l16, Wm);
-    emit_outputs<DK, DV, NT>(sm, Z, Wm, g, l16, t0, Treal, u.B, out_rsrc(va, r, h, DV),
+    emit_outputs<DK, DV, NT>(sm, Z, Wm, g, l16, t0, Treal, u.B, out_rsrc(va, r, h, DV, T - u.B),
                              col_of() * 4, HV * DV * 4);
     // the draft rows, from LDS; the thread mapping is that of the stage type
     if (nchunks == 1) {
@@ -1024,7 +1038,7 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_chunked(Verif
 // chunk's inputs, load theirs, then build the T x T matrices (wave 0: A and its
 // inverse; wave 1: C) while the state streams in. Verify takes Y = K H and
 // Z = Q H in one pass, so its state registers die right after it.
-template <int DK, int DV, int NT, bool VERIFY>
+template <int DK, int DV, int NT, bool VERIFY, bool VARLEN>
 __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_single(VerifyArgs va,
                                                                           FlushArgs fa) {
   constexpr int WAVES = DV / (16 * NT);
@@ -1036,8 +1050,8 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_single(Verify
   const CacheView &c = VERIFY ? va.c : fa.c;
   const int HV = c.hv;
   const int r = blockIdx.x / HV, h = blockIdx.x % HV;
-  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
-  const int g = lane >> 4, l16 = lane & 15;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int g = (tid >> 4) & 3, l16 = tid & 15;  // bit fields of the thread index: cheap to recompute
   const int colL = wave * 16 * NT + NT * l16;
   const bool lead = (h == 0 && tid == 0);
 
@@ -1054,13 +1068,25 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_single(Verify
   }
   int T;
   if constexpr (VERIFY) {
-    if (n + va.draft > C) {
+    // this request's draft length (per-request lengths: a separate instantiation)
+    const int D = VARLEN ? request_draft(va.draft_lens, r, va.draft) : va.draft;
+    if (VARLEN && D < 0) {
+      if (lead) raise_err(c.err, GDN_DERR_DRAFT);
+      return;
+    }
+    if (VARLEN && D == 0) return;  // no draft: nothing to emit or append
+    if (n + D > C) {
       if (lead) raise_err(c.err, GDN_DERR_CAPACITY);
       return;
     }
-    T = n + va.draft;
+    T = n + D;
+    // opaque past the checks: value facts drawn from them made the register
+    // allocation of the chunk loop spill
+    asm volatile("" : "+s"(T));
   } else {
     if (n < max(fa.min_len, 1)) return;  // not due: nothing is written
+    // verify_flush run as two calls: a request with a bad draft length is not flushed
+    if (fa.draft_lens && request_draft(fa.draft_lens, r, fa.max_draft) < 0) return;
     T = n;
   }
   const Unit u{r, h, s, h / (HV / c.hk), head, n, T, C};
@@ -1098,8 +1124,8 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_single(Verify
   contract<DK, DV, NT, VERIFY ? (kY | kZ) : kY>(sm, H, g, l16, Y, Z);
   solve_w<DK, DV, NT>(sm, Y, colL, g, l16, Wm);
   if constexpr (VERIFY) {
-    emit_outputs<DK, DV, NT>(sm, Z, Wm, g, l16, 0, T, u.B, out_rsrc(va, r, h, DV), colL * 4,
-                         HV * DV * 4);
+    emit_outputs<DK, DV, NT>(sm, Z, Wm, g, l16, 0, T, u.B, out_rsrc(va, r, h, DV, T - u.B),
+                             colL * 4, HV * DV * 4);
     if (wave < SW) sg.append(sm, sr, u, 0, T, h % (HV / c.hk) == 0);
   } else {
     fold_state<DK, DV, NT>(sm, Wm, g, l16, H);
@@ -1215,7 +1241,7 @@ __device__ Req ordered_request(const VerifyArgs &va, int mn, int q, int lane) {
 // for their fold. So each workgroup of a due slot counts itself in at
 // sync[num_slots + s HK + kh] once its fold inputs are staged, and the last
 // one of the key head's group appends k and q (the others have read by then).
-template <int DK, int DV, int NT>
+template <int DK, int DV, int NT, bool VARLEN>
 __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyArgs va,
                                                                          int min_len) {
   constexpr int WAVES = DV / (16 * NT);
@@ -1268,6 +1294,7 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyA
       if (si < 0 || si >= c.num_slots) continue;
       const int hs = c.head[si], ns = c.len[si];
       if (hs < 0 || hs >= c.cap || ns < mn || ns > c.cap) continue;
+      if (VARLEN && request_draft(va.draft_lens, i, va.draft) < 0) continue;  // skipped request
       c.head[si] = hs + ns - (hs + ns >= c.cap ? c.cap : 0);
       c.len[si] = 0;
     }
@@ -1287,9 +1314,17 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyA
     finish();
     return;
   }
+  // this request's draft length (the per-request lengths are a separate
+  // instantiation, so that the fixed-length kernel carries none of their code)
+  const int D = VARLEN ? request_draft(va.draft_lens, r, va.draft) : va.draft;
+  if (VARLEN && D < 0) {
+    if (lead) raise_err(c.err, GDN_DERR_DRAFT);
+    finish();
+    return;
+  }
   const bool due = n >= mn;
-  if (!due && n + va.draft > C) {
-    if (lead) raise_err(c.err, GDN_DERR_CAPACITY);
+  if (!due && ((VARLEN && D == 0) || n + D > C)) {  // capacity error, or nothing to do
+    if (lead && D > 0) raise_err(c.err, GDN_DERR_CAPACITY);
     finish();
     return;
   }
@@ -1335,7 +1370,7 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyA
   // ---- verify the draft from checkpoint H plus B committed tokens at hd. A due
   // slot's state is live here, so all waves stage (fewer rows each); otherwise
   // waves 0..SW-1 stage while the others' state loads stream in.
-  const Unit u{r, h, s, kh, hd, B, B + va.draft, C};
+  const Unit u{r, h, s, kh, hd, B, B + D, C};
   const Srcs sr = make_srcs<DK, DV>(c, u, &va, true);
   Stage<DK, DV, NT, true> sga;
   Stage<DK, DV, NT, true, 64 * SW> sgs;
@@ -1369,7 +1404,7 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyA
   f32x4 Y[2][NT], Z[2][NT], Wm[2][NT];
   contract<DK, DV, NT, kY | kZ>(sm, H, g, l16, Y, Z);
   solve_w<DK, DV, NT>(sm, Y, col_of(), g, l16, Wm);
-  emit_outputs<DK, DV, NT>(sm, Z, Wm, g, l16, 0, u.T, u.B, out_rsrc(va, r, h, DV), col_of() * 4,
+  emit_outputs<DK, DV, NT>(sm, Z, Wm, g, l16, 0, u.T, u.B, out_rsrc(va, r, h, DV, max(D, 1)), col_of() * 4,
                            HV * DV * 4);
   const bool kq_writer = due ? group_rank == G - 1 : h % G == 0;
   if (due)
@@ -1380,15 +1415,17 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyA
   finish();
 }
 
-template <int DK, int DV, bool VERIFY>
+template <int DK, int DV, bool VERIFY, bool VARLEN>
 hipError_t launch_t(const VerifyArgs &va, const FlushArgs &fa, int num_reqs, int hv, int cap,
                     hipStream_t stream) {
   constexpr int NT = 2;
   const dim3 grid(num_reqs * hv), block(64 * (DV / (16 * NT)));
   if (cap <= kCh)
-    hipLaunchKernelGGL((replay_single<DK, DV, NT, VERIFY>), grid, block, 0, stream, va, fa);
+    hipLaunchKernelGGL((replay_single<DK, DV, NT, VERIFY, VARLEN>), grid, block, 0, stream, va,
+                       fa);
   else
-    hipLaunchKernelGGL((replay_chunked<DK, DV, NT, VERIFY>), grid, block, 0, stream, va, fa);
+    hipLaunchKernelGGL((replay_chunked<DK, DV, NT, VERIFY, VARLEN>), grid, block, 0, stream, va,
+                       fa);
   return hipGetLastError();
 }
 
@@ -1397,12 +1434,19 @@ hipError_t launch_t(const VerifyArgs &va, const FlushArgs &fa, int num_reqs, int
 hipError_t launch_verify_flush_fused(const VerifyArgs &a, int min_len, hipStream_t stream) {
   constexpr int NT = 2;
   const dim3 grid(a.num_reqs * a.c.hv);
+  const bool varlen = a.draft_lens != nullptr;
   if (a.c.dk == 128) {
-    hipLaunchKernelGGL((replay_fused<128, 128, NT>), grid, dim3(64 * (128 / (16 * NT))), 0, stream,
-                       a, min_len);
+    const dim3 block(64 * (128 / (16 * NT)));
+    if (varlen)
+      hipLaunchKernelGGL((replay_fused<128, 128, NT, true>), grid, block, 0, stream, a, min_len);
+    else
+      hipLaunchKernelGGL((replay_fused<128, 128, NT, false>), grid, block, 0, stream, a, min_len);
   } else if (a.c.dk == 64) {
-    hipLaunchKernelGGL((replay_fused<64, 64, NT>), grid, dim3(64 * (64 / (16 * NT))), 0, stream,
-                       a, min_len);
+    const dim3 block(64 * (64 / (16 * NT)));
+    if (varlen)
+      hipLaunchKernelGGL((replay_fused<64, 64, NT, true>), grid, block, 0, stream, a, min_len);
+    else
+      hipLaunchKernelGGL((replay_fused<64, 64, NT, false>), grid, block, 0, stream, a, min_len);
   } else {
     return hipErrorInvalidValue;
   }
@@ -1419,15 +1463,23 @@ bool chunked_supported(int dk, int dv, bool in_f32, int draft) {
 
 hipError_t launch_verify_chunked(const VerifyArgs &a, hipStream_t stream) {
   FlushArgs none{};
-  if (a.c.dk == 128) return launch_t<128, 128, true>(a, none, a.num_reqs, a.c.hv, a.c.cap, stream);
-  if (a.c.dk == 64) return launch_t<64, 64, true>(a, none, a.num_reqs, a.c.hv, a.c.cap, stream);
+  const int R = a.num_reqs, HV = a.c.hv, C = a.c.cap;
+  if (a.draft_lens) {
+    if (a.c.dk == 128) return launch_t<128, 128, true, true>(a, none, R, HV, C, stream);
+    if (a.c.dk == 64) return launch_t<64, 64, true, true>(a, none, R, HV, C, stream);
+  } else {
+    if (a.c.dk == 128) return launch_t<128, 128, true, false>(a, none, R, HV, C, stream);
+    if (a.c.dk == 64) return launch_t<64, 64, true, false>(a, none, R, HV, C, stream);
+  }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_flush_chunked(const FlushArgs &a, hipStream_t stream) {
   VerifyArgs none{};
-  if (a.c.dk == 128) return launch_t<128, 128, false>(none, a, a.num_reqs, a.c.hv, a.c.cap, stream);
-  if (a.c.dk == 64) return launch_t<64, 64, false>(none, a, a.num_reqs, a.c.hv, a.c.cap, stream);
+  if (a.c.dk == 128)
+    return launch_t<128, 128, false, false>(none, a, a.num_reqs, a.c.hv, a.c.cap, stream);
+  if (a.c.dk == 64)
+    return launch_t<64, 64, false, false>(none, a, a.num_reqs, a.c.hv, a.c.cap, stream);
   return hipErrorInvalidValue;
 }
 

@@ -30,4 +30,13 @@ __device__ __forceinline__ void raise_err(int32_t *err, int32_t bit) {
   if (err) atomicOr(err, bit);
 }
 
+// Draft length of request r: dmax for every request when lens is null, else the
+// request's own length; -1 when that is outside [0, dmax]. Draft rows keep the
+// stride dmax either way (request r's rows start at r * dmax).
+__device__ __forceinline__ int request_draft(const int32_t *lens, int r, int dmax) {
+  if (!lens) return dmax;
+  const int d = lens[r];
+  return (d < 0 || d > dmax) ? -1 : d;
+}
+
 }  // namespace gdnr

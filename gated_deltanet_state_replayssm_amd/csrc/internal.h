@@ -18,8 +18,9 @@ struct CacheView {
 
 struct VerifyArgs {
   CacheView c;
-  int32_t num_reqs, draft;
+  int32_t num_reqs, draft;       // draft: D, or D_max with per-request lengths
   const int32_t *slot_idx;
+  const int32_t *draft_lens;     // per-request lengths in [0, draft], or null
   const void *q, *k, *v;
   const float *alpha, *beta;
   float *out;
@@ -29,6 +30,7 @@ struct RollbackArgs {
   CacheView c;
   int32_t num_reqs, draft;
   const int32_t *slot_idx;
+  const int32_t *draft_lens;     // as in VerifyArgs
   const int32_t *num_accepted;
 };
 
@@ -36,6 +38,10 @@ struct FlushArgs {
   CacheView c;
   int32_t num_reqs, min_len;
   const int32_t *slot_idx;
+  // verify_flush run as two calls with per-request draft lengths: a request
+  // whose length is outside [0, max_draft] is not flushed (null: no check)
+  const int32_t *draft_lens;
+  int32_t max_draft;
 };
 
 // Launchers return hipSuccess or the launch error. in_f32 selects fp32 inputs.

@@ -60,12 +60,18 @@ __global__ __launch_bounds__(kLanes) void verify_recurrent(VerifyArgs a) {
     if (lead) raise_err(c.err, GDN_DERR_SLOT);
     return;
   }
-  const int C = c.cap, D = a.draft;
+  const int C = c.cap, Dmax = a.draft;
   const int head = c.head[s], n = c.len[s];
   if (head < 0 || head >= C || n < 0 || n > C) {
     if (lead) raise_err(c.err, GDN_DERR_POINTER);
     return;
   }
+  const int D = request_draft(a.draft_lens, r, Dmax);
+  if (D < 0) {
+    if (lead) raise_err(c.err, GDN_DERR_DRAFT);
+    return;
+  }
+  if (D == 0) return;  // no draft: nothing to emit or append
   if (n + D > C) {
     if (lead) raise_err(c.err, GDN_DERR_CAPACITY);
     return;
@@ -89,7 +95,7 @@ __global__ __launch_bounds__(kLanes) void verify_recurrent(VerifyArgs a) {
     step_col<DK>(H, ks, c.ring_alpha[ring_vh + pos], c.ring_beta[ring_vh + pos], vj);
   }
   for (int jd = 0; jd < D; ++jd) {
-    const int64_t tok = (int64_t)r * D + jd;
+    const int64_t tok = (int64_t)r * Dmax + jd;
     __syncthreads();
     stage_vec<DK, F32IN>(ks, a.k, (tok * HK + kh) * DK);
     stage_vec<DK, F32IN>(qs, a.q, (tok * HK + kh) * DK);
@@ -102,7 +108,7 @@ __global__ __launch_bounds__(kLanes) void verify_recurrent(VerifyArgs a) {
 
   // tentative append of the draft behind the committed window
   for (int jd = 0; jd < D; ++jd) {
-    const int64_t tok = (int64_t)r * D + jd;
+    const int64_t tok = (int64_t)r * Dmax + jd;
     const int pos = (head + n + jd) % C;
     if (col) copy_in<F32IN>(c.ring_v, (ring_vh + pos) * DV + j, a.v, (tok * HV + h) * DV + j);
     if (tile == 0 && lane == 0) {
@@ -139,6 +145,8 @@ __global__ __launch_bounds__(kLanes) void flush_recurrent(FlushArgs a) {
     return;
   }
   if (n < max(a.min_len, 1)) return;  // not due: nothing is written
+  // verify_flush run as two calls: a request with a bad draft length is not flushed
+  if (a.draft_lens && request_draft(a.draft_lens, r, a.max_draft) < 0) return;
   const int HV = c.hv, HK = c.hk, G = HV / HK, kh = h / G;
   __shared__ float ks[DK];
 

@@ -25,8 +25,13 @@ __global__ __launch_bounds__(256) void rollback_kernel(RollbackArgs a) {
     raise_err(c.err, GDN_DERR_POINTER);
     return;
   }
+  const int D = request_draft(a.draft_lens, i, a.draft);
+  if (D < 0) {
+    raise_err(c.err, GDN_DERR_DRAFT);
+    return;
+  }
   const int acc = a.num_accepted[i];
-  if (acc < 0 || acc > a.draft) {
+  if (acc < 0 || acc > D) {
     raise_err(c.err, GDN_DERR_ACCEPT);
     return;
   }

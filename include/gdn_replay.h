@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define GDN_REPLAY_VERSION 2
+#define GDN_REPLAY_VERSION 3
 
 typedef enum {
   GDN_OK = 0,
@@ -59,7 +59,8 @@ enum {
   GDN_DERR_CAPACITY = 1,  /* verify: len + D > C;  rollback: len + a > C  */
   GDN_DERR_ACCEPT = 2,    /* rollback: a outside [0, D]                  */
   GDN_DERR_SLOT = 4,      /* slot index outside [0, num_slots)           */
-  GDN_DERR_POINTER = 8    /* head outside [0, C) or len outside [0, C]   */
+  GDN_DERR_POINTER = 8,   /* head outside [0, C) or len outside [0, C]   */
+  GDN_DERR_DRAFT = 16     /* *_varlen: draft_lens[i] outside [0, max_draft] */
 };
 
 /*
@@ -189,6 +190,38 @@ int gdn_replay_verify_flush(const gdn_replay_cache *c, int32_t num_reqs, const i
                             int32_t draft_len, int32_t min_len, const void *q, const void *k,
                             const void *v, const float *alpha, const float *beta, float *out,
                             hipStream_t stream);
+
+/*
+ * Per-request draft lengths. Speculative decoding drafts a block of tokens per
+ * request and keeps the prefix up to the first rejected one ("Inference
+ * Engineering", chapter 5, section 5.2); here each request i drafts its own
+ * D_i = draft_lens[i] tokens, 0 <= D_i <= max_draft. D_i = 1 with every token
+ * accepted is plain (non-speculative) decode; D_i = 0 gives the request no
+ * draft this step (nothing appended or emitted; verify_flush still flushes it).
+ *
+ * The draft arrays keep the layout of the fixed-length calls with
+ * D = max_draft: request i's tokens are rows 0 .. D_i - 1 of its max_draft-row
+ * block of q, k, v, alpha, beta and out. Rows D_i .. max_draft - 1 are neither
+ * read nor written.
+ *
+ *   draft_lens [num_reqs] int32 (device).   max_draft: 1..C (host value).
+ * Device errors as for the fixed-length calls, plus DRAFT when D_i is outside
+ * [0, max_draft] (request skipped with no writes; verify_flush does not flush
+ * it either). Checks run in the order slot, pointers, draft length, then
+ * capacity or accept count. rollback_varlen needs a in [0, D_i].
+ */
+int gdn_replay_verify_varlen(const gdn_replay_cache *c, int32_t num_reqs, const int32_t *slot_idx,
+                             const int32_t *draft_lens, int32_t max_draft, const void *q,
+                             const void *k, const void *v, const float *alpha, const float *beta,
+                             float *out, hipStream_t stream);
+int gdn_replay_verify_flush_varlen(const gdn_replay_cache *c, int32_t num_reqs,
+                                   const int32_t *slot_idx, const int32_t *draft_lens,
+                                   int32_t max_draft, int32_t min_len, const void *q,
+                                   const void *k, const void *v, const float *alpha,
+                                   const float *beta, float *out, hipStream_t stream);
+int gdn_replay_rollback_varlen(const gdn_replay_cache *c, int32_t num_reqs,
+                               const int32_t *slot_idx, const int32_t *draft_lens,
+                               int32_t max_draft, const int32_t *num_accepted, hipStream_t stream);
 
 /* Human-readable text of a gdn_status (static storage). */
 const char *gdn_replay_strerror(int status);

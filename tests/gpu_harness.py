@@ -20,6 +20,7 @@ from gated_deltanet_state_replayssm_amd.cache import ReplayCache, to_device
 from oracle import gdn_oracle as go
 
 TOL = 2e-3
+CANARY = 12345.0  # pre-filled output value that a row no call writes keeps
 
 
 def say(*a):
@@ -73,21 +74,37 @@ class Pair:
             if host["ring_q"] is not None:
                 assert np.array_equal(host["ring_q"][s], o.ring_q[s]), f"ring_q slot {s}"
 
-    def verify(self, slot_idx, dr, label=""):
-        say(f"  verify {label} R={len(slot_idx)} D={dr['alpha'].shape[1]}")
+    def _out_buffer(self, dr):
+        R, D = dr["alpha"].shape[:2]
+        return torch.full((R, D, self.wl.hv, self.wl.dv), CANARY, dtype=torch.float32,
+                          device="cuda")
+
+    def _check_out(self, got, ref, what):
+        """Rows the oracle wrote (not NaN): within the bar over the call's
+        tensor; rows it did not write (skipped requests, rows past a request's
+        draft length): still holding the canary."""
+        written = ~np.isnan(ref)
+        if written.any():
+            e = rel_err(got[written], ref[written])
+            self.worst["out"] = max(self.worst["out"], e)
+            assert e <= TOL, f"{what} outputs: rel err {e:.3e} > {TOL}"
+        assert (got[~written] == CANARY).all(), f"{what} wrote rows it should not have"
+
+    def _lens_dev(self, lens):
+        return None if lens is None else to_device(np.asarray(lens, np.int32))
+
+    def verify(self, slot_idx, dr, label="", lens=None):
+        say(f"  verify {label} R={len(slot_idx)} D={dr['alpha'].shape[1]}"
+            + ("" if lens is None else f" lens={list(lens)[:8]}"))
         before = self.gpu.state.clone()
         dev = {k: to_device(v) for k, v in dr.items()}
         out = self.gpu.verify(to_device(slot_idx), dev["q"], dev["k"], dev["v"], dev["alpha"],
-                              dev["beta"])
+                              dev["beta"], out=self._out_buffer(dr), draft_lens=self._lens_dev(lens))
         torch.cuda.synchronize()
         sel = self._sel(slot_idx)
-        ref = self.orc.verify(slot_idx[sel], *(dr[x][sel] for x in ("q", "k", "v", "alpha", "beta")))
-        got = out.cpu().numpy()[sel]
-        ok = ~np.isnan(ref).any(axis=(1, 2, 3))
-        if ok.any():
-            e = rel_err(got[ok], ref[ok])
-            self.worst["out"] = max(self.worst["out"], e)
-            assert e <= TOL, f"verify outputs: rel err {e:.3e} > {TOL}"
+        ref = self.orc.verify(slot_idx[sel], *(dr[x][sel] for x in ("q", "k", "v", "alpha", "beta")),
+                              draft_lens=None if lens is None else np.asarray(lens)[sel])
+        self._check_out(out.cpu().numpy()[sel], ref, "verify")
         assert torch.equal(before, self.gpu.state), "verify modified the state"
         host = self.gpu.to_numpy()
         self._check_common(host)
@@ -108,35 +125,35 @@ class Pair:
         assert np.array_equal(host["state"][others].view(np.uint32),
                               before[others].view(np.uint32)), "unflushed slot state changed"
 
-    def verify_flush(self, slot_idx, min_len, dr, label=""):
-        say(f"  verify_flush {label} R={len(slot_idx)} D={dr['alpha'].shape[1]} min_len={min_len}")
+    def verify_flush(self, slot_idx, min_len, dr, label="", lens=None):
+        say(f"  verify_flush {label} R={len(slot_idx)} D={dr['alpha'].shape[1]} min_len={min_len}"
+            + ("" if lens is None else f" lens={list(lens)[:8]}"))
         before = self.gpu.state.cpu().numpy()
         len_before = self.orc.len.copy()
         dev = {k: to_device(v) for k, v in dr.items()}
         out = self.gpu.verify_flush(to_device(slot_idx), min_len, dev["q"], dev["k"], dev["v"],
-                                    dev["alpha"], dev["beta"])
+                                    dev["alpha"], dev["beta"], out=self._out_buffer(dr),
+                                    draft_lens=self._lens_dev(lens))
         torch.cuda.synchronize()
         sel = self._sel(slot_idx)
         ref = self.orc.verify_flush(slot_idx[sel], min_len,
-                                    *(dr[x][sel] for x in ("q", "k", "v", "alpha", "beta")))
-        got = out.cpu().numpy()[sel]
-        ok = ~np.isnan(ref).any(axis=(1, 2, 3))
-        if ok.any():
-            e = rel_err(got[ok], ref[ok])
-            self.worst["out"] = max(self.worst["out"], e)
-            assert e <= TOL, f"verify_flush outputs: rel err {e:.3e} > {TOL}"
+                                    *(dr[x][sel] for x in ("q", "k", "v", "alpha", "beta")),
+                                    draft_lens=None if lens is None else np.asarray(lens)[sel])
+        self._check_out(out.cpu().numpy()[sel], ref, "verify_flush")
         host = self.gpu.to_numpy()
         self._check_common(host)
         self._check_flushed(host, before, slot_idx, sel, min_len, len_before)
         return out
 
-    def rollback(self, slot_idx, draft_len, acc, label=""):
+    def rollback(self, slot_idx, draft_len, acc, label="", lens=None):
         say(f"  rollback {label}")
         before = self.gpu.state.clone()
-        self.gpu.rollback(to_device(slot_idx), draft_len, to_device(acc))
+        self.gpu.rollback(to_device(slot_idx), draft_len, to_device(acc),
+                          draft_lens=self._lens_dev(lens))
         torch.cuda.synchronize()
         sel = self._sel(slot_idx)
-        self.orc.rollback(slot_idx[sel], draft_len, acc[sel])
+        self.orc.rollback(slot_idx[sel], draft_len, acc[sel],
+                          draft_lens=None if lens is None else np.asarray(lens)[sel])
         assert torch.equal(before, self.gpu.state), "rollback modified the state"
         self._check_common(self.gpu.to_numpy())
 
@@ -164,15 +181,16 @@ def run_schedule(wl: synth.Workload, steps: int, seed: int, layers: int = 1, wit
         pairs.append(Pair(wl, init, with_q=with_q, oracle_slots=oracle_slots))
     for step in range(steps):
         slots = synth.make_slot_idx(wl, rng)
-        acc = synth.sample_accepted(wl, rng)
+        lens = synth.sample_draft_lens(wl, rng)   # None: every request drafts wl.draft
+        acc = synth.sample_accepted(wl, rng, draft_lens=lens)
         for L, p in enumerate(pairs):
             dr = synth.make_draft(wl, rng)
             if fused:
-                p.verify_flush(slots, wl.flush_min_len, dr, f"{label} L{L} step{step}")
+                p.verify_flush(slots, wl.flush_min_len, dr, f"{label} L{L} step{step}", lens=lens)
             else:
-                p.verify(slots, dr, f"{label} L{L} step{step}")
+                p.verify(slots, dr, f"{label} L{L} step{step}", lens=lens)
         for L, p in enumerate(pairs):
-            p.rollback(slots, wl.draft, acc, f"{label} L{L} step{step}")
+            p.rollback(slots, wl.draft, acc, f"{label} L{L} step{step}", lens=lens)
         if not fused:
             for L, p in enumerate(pairs):
                 p.flush(slots, wl.flush_min_len, f"{label} L{L} step{step}")

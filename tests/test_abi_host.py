@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert b.version() == 2
+    assert b.version() == 3
     for st in (b.GDN_OK, b.GDN_EINVAL, b.GDN_EUNSUPPORTED, b.GDN_EHIP):
         assert b.load().gdn_replay_strerror(st)
     assert b.load().gdn_replay_strerror(12345) == b"unknown status"
@@ -112,6 +112,45 @@ def test_call_validation():
                dict(k=None), dict(be=None), dict(out=FAKE + 4),
                dict(slot=None)):
         assert _verify_flush(c, **kw) == b.GDN_EINVAL, kw
+
+
+def _verify_varlen(c, num_reqs=2, dmax=4, lens=FAKE, **ptrs):
+    p = dict(slot=FAKE, q=FAKE, k=FAKE, v=FAKE, a=FAKE, be=FAKE, out=FAKE)
+    p.update(ptrs)
+    return b.verify_varlen_raw(c, num_reqs, p["slot"], lens, dmax, p["q"], p["k"], p["v"], p["a"],
+                               p["be"], p["out"], None)
+
+
+def _verify_flush_varlen(c, num_reqs=2, dmax=4, lens=FAKE, min_len=1, **ptrs):
+    p = dict(slot=FAKE, q=FAKE, k=FAKE, v=FAKE, a=FAKE, be=FAKE, out=FAKE)
+    p.update(ptrs)
+    return b.verify_flush_varlen_raw(c, num_reqs, p["slot"], lens, dmax, min_len, p["q"], p["k"],
+                                     p["v"], p["a"], p["be"], p["out"], None)
+
+
+def test_varlen_call_validation():
+    """Per-request draft lengths: the lengths pointer is required (and 4-byte
+    aligned), the maximum obeys the fixed-length call's bounds; the cache
+    checks apply unchanged; zero requests launch nothing."""
+    c = _cache()
+    for fn in (_verify_varlen, _verify_flush_varlen):
+        assert fn(c, lens=None) == b.GDN_EINVAL
+        assert fn(c, lens=FAKE + 2) == b.GDN_EINVAL
+        assert fn(c, dmax=0) == b.GDN_EINVAL
+        assert fn(c, dmax=9) == b.GDN_EINVAL              # max_draft > C
+        assert fn(c, num_reqs=5) == b.GDN_EINVAL
+        assert fn(c, out=None) == b.GDN_EINVAL
+        assert fn(_cache(d_k=48, d_v=48)) == b.GDN_EUNSUPPORTED
+        assert fn(c, num_reqs=0, lens=None, q=None) == b.GDN_OK
+    rb = b.rollback_varlen_raw
+    assert rb(c, 2, FAKE, None, 4, FAKE, None) == b.GDN_EINVAL
+    assert rb(c, 2, FAKE, FAKE, 0, FAKE, None) == b.GDN_EINVAL
+    assert rb(c, 2, FAKE, FAKE, 4, None, None) == b.GDN_EINVAL
+    assert rb(_cache(ring_cap=0), 2, FAKE, FAKE, 4, FAKE, None) == b.GDN_EINVAL
+    assert rb(c, 0, None, None, 4, None, None) == b.GDN_OK
+    lib = b.load()
+    assert lib.gdn_replay_verify_varlen(None, 1, FAKE, FAKE, 1, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                        FAKE, None) == b.GDN_EINVAL
 
 
 def test_zero_requests_is_a_noop_without_launch():

@@ -1,0 +1,142 @@
+"""GPU parity of the per-request draft length entry points (gdn_replay_verify_varlen,
+gdn_replay_verify_flush_varlen, gdn_replay_rollback_varlen) and of plain decode
+(D = 1), against the fp64 oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+from gated_deltanet_state_replayssm_amd import synth
+from gated_deltanet_state_replayssm_amd.cache import ReplayCache, to_device
+from tests.gpu_harness import Pair, run_schedule, say
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from gated_deltanet_state_replayssm_amd import binding
+    binding.load()
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_varlen_multi_step(fused):
+    """Lengths 0..16 per request and step, with flushes, d = 128, capacity 32."""
+    wl = synth.Workload("vl", 6, 8, 4, 2, 128, 128, 32, 16, synth.BF16, 16, 2,
+                        "clipnormal:12:3", "uniform:0:15", "uniform:0:16")
+    say(f"case varlen multi-step fused={fused}")
+    pairs = run_schedule(wl, 6, 501, layers=2, label="vl", fused=fused)
+    say(f"  worst {pairs[0].worst}")
+
+
+def test_varlen_pages_point_sampled():
+    """32 requests x 32 heads, lengths U{1..16}, the fused order, sampled slots."""
+    wl = W["r32_hv32_hk16_d128_varlen"]
+    say("case varlen r32 full size, sampled")
+    rng = np.random.default_rng(502)
+    sample = rng.choice(wl.num_slots, 6, replace=False)
+    pairs = run_schedule(wl, 4, synth.seed_for(wl.name, 0, 0), oracle_slots=sample, label="vlf",
+                         fused=True)
+    say(f"  worst {pairs[0].worst}")
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_plain_decode(fused):
+    """D = 1, every token kept: the replay path as a non-speculative decoder."""
+    wl = synth.Workload("d1", 5, 6, 4, 2, 128, 128, 32, 1, synth.BF16, 16, 1, "fixed:1",
+                        "uniform:0:15")
+    say(f"case decode D=1 fused={fused}")
+    pairs = run_schedule(wl, 20, 503, label="d1", fused=fused)
+    assert pairs[0].flushed_count > 0
+    say(f"  worst {pairs[0].worst}")
+
+
+def test_plain_decode_pages_point_sampled():
+    wl = W["r32_hv32_hk16_d128_d1"]
+    say("case decode r32 full size, sampled")
+    rng = np.random.default_rng(504)
+    sample = rng.choice(wl.num_slots, 6, replace=False)
+    run_schedule(wl, 18, synth.seed_for(wl.name, 0, 0), oracle_slots=sample, label="d1f",
+                 fused=True)
+
+
+@pytest.mark.parametrize("dk,dt,C,D", [(128, synth.BF16, 80, 16), (32, synth.BF16, 12, 5),
+                                       (16, synth.F32, 12, 5)])
+@pytest.mark.parametrize("fused", [False, True])
+def test_varlen_other_kernels(dk, dt, C, D, fused):
+    """The multi-chunk kernel (capacity 80) and the token-by-token kernel (small
+    dims, fp32 inputs); verify_flush runs there as flush then verify."""
+    wl = synth.Workload("vo", 3, 5, 4, 2, dk, dk, C, D, dt, max(C // 2, 2), 1, "uniform",
+                        f"uniform:0:{C - D}", f"uniform:0:{D}")
+    say(f"case varlen d={dk} {dt} C={C} D={D} fused={fused}")
+    run_schedule(wl, 5, 505 + dk + C, label=f"vo{dk}", fused=fused)
+
+
+@pytest.mark.parametrize("dk,C", [(128, 32), (128, 80), (32, 12)])
+def test_varlen_device_errors(dk, C):
+    """A length outside [0, max_draft] sets DRAFT and skips the request with no
+    writes: no outputs, no append, no flush (also when the slot is due); a
+    rollback with a > D_i sets ACCEPT."""
+    D = 4
+    wl = synth.Workload("ve", 4, 6, 4, 2, dk, dk, C, D, synth.BF16, 1, 1, "uniform",
+                        "fixed:0")
+    say(f"case varlen device errors d={dk} C={C}")
+    rng = np.random.default_rng(506 + C)
+    init = synth.make_cache_init(wl, rng)
+    init["len"][:] = [5, 6, 2, 7, 1, 0]
+    for fused in (False, True):
+        p = Pair(wl, init)
+        slots = np.array([0, 1, 2, 3], np.int32)
+        lens = np.array([-1, 5, 0, 3], np.int32)     # bad, bad (> max 4), empty, fine
+        if fused:
+            p.verify_flush(slots, 6, synth.make_draft(wl, rng), "errors", lens=lens)
+            # slot 1 is due (len 6 >= 6) but its length is bad: not flushed
+            assert int(p.gpu.len[1].item()) == 6
+            assert int(p.gpu.len[3].item()) == 0   # due, flushed, then verified
+        else:
+            p.verify(slots, synth.make_draft(wl, rng), "errors", lens=lens)
+        assert int(p.gpu.err.item()) == 16
+        p.rollback(slots, D, np.array([0, 0, 1, 2], np.int32), "errors", lens=lens)
+        # slot 2 drafted nothing: a = 1 > 0 is an ACCEPT error
+        assert int(p.gpu.err.item()) == 16 | 2
+
+
+def test_varlen_full_lengths_equal_fixed_call_bitwise():
+    """With every length equal to the maximum the varlen calls give the bits of
+    the fixed-length calls."""
+    wl = W["r32_hv32_hk16_d128_f16"]
+    say("case varlen == fixed, bitwise")
+    rng = np.random.default_rng(507)
+    init = synth.make_cache_init(wl, rng, init_len=rng.integers(0, 17, wl.num_slots))
+    a = ReplayCache.from_numpy(init, wl.hv, wl.hk, wl.dk, wl.dv, wl.cap, wl.in_dtype)
+    b = ReplayCache.from_numpy(init, wl.hv, wl.hk, wl.dk, wl.dv, wl.cap, wl.in_dtype)
+    dr = {k: to_device(v) for k, v in synth.make_draft(wl, rng).items()}
+    slots = to_device(synth.make_slot_idx(wl, rng))
+    full = to_device(np.full(wl.num_reqs, wl.draft, np.int32))
+    acc = to_device(synth.sample_accepted(wl, rng))
+    oa = a.verify_flush(slots, 16, dr["q"], dr["k"], dr["v"], dr["alpha"], dr["beta"],
+                        draft_lens=full)
+    ob = b.verify_flush(slots, 16, dr["q"], dr["k"], dr["v"], dr["alpha"], dr["beta"])
+    a.rollback(slots, wl.draft, acc, draft_lens=full)
+    b.rollback(slots, wl.draft, acc)
+    # next step: the slots left with len >= 16 are folded first, the rest fit
+    oa2 = a.verify_flush(slots, 16, dr["q"], dr["k"], dr["v"], dr["alpha"], dr["beta"],
+                         draft_lens=full)
+    ob2 = b.verify_flush(slots, 16, dr["q"], dr["k"], dr["v"], dr["alpha"], dr["beta"])
+    oa3 = a.verify(slots, dr["q"], dr["k"], dr["v"], dr["alpha"], dr["beta"], draft_lens=full)
+    ob3 = b.verify(slots, dr["q"], dr["k"], dr["v"], dr["alpha"], dr["beta"])
+    torch.cuda.synchronize()
+    assert int(a.err.item()) == 0 and int(b.err.item()) == 0
+    assert torch.equal(oa.view(torch.int32), ob.view(torch.int32))
+    assert torch.equal(oa2.view(torch.int32), ob2.view(torch.int32))
+    assert torch.equal(oa3.view(torch.int32), ob3.view(torch.int32))
+    for name in ("state", "head", "len", "ring_k", "ring_v", "ring_alpha", "ring_beta", "ring_q"):
+        x, y = getattr(a, name), getattr(b, name)
+        if x.dtype == torch.float32:
+            x, y = x.view(torch.int32), y.view(torch.int32)
+        elif x.dtype == torch.bfloat16:
+            x, y = x.view(torch.int16), y.view(torch.int16)
+        assert torch.equal(x, y), name

@@ -1163,6 +1163,7 @@ __device__ __forceinline__ int nth_bit(uint64_t m, int n) {
 
 struct Req {
   int r, s, head, len;
+  int due;  // number of due requests in the call
 };
 
 __device__ Req ordered_request(const VerifyArgs &va, int mn, int q, int lane) {
@@ -1185,7 +1186,7 @@ __device__ Req ordered_request(const VerifyArgs &va, int mn, int q, int lane) {
     const int nd = __popcll(dm);
     const int r = q < nd ? nth_bit(dm, q) : nth_bit(~dm & lanes(0), q - nd);
     return Req{r, __builtin_amdgcn_readlane(si, r), __builtin_amdgcn_readlane(hi, r),
-               __builtin_amdgcn_readlane(ni, r)};
+               __builtin_amdgcn_readlane(ni, r), nd};
   }
   auto due_mask = [&](int j) -> uint64_t {
     const int i = 64 * j + lane;
@@ -1212,7 +1213,7 @@ __device__ Req ordered_request(const VerifyArgs &va, int mn, int q, int lane) {
     }
     left -= cnt;
   }
-  Req o{r, va.slot_idx[r], 0, 0};
+  Req o{r, va.slot_idx[r], 0, 0, nd};
   if (o.s >= 0 && o.s < c.num_slots) {
     o.head = c.head[o.s];
     o.len = c.len[o.s];
@@ -1277,7 +1278,10 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyA
 
   // Every workgroup counts itself in at its end (after a barrier, so that all
   // its waves have read the pointers); the last one moves the due slots' pointers.
+  // With no due request there is nothing to move and no count is taken (every
+  // workgroup sees the same count, as no pointer changes during the call).
   auto finish = [&]() {
+    if (rq.due == 0) return;
     __syncthreads();
     if (tid == 0) {
       int last = 0;

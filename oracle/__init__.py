@@ -9,4 +9,6 @@ CPU-baseline leg use it. It shares no code with the HIP library.
   bookkeeping  pure-integer model of the ring pointers and error bits.
   wy_check     fp64 chunk (WY / UT) form of the same replay, used only to pin
                the algebra that the HIP kernels implement.
+  norm_oracle  fp64 gated RMSNorm of the GDN output and its FP8 (OCP E4M3)
+               quantisation with one scale per (token, head).
 """

@@ -102,6 +102,58 @@ def byte_model_fused(wl, lens_at_call, folded, drafts=None):
             + fold_only * wl.hv * wl.dk * wl.dv * 4 + fold_only_ring)
 
 
+def norm_leg(wl, layers, steps, warmup):
+    """The step after the recurrence: gated RMSNorm + FP8 of one layer's verify
+    output ([R * D] rows x HV heads x d_v), timed with HIP events over `steps`
+    rounds of `layers` launches, each layer on its own buffers (the 24 layers'
+    inputs do not fit in the Infinity Cache), replayed from a HIP graph. Bytes: o
+    fp32 + z bf16 read, codes written, one fp32 scale per (row, head), the d_v
+    weight."""
+    import torch
+
+    from gated_deltanet_state_replayssm_amd import synth
+    from gated_deltanet_state_replayssm_amd.cache import to_device
+    from gated_deltanet_state_replayssm_amd.norm import gated_rmsnorm_fp8
+
+    rows, H, dv = wl.num_reqs * wl.draft, wl.hv, wl.dv
+    rng = np.random.default_rng(synth.seed_for(wl.name, 0, 90))
+    w = to_device(rng.uniform(0.5, 1.5, dv).astype(np.float32))
+    torch.manual_seed(synth.seed_for(wl.name, 0, 91))
+    bufs = []
+    for L in range(layers):
+        o = torch.randn((rows, H, dv), device="cuda")
+        z = torch.randn((rows, H, dv), device="cuda").to(torch.bfloat16)
+        q = torch.empty((rows, H, dv), dtype=torch.uint8, device="cuda")
+        sc = torch.empty((rows, H), dtype=torch.float32, device="cuda")
+        bufs.append((o, z, q, sc))
+    # the launches are captured in a HIP graph: a kernel of a few microseconds
+    # would otherwise be timed at the rate the host issues launches
+    for o, z, q, sc in bufs:
+        gated_rmsnorm_fp8(o, z, w, 1e-6, q, sc)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for o, z, q, sc in bufs:
+            gated_rmsnorm_fp8(o, z, w, 1e-6, q, sc)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    marks = []
+    for it in range(warmup + steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        if it >= warmup:
+            marks.append((e0, e1))
+    torch.cuda.synchronize()
+    us = sum(a.elapsed_time(b) for a, b in marks) * 1e3 / (len(marks) * layers)
+    del g
+    nbytes = rows * H * dv * (4 + 2 + 1) + rows * H * 4 + dv * 4
+    del bufs
+    return {"us": round(us, 2), "bytes": int(nbytes), "gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "what": f"gated RMSNorm + FP8 of [{rows}][{H}][{dv}] (rows = requests x draft)"}
+
+
 def cpu_baseline(wl, seconds_budget=15.0):
     """The fp64 oracle, as it stands, on a bounded sample of the same workload:
     verify + rollback + flush of whole layers (every request, buffer 5 + draft D,
@@ -457,6 +509,7 @@ def main():
         "pages_context": {"b200_custom_kernel_us_per_layer": "23-24",
                           "b200_triton_us_per_layer": "72-80"},
     }
+    kernels["gated_rmsnorm_fp8"] = norm_leg(wl, layers, max(args.steps // 2, 5), 3)
     if "fused" in res and res["fused"]["graph_ms"] is not None:
         gm = res["fused"]["graph_ms"]
         line["graph_step"] = {"ms_per_step": round(gm, 4),

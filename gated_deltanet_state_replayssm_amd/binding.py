@@ -20,7 +20,7 @@ GDN_DERR_DRAFT = 16
 EXPORTED = ("gdn_replay_verify", "gdn_replay_rollback", "gdn_replay_flush",
             "gdn_replay_verify_flush", "gdn_replay_verify_varlen",
             "gdn_replay_verify_flush_varlen", "gdn_replay_rollback_varlen",
-            "gdn_replay_strerror", "gdn_replay_version")
+            "gdn_gated_rmsnorm_fp8", "gdn_replay_strerror", "gdn_replay_version")
 
 
 class GdnReplayCache(ctypes.Structure):
@@ -81,6 +81,8 @@ def load(path: str = LIB_PATH):
     lib.gdn_replay_verify_flush_varlen.restype = ctypes.c_int
     lib.gdn_replay_rollback_varlen.argtypes = [P, I32, VP, VP, I32, VP, VP]
     lib.gdn_replay_rollback_varlen.restype = ctypes.c_int
+    lib.gdn_gated_rmsnorm_fp8.argtypes = [I32, I32, I32, VP, VP, VP, ctypes.c_float, VP, VP, VP]
+    lib.gdn_gated_rmsnorm_fp8.restype = ctypes.c_int
     lib.gdn_replay_strerror.argtypes = [ctypes.c_int]
     lib.gdn_replay_strerror.restype = ctypes.c_char_p
     lib.gdn_replay_version.argtypes = []
@@ -182,6 +184,15 @@ def rollback_varlen(cache, num_reqs, slot_idx, draft_lens, max_draft, num_accept
     _check("gdn_replay_rollback_varlen",
            rollback_varlen_raw(cache, num_reqs, slot_idx, draft_lens, max_draft, num_accepted,
                                stream))
+
+
+def gated_rmsnorm_fp8_raw(rows, num_heads, d_v, o, z, weight, eps, q, scale, stream) -> int:
+    return load().gdn_gated_rmsnorm_fp8(rows, num_heads, d_v, o, z, weight, eps, q, scale, stream)
+
+
+def gated_rmsnorm_fp8(rows, num_heads, d_v, o, z, weight, eps, q, scale, stream) -> None:
+    _check("gdn_gated_rmsnorm_fp8",
+           gated_rmsnorm_fp8_raw(rows, num_heads, d_v, o, z, weight, eps, q, scale, stream))
 
 
 def version() -> int:

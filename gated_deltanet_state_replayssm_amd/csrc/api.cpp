@@ -226,6 +226,29 @@ int gdn_replay_flush(const gdn_replay_cache *c, int32_t num_reqs, const int32_t 
   return launch_flush(c, flush_args(c, num_reqs, slot_idx, min_len), stream);
 }
 
+int gdn_gated_rmsnorm_fp8(int32_t rows, int32_t num_heads, int32_t d_v, const float *o,
+                          const void *z, const float *weight, float eps, uint8_t *q, float *scale,
+                          hipStream_t stream) {
+  if (rows < 0 || num_heads < 1 || d_v < 1) return GDN_EINVAL;
+  if (!gdnr::norm_supported(d_v)) return GDN_EUNSUPPORTED;
+  if ((int64_t)rows * num_heads > (int64_t(1) << 33)) return GDN_EUNSUPPORTED;  // grid size
+  if (!(eps > 0.f) || eps > 1.f) return GDN_EINVAL;  // also rejects NaN
+  if (rows == 0) return GDN_OK;
+  if (!o || !z || !weight || !q || !scale) return GDN_EINVAL;
+  if (!aligned(o, 16) || !aligned(z, 8) || !aligned(weight, 16) || !aligned(q, 4) ||
+      !aligned(scale, 4))
+    return GDN_EINVAL;
+  gdnr::NormArgs a;
+  a.groups = (int64_t)rows * num_heads;
+  a.o = o;
+  a.z = z;
+  a.weight = weight;
+  a.eps = eps;
+  a.q = q;
+  a.scale = scale;
+  return gdnr::launch_gated_rmsnorm_fp8(a, d_v, stream) == hipSuccess ? GDN_OK : GDN_EHIP;
+}
+
 const char *gdn_replay_strerror(int status) {
   switch (status) {
     case GDN_OK: return "ok";

@@ -409,11 +409,6 @@ struct Stage {
 // Inclusive scan over lanes 0..31 of a wave with DPP row shifts (within rows of
 // 16 lanes) and a row broadcast of lane 15 into the second row. Lanes 32..63 get
 // their own scan of lanes 32..63.
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ float dpp_or(float identity, float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(identity), __float_as_int(v),
-                                                    CTRL, ROW_MASK, 0xf, false));
-}
 __device__ __forceinline__ float scan32_add(float v) {
   v += dpp_or<0x111, 0xf>(0.f, v);  // row_shr:1
   v += dpp_or<0x112, 0xf>(0.f, v);  // row_shr:2

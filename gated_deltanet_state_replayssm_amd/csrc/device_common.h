@@ -26,6 +26,14 @@ __device__ __forceinline__ void copy_in(void *dst, int64_t di, const void *src, 
   }
 }
 
+// v moved by the DPP control CTRL within the rows enabled by ROW_MASK; lanes
+// with no source (and rows not enabled) get identity.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_or(float identity, float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(identity), __float_as_int(v),
+                                                    CTRL, ROW_MASK, 0xf, false));
+}
+
 __device__ __forceinline__ void raise_err(int32_t *err, int32_t bit) {
   if (err) atomicOr(err, bit);
 }

@@ -58,6 +58,19 @@ hipError_t launch_verify_recurrent(const VerifyArgs &a, bool in_f32, hipStream_t
 hipError_t launch_flush_recurrent(const FlushArgs &a, bool in_f32, hipStream_t stream);
 hipError_t launch_rollback(const RollbackArgs &a, hipStream_t stream);
 
+// Gated RMSNorm + FP8 quantisation of groups of d_v values (norm.hip).
+struct NormArgs {
+  int64_t groups;        // rows * heads
+  const float *o;        // [groups][d_v] fp32
+  const void *z;         // [groups][d_v] bf16 (gate)
+  const float *weight;   // [d_v] fp32
+  float eps;
+  uint8_t *q;            // [groups][d_v] OCP E4M3 codes
+  float *scale;          // [groups] fp32
+};
+bool norm_supported(int dv);
+hipError_t launch_gated_rmsnorm_fp8(const NormArgs &a, int dv, hipStream_t stream);
+
 // head dims with a compiled kernel
 inline bool dims_supported(int dk, int dv) {
   return dk == dv && (dk == 16 || dk == 32 || dk == 64 || dk == 128);

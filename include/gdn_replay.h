@@ -223,6 +223,35 @@ int gdn_replay_rollback_varlen(const gdn_replay_cache *c, int32_t num_reqs,
                                const int32_t *slot_idx, const int32_t *draft_lens,
                                int32_t max_draft, const int32_t *num_accepted, hipStream_t stream);
 
+/*
+ * gdn_gated_rmsnorm_fp8 — the step after the recurrence: gated RMSNorm of the
+ * GDN output followed by FP8 quantisation, in one kernel ("The inference stack
+ * behind OCRia", section on fusing kernels: the gated RMSNorm and the FP8
+ * quantisation of its result run as one kernel so that the normalised values
+ * never go through HBM). For every (row t, head h) group of d_v values:
+ *     r = sqrt(mean_j o[t][h][j]^2 + eps)
+ *     y_j = o[t][h][j] / r * weight[j] * silu(z[t][h][j]),  silu(x) = x / (1 + e^-x)
+ *     scale[t][h] = max_j |y_j| / 448   (1 when every y_j is 0)
+ *     q[t][h][j] = E4M3(y_j / scale[t][h])
+ * E4M3 is the OCP 8-bit float (sign, 4 exponent bits, bias 7, 3 mantissa bits,
+ * largest finite 448), rounded to nearest even and saturating; a group
+ * dequantises as q * scale. Computed in fp32.
+ *
+ *   rows >= 0 (0 is a no-op), num_heads >= 1, d_v in {16, 32, 64, 128}.
+ *   o      [rows][num_heads][d_v] fp32 (e.g. the out of gdn_replay_verify with
+ *          rows = num_reqs * D), 16-byte aligned.
+ *   z      [rows][num_heads][d_v] bf16 gate, 8-byte aligned.
+ *   weight [d_v] fp32, shared by the heads, 16-byte aligned.   eps in (0, 1] (an
+ *          all-zero group then normalises to zeros).
+ *   q      [rows][num_heads][d_v] uint8 codes (4-byte aligned); scale
+ *          [rows][num_heads] fp32. Outputs must not alias inputs.
+ * Errors: synchronous only (EINVAL / EUNSUPPORTED / EHIP); nothing is enqueued
+ * on error.
+ */
+int gdn_gated_rmsnorm_fp8(int32_t rows, int32_t num_heads, int32_t d_v, const float *o,
+                          const void *z, const float *weight, float eps, uint8_t *q, float *scale,
+                          hipStream_t stream);
+
 /* Human-readable text of a gdn_status (static storage). */
 const char *gdn_replay_strerror(int status);
 

@@ -15,7 +15,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "gd
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(gdn_replay_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(gdn_\w+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -151,6 +151,36 @@ def test_varlen_call_validation():
     lib = b.load()
     assert lib.gdn_replay_verify_varlen(None, 1, FAKE, FAKE, 1, FAKE, FAKE, FAKE, FAKE, FAKE,
                                         FAKE, None) == b.GDN_EINVAL
+
+
+def test_norm_call_validation():
+    """gdn_gated_rmsnorm_fp8: sizes, supported head dims, eps, NULL and
+    misaligned pointers are rejected before any launch; zero rows is a no-op."""
+    f = b.gated_rmsnorm_fp8_raw
+    ok = dict(rows=4, num_heads=2, d_v=128, o=FAKE, z=FAKE, weight=FAKE, eps=1e-6, q=FAKE,
+              scale=FAKE, stream=None)
+
+    def call(**over):
+        kw = dict(ok)
+        kw.update(over)
+        return f(**kw)
+
+    assert call(rows=-1) == b.GDN_EINVAL
+    assert call(num_heads=0) == b.GDN_EINVAL
+    assert call(d_v=48) == b.GDN_EUNSUPPORTED
+    assert call(d_v=256) == b.GDN_EUNSUPPORTED
+    assert call(eps=-1.0) == b.GDN_EINVAL
+    assert call(eps=0.0) == b.GDN_EINVAL
+    assert call(eps=float("nan")) == b.GDN_EINVAL
+    for name in ("o", "z", "weight", "q", "scale"):
+        assert call(**{name: None}) == b.GDN_EINVAL, name
+    assert call(o=FAKE + 8) == b.GDN_EINVAL
+    assert call(z=FAKE + 2) == b.GDN_EINVAL
+    assert call(z=FAKE + 4) == b.GDN_EINVAL
+    assert call(weight=FAKE + 8) == b.GDN_EINVAL
+    assert call(q=FAKE + 2) == b.GDN_EINVAL
+    assert call(rows=1 << 30, num_heads=4096) == b.GDN_EUNSUPPORTED
+    assert call(rows=0, o=None, q=None) == b.GDN_OK
 
 
 def test_zero_requests_is_a_noop_without_launch():

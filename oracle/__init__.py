@@ -11,4 +11,6 @@ CPU-baseline leg use it. It shares no code with the HIP library.
                the algebra that the HIP kernels implement.
   norm_oracle  fp64 gated RMSNorm of the GDN output and its FP8 (OCP E4M3)
                quantisation with one scale per (token, head).
+  conv_oracle  fp64 short causal convolution before the recurrence, its input
+               history kept in a ring that shares the recurrence's pointers.
 """

@@ -154,6 +154,62 @@ def norm_leg(wl, layers, steps, warmup):
             "what": f"gated RMSNorm + FP8 of [{rows}][{H}][{dv}] (rows = requests x draft)"}
 
 
+def conv_leg(wl, layers, steps, warmup, width=4):
+    """The step before the recurrence: the causal convolution of the draft block
+    over the q, k, v channels (2 HK dk + HV dv), width 4, with its ring history,
+    for every layer (each with its own ring and pointers), replayed from a HIP
+    graph. Bytes: x read, y written, x appended, K - 1 history rows read, the
+    weights and bias."""
+    import torch
+
+    from gated_deltanet_state_replayssm_amd import synth
+    from gated_deltanet_state_replayssm_amd.cache import ReplayCache, to_device
+    from gated_deltanet_state_replayssm_amd.conv import ConvRing
+
+    R, D, C = wl.num_reqs, wl.draft, wl.cap
+    CH = 2 * wl.hk * wl.dk + wl.hv * wl.dv
+    rng = np.random.default_rng(synth.seed_for(wl.name, 0, 92))
+    torch.manual_seed(synth.seed_for(wl.name, 0, 93))
+    slots = to_device(np.arange(R, dtype=np.int32))
+    legs = []
+    for L in range(layers):
+        # the convolution reads only the pointers of the layer's cache
+        cache = ReplayCache(wl.num_slots, 1, 1, 16, 16, C, wl.in_dtype)
+        cache.head.copy_(to_device(rng.integers(0, C, wl.num_slots).astype(np.int32)))
+        cache.len.copy_(to_device(rng.integers(0, C - D + 1, wl.num_slots).astype(np.int32)))
+        ring = ConvRing(cache, CH, width)
+        ring.ring.normal_()
+        x = torch.randn((R, D, CH), device="cuda").to(torch.bfloat16)
+        y = torch.empty_like(x)
+        w = torch.randn((CH, width), device="cuda") * 0.5
+        b = torch.randn((CH,), device="cuda")
+        legs.append((ring, x, y, w, b))
+    for ring, x, y, w, b in legs:
+        ring.update(slots, x, w, b, y)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for ring, x, y, w, b in legs:
+            ring.update(slots, x, w, b, y)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    marks = []
+    for it in range(warmup + steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        if it >= warmup:
+            marks.append((e0, e1))
+    torch.cuda.synchronize()
+    assert all(int(ring.cache.err.item()) == 0 for ring, *_ in legs)
+    us = sum(a.elapsed_time(b) for a, b in marks) * 1e3 / (len(marks) * layers)
+    nbytes = R * D * CH * 2 * 3 + R * (width - 1) * CH * 2 + CH * (width + 1) * 4
+    del g, legs
+    return {"us": round(us, 2), "bytes": int(nbytes), "gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "what": f"causal conv width {width} over [{R}][{D}][{CH}] with ring history"}
+
+
 def cpu_baseline(wl, seconds_budget=15.0):
     """The fp64 oracle, as it stands, on a bounded sample of the same workload:
     verify + rollback + flush of whole layers (every request, buffer 5 + draft D,
@@ -510,6 +566,7 @@ def main():
                           "b200_triton_us_per_layer": "72-80"},
     }
     kernels["gated_rmsnorm_fp8"] = norm_leg(wl, layers, max(args.steps // 2, 5), 3)
+    kernels["causal_conv_update"] = conv_leg(wl, layers, max(args.steps // 2, 5), 3)
     if "fused" in res and res["fused"]["graph_ms"] is not None:
         gm = res["fused"]["graph_ms"]
         line["graph_step"] = {"ms_per_step": round(gm, 4),

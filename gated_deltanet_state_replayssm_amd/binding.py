@@ -20,7 +20,8 @@ GDN_DERR_DRAFT = 16
 EXPORTED = ("gdn_replay_verify", "gdn_replay_rollback", "gdn_replay_flush",
             "gdn_replay_verify_flush", "gdn_replay_verify_varlen",
             "gdn_replay_verify_flush_varlen", "gdn_replay_rollback_varlen",
-            "gdn_gated_rmsnorm_fp8", "gdn_replay_strerror", "gdn_replay_version")
+            "gdn_gated_rmsnorm_fp8", "gdn_causal_conv_update", "gdn_replay_strerror",
+            "gdn_replay_version")
 
 
 class GdnReplayCache(ctypes.Structure):
@@ -83,6 +84,8 @@ def load(path: str = LIB_PATH):
     lib.gdn_replay_rollback_varlen.restype = ctypes.c_int
     lib.gdn_gated_rmsnorm_fp8.argtypes = [I32, I32, I32, VP, VP, VP, ctypes.c_float, VP, VP, VP]
     lib.gdn_gated_rmsnorm_fp8.restype = ctypes.c_int
+    lib.gdn_causal_conv_update.argtypes = [P, VP, I32, I32, I32, VP, I32, VP, VP, VP, VP, VP]
+    lib.gdn_causal_conv_update.restype = ctypes.c_int
     lib.gdn_replay_strerror.argtypes = [ctypes.c_int]
     lib.gdn_replay_strerror.restype = ctypes.c_char_p
     lib.gdn_replay_version.argtypes = []
@@ -193,6 +196,19 @@ def gated_rmsnorm_fp8_raw(rows, num_heads, d_v, o, z, weight, eps, q, scale, str
 def gated_rmsnorm_fp8(rows, num_heads, d_v, o, z, weight, eps, q, scale, stream) -> None:
     _check("gdn_gated_rmsnorm_fp8",
            gated_rmsnorm_fp8_raw(rows, num_heads, d_v, o, z, weight, eps, q, scale, stream))
+
+
+def causal_conv_update_raw(cache: GdnReplayCache, conv_ring, channels, width, num_reqs, slot_idx,
+                           draft_len, x, weight, bias, y, stream) -> int:
+    return load().gdn_causal_conv_update(ctypes.byref(cache), conv_ring, channels, width, num_reqs,
+                                         slot_idx, draft_len, x, weight, bias, y, stream)
+
+
+def causal_conv_update(cache, conv_ring, channels, width, num_reqs, slot_idx, draft_len, x, weight,
+                       bias, y, stream) -> None:
+    _check("gdn_causal_conv_update",
+           causal_conv_update_raw(cache, conv_ring, channels, width, num_reqs, slot_idx, draft_len,
+                                  x, weight, bias, y, stream))
 
 
 def version() -> int:

@@ -249,6 +249,38 @@ int gdn_gated_rmsnorm_fp8(int32_t rows, int32_t num_heads, int32_t d_v, const fl
   return gdnr::launch_gated_rmsnorm_fp8(a, d_v, stream) == hipSuccess ? GDN_OK : GDN_EHIP;
 }
 
+int gdn_causal_conv_update(const gdn_replay_cache *c, void *conv_ring, int32_t channels,
+                           int32_t width, int32_t num_reqs, const int32_t *slot_idx,
+                           int32_t draft_len, const void *x, const float *weight,
+                           const float *bias, void *y, hipStream_t stream) {
+  int st = check_cache(c);
+  if (st != GDN_OK) return st;
+  if (channels < 2 || channels % 2 != 0) return GDN_EINVAL;
+  if (!gdnr::conv_width_supported(width)) return GDN_EUNSUPPORTED;
+  if (c->in_dtype != GDN_BF16) return GDN_EUNSUPPORTED;
+  if (num_reqs < 0 || num_reqs > c->num_slots) return GDN_EINVAL;
+  if (draft_len < 1 || draft_len + width - 1 > c->ring_cap) return GDN_EINVAL;
+  if ((channels / 2 + 255) / 256 > 65535 || num_reqs > 65535) return GDN_EUNSUPPORTED;  // grid
+  if (draft_len > 65535) return GDN_EUNSUPPORTED;
+  if (num_reqs == 0) return GDN_OK;
+  if (!conv_ring || !slot_idx || !x || !weight || !y) return GDN_EINVAL;
+  if (!aligned(conv_ring, 4) || !aligned(slot_idx, 4) || !aligned(x, 4) || !aligned(weight, 4) ||
+      (bias && !aligned(bias, 4)) || !aligned(y, 4))
+    return GDN_EINVAL;
+  gdnr::ConvArgs a;
+  a.c = view_of(c);
+  a.num_reqs = num_reqs;
+  a.draft = draft_len;
+  a.channels = channels;
+  a.slot_idx = slot_idx;
+  a.ring = conv_ring;
+  a.x = x;
+  a.weight = weight;
+  a.bias = bias;
+  a.y = y;
+  return gdnr::launch_causal_conv_update(a, width, stream) == hipSuccess ? GDN_OK : GDN_EHIP;
+}
+
 const char *gdn_replay_strerror(int status) {
   switch (status) {
     case GDN_OK: return "ok";

@@ -71,6 +71,21 @@ struct NormArgs {
 bool norm_supported(int dv);
 hipError_t launch_gated_rmsnorm_fp8(const NormArgs &a, int dv, hipStream_t stream);
 
+// Causal convolution of a draft block with its input ring (conv.hip); the ring
+// shares head / len / capacity with the cache c.
+struct ConvArgs {
+  CacheView c;
+  int32_t num_reqs, draft, channels;
+  const int32_t *slot_idx;
+  void *ring;            // [num_slots][C][channels] bf16
+  const void *x;         // [num_reqs][draft][channels] bf16
+  const float *weight;   // [channels][width]
+  const float *bias;     // [channels] or null
+  void *y;               // [num_reqs][draft][channels] bf16
+};
+bool conv_width_supported(int k);
+hipError_t launch_causal_conv_update(const ConvArgs &a, int width, hipStream_t stream);
+
 // head dims with a compiled kernel
 inline bool dims_supported(int dk, int dv) {
   return dk == dv && (dk == 16 || dk == 32 || dk == 64 || dk == 128);

@@ -252,6 +252,39 @@ int gdn_gated_rmsnorm_fp8(int32_t rows, int32_t num_heads, int32_t d_v, const fl
                           const void *z, const float *weight, float eps, uint8_t *q, float *scale,
                           hipStream_t stream);
 
+/*
+ * gdn_causal_conv_update — the step before the recurrence: the short causal
+ * convolution of a GDN layer over a draft block, with its state kept the
+ * ReplaySSM way. GDN layers convolve their q, k, v projections causally before
+ * the recurrence ("The inference stack behind OCRia", LlamaIndex, which lists a
+ * faster causal convolution for GDN layers among its kernels); the state is the
+ * last K - 1 inputs of the committed stream, and, as for the recurrence's
+ * inputs ("Making speculative verification cheaper"), it lives in a ring whose
+ * pointers move instead of being restored:
+ *   conv_ring [num_slots][C][channels] bf16, caller-owned, zero when a slot starts;
+ *             it shares num_slots, C, head, len and err with the cache c.
+ * For request i (slot s = slot_idx[i], h = head[s], n = len[s]) and channel ch:
+ *   y[i][j][ch] = silu(bias[ch] + sum_{t<K} weight[ch][t] * x_{j-K+1+t}[ch]),
+ * where x_{-m} (m >= 1) is conv_ring[s][(h + n - m) mod C][ch]; then the draft x
+ * is appended at conv_ring[s][(h + n + j) mod C] (where gdn_replay_verify appends
+ * its rows). Pointers are not changed: gdn_replay_rollback and gdn_replay_flush
+ * (or verify_flush) move them for both rings. Call it before the step's
+ * rollback, with the same slots and D as the step's verify.
+ *   channels even >= 2; width K in 1..8; D >= 1 with D + K - 1 <= C (the draft
+ *   never overwrites the history it reads); inputs bf16 only (in_dtype).
+ *   x, y      [num_reqs][D][channels] bf16 (y rounded to nearest even), 4-byte aligned.
+ *   weight    [channels][K] fp32;  bias [channels] fp32 or NULL.
+ * Only the last K - 1 committed inputs are read, so len + D may exceed C (the
+ * draft then overwrites inputs no step reads again): the call can run before a
+ * gdn_replay_verify_flush that folds the due slots in the same step.
+ * Device errors: SLOT, POINTER as for verify: the request is skipped with no
+ * writes.
+ */
+int gdn_causal_conv_update(const gdn_replay_cache *c, void *conv_ring, int32_t channels,
+                           int32_t width, int32_t num_reqs, const int32_t *slot_idx,
+                           int32_t draft_len, const void *x, const float *weight,
+                           const float *bias, void *y, hipStream_t stream);
+
 /* Human-readable text of a gdn_status (static storage). */
 const char *gdn_replay_strerror(int status);
 

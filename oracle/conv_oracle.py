@@ -28,13 +28,17 @@ committed stream, so it gets the same treatment as the recurrence's inputs:
 
 Readings taken (listed in the design notes): depthwise, width K, bias optional,
 silu after the convolution, fp32 weights, bf16 inputs; the ring needs
-C >= D + K - 1 so that the draft never overwrites the history it reads.
+C >= D + K - 1 so that the draft never overwrites the history it reads. Only the
+last K - 1 committed inputs are ever read, so (unlike the recurrence's ring,
+whose committed rows wait for the flush) len + D may exceed C: the draft then
+overwrites committed inputs that no step reads again. This lets the step run
+before a verify_flush that folds the due slots first.
 """
 from __future__ import annotations
 
 import numpy as np
 
-from .gdn_oracle import ERR_CAPACITY, ERR_POINTER, ERR_SLOT, to_f64
+from .gdn_oracle import ERR_POINTER, ERR_SLOT, to_f64
 
 
 def silu(x):
@@ -50,16 +54,19 @@ class ConvOracle:
         self.cap = int(cap)
         self.err = 0
 
-    def update(self, head, length, slot_idx, x, weight, bias=None) -> np.ndarray:
+    def update(self, head, length, slot_idx, x, weight, bias=None, magnitudes=False):
         """Outputs [R, D, CH] (NaN for skipped requests) of the draft x [R, D, CH];
         appends x to the ring. head / length: the slots' pointers before the
-        step's rollback (they are not changed here)."""
+        step's rollback (they are not changed here). With magnitudes=True also
+        returns |b| + sum_i |w_i x_i| per output (the scale of the rounding
+        error of any evaluation of the sum)."""
         slot_idx = np.asarray(slot_idx)
         R, D, CH = np.asarray(x).shape
         w = np.asarray(weight, dtype=np.float64)          # [CH, K]
         K = w.shape[1]
         b = np.zeros(CH) if bias is None else np.asarray(bias, dtype=np.float64)
         out = np.full((R, D, CH), np.nan)
+        mag = np.full((R, D, CH), np.nan)
         for i in range(R):
             s = int(slot_idx[i])
             if s < 0 or s >= self.ring.shape[0]:
@@ -69,17 +76,17 @@ class ConvOracle:
             if not (0 <= h < self.cap and 0 <= n <= self.cap):
                 self.err |= ERR_POINTER
                 continue
-            if n + D > self.cap:
-                self.err |= ERR_CAPACITY
-                continue
             # history: the K - 1 inputs before the draft, oldest first
             hist = [to_f64(self.ring[s, (h + n - (K - 1) + m) % self.cap]) for m in range(K - 1)]
             seq = hist + [to_f64(np.asarray(x[i, j])) for j in range(D)]
             for j in range(D):
                 acc = b.copy()
+                m = np.abs(b)
                 for t in range(K):
                     acc = acc + w[:, t] * seq[j + t]
+                    m = m + np.abs(w[:, t] * seq[j + t])
                 out[i, j] = silu(acc)
+                mag[i, j] = m
             for j in range(D):
                 self.ring[s, (h + n + j) % self.cap] = x[i, j]
-        return out
+        return (out, mag) if magnitudes else out

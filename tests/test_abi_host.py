@@ -183,6 +183,35 @@ def test_norm_call_validation():
     assert call(rows=0, o=None, q=None) == b.GDN_OK
 
 
+def test_conv_call_validation():
+    """gdn_causal_conv_update: cache checks, channel count, width, D + K - 1 <= C,
+    bf16 inputs only, NULL / misaligned pointers; zero requests is a no-op."""
+    f = b.causal_conv_update_raw
+    c = _cache(ring_cap=8)
+    ok = dict(conv_ring=FAKE, channels=64, width=4, num_reqs=2, slot_idx=FAKE, draft_len=4,
+              x=FAKE, weight=FAKE, bias=None, y=FAKE, stream=None)
+
+    def call(cache=c, **over):
+        kw = dict(ok)
+        kw.update(over)
+        return f(cache, **kw)
+
+    assert call(cache=_cache(num_slots=0)) == b.GDN_EINVAL
+    assert call(channels=63) == b.GDN_EINVAL
+    assert call(channels=0) == b.GDN_EINVAL
+    assert call(width=0) == b.GDN_EUNSUPPORTED
+    assert call(width=9) == b.GDN_EUNSUPPORTED
+    assert call(draft_len=6) == b.GDN_EINVAL            # 6 + 4 - 1 > 8
+    assert call(draft_len=0) == b.GDN_EINVAL
+    assert call(num_reqs=5) == b.GDN_EINVAL
+    assert call(cache=_cache(ring_cap=8, in_dtype=b.GDN_F32)) == b.GDN_EUNSUPPORTED
+    for name in ("conv_ring", "slot_idx", "x", "weight", "y"):
+        assert call(**{name: None}) == b.GDN_EINVAL, name
+    assert call(x=FAKE + 2) == b.GDN_EINVAL
+    assert call(bias=FAKE + 2) == b.GDN_EINVAL
+    assert call(num_reqs=0, x=None, conv_ring=None) == b.GDN_OK
+
+
 def test_zero_requests_is_a_noop_without_launch():
     c = _cache()
     assert _verify(c, num_reqs=0, q=None, k=None) == b.GDN_OK

@@ -78,10 +78,36 @@ def test_errors_skip_the_request():
     C, CH, D = 8, 4, 4
     ring = np.zeros((2, C, CH), np.float32)
     orc = co.ConvOracle(ring, C)
-    x = np.ones((3, D, CH), np.float32)
-    y = orc.update(np.array([0, 9]), np.array([5, 0]), [0, 1, 7], x, np.ones((CH, 4)))
-    assert orc.err == go.ERR_CAPACITY | go.ERR_POINTER | go.ERR_SLOT
+    x = np.ones((2, D, CH), np.float32)
+    y = orc.update(np.array([0, 9]), np.array([5, 0]), [1, 7], x, np.ones((CH, 4)))
+    assert orc.err == go.ERR_POINTER | go.ERR_SLOT
     assert np.isnan(y).all() and not orc.ring.any()
+
+
+def test_long_committed_window_keeps_the_history():
+    """len + D > C is fine for the convolution: the draft overwrites committed
+    inputs older than the K - 1 it reads, and the next step still reads the
+    right ones (the shift kernel returns the inputs K - 1 tokens back)."""
+    K, C, CH, D = 4, 8, 2, 4
+    rng = np.random.default_rng(5)
+    orc = co.ConvOracle(np.zeros((1, C, CH), np.float32), C)
+    w = np.zeros((CH, K)); w[:, 0] = 1
+    head, n = np.array([0]), np.array([7])
+    stream = rng.standard_normal((7, CH)).astype(np.float32)
+    for t in range(7):
+        orc.ring[0, t] = stream[t]
+    x = rng.standard_normal((1, D, CH)).astype(np.float32)
+    y = orc.update(head, n, [0], x, w)
+    assert orc.err == 0
+    np.testing.assert_allclose(y[0], _silu(np.concatenate([stream[4:], x[0, :1]]).astype(np.float64)),
+                               rtol=1e-15)
+    # the 7 committed tokens were folded (head 7, len 0) and all D accepted
+    # (len 4): the next history is x[1:], at positions 0..2 now
+    x2 = rng.standard_normal((1, D, CH)).astype(np.float32)
+    y2 = orc.update(np.array([7]), np.array([4]), [0], x2, w)
+    assert orc.err == 0
+    np.testing.assert_allclose(y2[0], _silu(np.concatenate([x[0, 1:], x2[0, :1]]).astype(np.float64)),
+                               rtol=1e-15)
 
 
 def test_planted_history_mistake_is_caught(monkeypatch):

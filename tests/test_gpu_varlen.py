@@ -63,12 +63,13 @@ def test_plain_decode_pages_point_sampled():
                  fused=True)
 
 
-@pytest.mark.parametrize("dk,dt,C,D", [(128, synth.BF16, 80, 16), (32, synth.BF16, 12, 5),
-                                       (16, synth.F32, 12, 5)])
+@pytest.mark.parametrize("dk,dt,C,D", [(128, synth.BF16, 80, 16), (64, synth.BF16, 32, 16),
+                                       (32, synth.BF16, 12, 5), (16, synth.F32, 12, 5)])
 @pytest.mark.parametrize("fused", [False, True])
 def test_varlen_other_kernels(dk, dt, C, D, fused):
-    """The multi-chunk kernel (capacity 80) and the token-by-token kernel (small
-    dims, fp32 inputs); verify_flush runs there as flush then verify."""
+    """The multi-chunk kernel (capacity 80), the d = 64 kernels, and the
+    token-by-token kernel (small dims, fp32 inputs; verify_flush runs there as
+    flush then verify)."""
     wl = synth.Workload("vo", 3, 5, 4, 2, dk, dk, C, D, dt, max(C // 2, 2), 1, "uniform",
                         f"uniform:0:{C - D}", f"uniform:0:{D}")
     say(f"case varlen d={dk} {dt} C={C} D={D} fused={fused}")

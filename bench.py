@@ -2,12 +2,14 @@
 
 One step = the whole path over every GDN layer of the model for one batch
 ("The inference stack behind OCRia", section "Making speculative verification
-cheaper": 32 concurrent requests, 24 GDN layers). Two orders of the same work
+cheaper": 32 concurrent requests, 24 GDN layers). Three orders of the same work
 are timed, each on its own caches built from the same seeded inputs:
 
   fused     verify_flush on all layers (the periodic flush folded into the
             verify of the next step), then rollback on all layers;
-  separate  verify on all layers, rollback on all layers, flush on all layers.
+  separate  verify on all layers, rollback on all layers, flush on all layers;
+  step      rollback_verify_flush on all layers: one call per layer and step,
+            the previous step's rollback and the flush folded into the verify.
 
 Each layer has its own cache (state + ring + pointers), so the 24 states (1.5 GiB
 at 32 requests) do not fit in the 256 MB Infinity Cache and every call streams
@@ -16,17 +18,19 @@ its state from HBM.
 Timing: HIP events on the launch stream bracket each group of 24 launches of
 every timed step. The headline value is the verify + flush time per layer in
 microseconds (the fused kernel's time, or verify + flush for the separate
-order), averaged over the timed steps. Algorithmic bytes come from the byte
+order), averaged over the timed steps; each order also reports its whole step
+per layer (rollback included). Algorithmic bytes come from the byte
 model below, evaluated with the actual buffer lengths of every call (tracked on
 the host from the known schedule).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
-                    [--path both|fused|separate]
+                    [--path all|fused|separate|step]
     python bench.py --sweep [--steps K] [--warmup W]   (replay cost vs buffer length)
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -330,7 +334,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="r32_hv32_hk16_d128_f16")
     ap.add_argument("--layers", type=int, default=None)
-    ap.add_argument("--path", choices=("both", "fused", "separate"), default="both")
+    ap.add_argument("--path", choices=("all", "fused", "separate", "step"), default="all")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the step benchmark: verify at fixed committed-buffer "
@@ -360,7 +364,7 @@ def main():
     wl = synth.WORKLOADS[args.workload]
     layers = args.layers or wl.layers
     stream = torch.cuda.current_stream()
-    paths = ("fused", "separate") if args.path == "both" else (args.path,)
+    paths = ("fused", "separate", "step") if args.path == "all" else (args.path,)
 
     inits = []
     for L in range(layers):
@@ -392,9 +396,22 @@ def main():
         # the host's copy of the schedule (identical on every layer)
         sched = []
         lens = init_len.copy()
+        # step order: accepted count and draft length of each slot's previous
+        # draft (a slot missing from a batch drops its pending draft: all rejected)
+        p_acc = np.zeros(wl.num_slots, np.int32)
+        p_len = np.zeros(wl.num_slots, np.int32)
         for slots, acc, dl in steps:
+            extra = {}
+            if path == "step":
+                pa, pl = p_acc[slots].copy(), p_len[slots].copy()
+                extra = dict(pacc=to_device(pa), plens=None if dl is None else to_device(pl))
+                lens[slots] += pa
+                p_acc[:] = 0
+                p_len[:] = 0
+                p_acc[slots] = acc
+                p_len[slots] = wl.draft if dl is None else dl
             lv = lens[slots].copy()
-            if path == "fused":
+            if path in ("fused", "step"):
                 due = lv >= F
                 folded = lv[due].copy()
                 lens[slots] = np.where(due, 0, lv) + acc
@@ -403,29 +420,63 @@ def main():
                 due = lens[slots] >= F
                 folded = lens[slots][due].copy()
                 lens[slots[due]] = 0
+            if path == "step":
+                lens[slots] = np.where(due, 0, lv)
             sched.append(dict(slots=to_device(slots), acc=to_device(acc), lv=lv, folded=folded,
-                              dl=None if dl is None else to_device(dl), drafts=dl))
+                              dl=None if dl is None else to_device(dl), drafts=dl, **extra))
         torch.cuda.synchronize()
 
-        def run_step(step, marks):
+        # The timed loop calls the C entry points with arguments marshalled
+        # beforehand (the cache methods' per-call checks and ctypes set-up cost
+        # more host time than a short kernel takes, which would time the host).
+        lib = binding.load()
+        sh = stream.cuda_stream
+        refs = [ctypes.byref(c.struct()) for c in caches]
+        ptr = lambda t: None if t is None else t.data_ptr()
+        dptr = [[tuple(d[x].data_ptr() for x in ("q", "k", "v", "alpha", "beta")) for d in ds]
+                for ds in drafts]
+        R, D, FM, outp = wl.num_reqs, wl.draft, wl.flush_min_len, out.data_ptr()
+
+        def prepared(step):
             sc = sched[step]
+            sl, dl = ptr(sc["slots"]), ptr(sc["dl"])
+            main, rb, fl = [], [], []
+            for L in range(layers):
+                dp = dptr[L][step % 2] + (outp, sh)
+                if path == "fused":
+                    main.append((lib.gdn_replay_verify_flush, (refs[L], R, sl, D, FM) + dp)
+                                if dl is None else
+                                (lib.gdn_replay_verify_flush_varlen,
+                                 (refs[L], R, sl, dl, D, FM) + dp))
+                elif path == "step":
+                    main.append((lib.gdn_replay_rollback_verify_flush,
+                                 (refs[L], R, sl, ptr(sc["pacc"]), ptr(sc["plens"]), D, dl, D,
+                                  FM) + dp))
+                else:
+                    main.append((lib.gdn_replay_verify, (refs[L], R, sl, D) + dp)
+                                if dl is None else
+                                (lib.gdn_replay_verify_varlen, (refs[L], R, sl, dl, D) + dp))
+                if path != "step":
+                    rb.append((lib.gdn_replay_rollback, (refs[L], R, sl, D, ptr(sc["acc"]), sh))
+                              if dl is None else
+                              (lib.gdn_replay_rollback_varlen,
+                               (refs[L], R, sl, dl, D, ptr(sc["acc"]), sh)))
+                if path == "separate":
+                    fl.append((lib.gdn_replay_flush, (refs[L], R, sl, FM, sh)))
+            return main, rb, fl
+
+        calls = [prepared(step) for step in range(total)]
+        status = []
+
+        def run_step(step, marks):
+            main, rb, fl = calls[step]
             e = [ev() for _ in range(4)]
             e[0].record(stream)
-            for L in range(layers):
-                d = drafts[L][step % 2]
-                if path == "fused":
-                    caches[L].verify_flush(sc["slots"], wl.flush_min_len, d["q"], d["k"], d["v"],
-                                           d["alpha"], d["beta"], out=out, draft_lens=sc["dl"])
-                else:
-                    caches[L].verify(sc["slots"], d["q"], d["k"], d["v"], d["alpha"], d["beta"],
-                                     out=out, draft_lens=sc["dl"])
+            status.extend([fn(*a) for fn, a in main])
             e[1].record(stream)
-            for L in range(layers):
-                caches[L].rollback(sc["slots"], wl.draft, sc["acc"], draft_lens=sc["dl"])
+            status.extend([fn(*a) for fn, a in rb])
             e[2].record(stream)
-            if path == "separate":
-                for L in range(layers):
-                    caches[L].flush(sc["slots"], wl.flush_min_len)
+            status.extend([fn(*a) for fn, a in fl])
             e[3].record(stream)
             marks.append(e)
 
@@ -447,13 +498,14 @@ def main():
             tr += e[1].elapsed_time(e[2])
             tf += e[2].elapsed_time(e[3])
             sc = sched[step]
-            if path == "fused":
+            if path in ("fused", "step"):
                 b_v, b_f = byte_model_fused(wl, sc["lv"], sc["folded"], sc["drafts"]), 0
             else:
                 b_v, b_f = byte_model(wl, sc["lv"], sc["folded"], sc["drafts"])
             vb += b_v * layers          # every layer sees the same lengths
             fb += b_f * layers
-        graph_ms = graph_leg(caches, sched) if path == "fused" else None
+        graph_ms = graph_leg(caches, sched, path) if path in ("fused", "step") else None
+        assert not any(status), f"{path}: call status {sorted(set(status))}"
         errs = [int(c.err.item()) for c in caches]
         assert not any(errs), f"{path}: device error bits set: {errs}"
         del caches
@@ -464,37 +516,47 @@ def main():
                  us_flush=tf * 1e3 / n_launch if path == "separate" else 0.0,
                  v_bytes=vb / n_launch, f_bytes=fb / n_launch)
         r["us_layer"] = r["us_verify"] + r["us_flush"]
+        r["us_step_layer"] = r["us_layer"] + r["us_rollback"]
         r["bytes_layer"] = r["v_bytes"] + r["f_bytes"]
         r["gbps"] = r["bytes_layer"] / (r["us_layer"] * 1e-6) / 1e9
         r["v_gbps"] = r["v_bytes"] / (r["us_verify"] * 1e-6) / 1e9
         r["f_gbps"] = r["f_bytes"] / (r["us_flush"] * 1e-6) / 1e9 if r["us_flush"] > 0 else 0.0
         return r
 
-    def graph_leg(caches, sched):
+    def graph_leg(caches, sched, path):
         """Secondary figure: one whole step (verify_flush then rollback on every
-        layer) captured once in a HIP graph and replayed for the timed steps'
-        schedules, whose slot permutation and accept counts are copied into the
-        graph's input buffers before each replay. Returns ms per replayed step
-        (HIP events around each replay)."""
-        slots_buf = sched[0]["slots"].clone()
-        acc_buf = sched[0]["acc"].clone()
-        dl_buf = None if sched[0]["dl"] is None else sched[0]["dl"].clone()
+        layer, or rollback_verify_flush on every layer) captured once in a HIP
+        graph and replayed for the timed steps' schedules, whose slot
+        permutation, accept counts and lengths are copied into the graph's input
+        buffers before each replay. Returns ms per replayed step (HIP events
+        around each replay)."""
+        clone = lambda key: None if sched[0].get(key) is None else sched[0][key].clone()
+        bufs = {key: clone(key) for key in ("slots", "acc", "dl", "pacc", "plens")}
+        slots_buf, acc_buf, dl_buf = bufs["slots"], bufs["acc"], bufs["dl"]
         d = drafts
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for L in range(layers):
                 dd = d[L][0]
-                caches[L].verify_flush(slots_buf, wl.flush_min_len, dd["q"], dd["k"], dd["v"],
-                                       dd["alpha"], dd["beta"], out=out, draft_lens=dl_buf)
-            for L in range(layers):
-                caches[L].rollback(slots_buf, wl.draft, acc_buf, draft_lens=dl_buf)
+                if path == "step":
+                    caches[L].rollback_verify_flush(slots_buf, bufs["pacc"], wl.draft,
+                                                    wl.flush_min_len, dd["q"], dd["k"], dd["v"],
+                                                    dd["alpha"], dd["beta"], out=out,
+                                                    prev_draft_lens=bufs["plens"],
+                                                    draft_lens=dl_buf)
+                else:
+                    caches[L].verify_flush(slots_buf, wl.flush_min_len, dd["q"], dd["k"],
+                                           dd["v"], dd["alpha"], dd["beta"], out=out,
+                                           draft_lens=dl_buf)
+            if path != "step":
+                for L in range(layers):
+                    caches[L].rollback(slots_buf, wl.draft, acc_buf, draft_lens=dl_buf)
         torch.cuda.synchronize()
         times = []
         for step in range(args.warmup, total):
-            slots_buf.copy_(sched[step]["slots"])
-            acc_buf.copy_(sched[step]["acc"])
-            if dl_buf is not None:
-                dl_buf.copy_(sched[step]["dl"])
+            for key, buf in bufs.items():
+                if buf is not None:
+                    buf.copy_(sched[step][key])
             e0, e1 = ev(), ev()
             e0.record(stream)
             g.replay()
@@ -515,13 +577,19 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    head = res["fused"] if "fused" in res else res["separate"]
+    order = next(p for p in ("fused", "separate", "step") if p in res)
+    head = res[order]
     kernels = {}
     if "fused" in res:
         f = res["fused"]
         kernels["verify_flush"] = {"us": round(f["us_verify"], 2), "bytes": int(f["v_bytes"]),
                                    "gbps": round(f["v_gbps"], 1)}
         kernels["rollback_fused_order"] = {"us": round(f["us_rollback"], 2)}
+    if "step" in res:
+        st = res["step"]
+        kernels["rollback_verify_flush"] = {"us": round(st["us_verify"], 2),
+                                            "bytes": int(st["v_bytes"]),
+                                            "gbps": round(st["v_gbps"], 1)}
     if "separate" in res:
         sp = res["separate"]
         kernels["verify"] = {"us": round(sp["us_verify"], 2), "bytes": int(sp["v_bytes"]),
@@ -529,11 +597,13 @@ def main():
         kernels["flush"] = {"us": round(sp["us_flush"], 2), "bytes": int(sp["f_bytes"]),
                             "gbps": round(sp["f_gbps"], 1)}
         kernels["rollback"] = {"us": round(sp["us_rollback"], 2)}
-    if "fused" in res:
-        dominant, dom = "verify_flush", kernels["verify_flush"]
-    else:
+    if order == "fused":
+        dominant = "verify_flush"
+    elif order == "separate":
         dominant = "verify" if kernels["verify"]["us"] >= kernels["flush"]["us"] else "flush"
-        dom = kernels[dominant]
+    else:
+        dominant = "rollback_verify_flush"
+    dom = kernels[dominant]
     line = {
         "metric": METRIC,
         "value": round(head["us_layer"], 2),
@@ -552,7 +622,7 @@ def main():
                    "ring_cap": wl.cap, "flush_min_len": wl.flush_min_len, "layers": layers,
                    "draft_lens": wl.draft_lens,
                    "inputs": wl.in_dtype, "state": "f32",
-                   "order": "fused" if "fused" in res else "separate"},
+                   "order": order},
         "hbm_gbps": round(head["gbps"], 1),
         "hbm_frac": round(head["gbps"] / HBM_PEAK_GBPS, 4),
         "bytes_per_layer": int(head["bytes_layer"]),
@@ -573,6 +643,15 @@ def main():
                               "us_per_layer": round(gm * 1e3 / layers, 2),
                               "what": "verify_flush + rollback on every layer, one HIP graph "
                                       "replay per step, HIP events around each replay"}
+    line["whole_step_us_per_layer"] = {p: round(r["us_step_layer"], 2) for p, r in res.items()}
+    if "step" in res:
+        st = res["step"]
+        line["one_call_step"] = {"us_per_layer": round(st["us_layer"], 2),
+                                 "hbm_gbps": round(st["gbps"], 1),
+                                 "bytes_per_layer": int(st["bytes_layer"]),
+                                 "graph_ms_per_step": round(st["graph_ms"], 4),
+                                 "what": "rollback_verify_flush on every layer: the previous "
+                                         "step's rollback and the flush folded into the verify"}
     if "separate" in res:
         sp = res["separate"]
         line["separate_order"] = {"us_per_layer": round(sp["us_layer"], 2),

@@ -20,6 +20,7 @@ GDN_DERR_DRAFT = 16
 EXPORTED = ("gdn_replay_verify", "gdn_replay_rollback", "gdn_replay_flush",
             "gdn_replay_verify_flush", "gdn_replay_verify_varlen",
             "gdn_replay_verify_flush_varlen", "gdn_replay_rollback_varlen",
+            "gdn_replay_rollback_verify_flush",
             "gdn_gated_rmsnorm_fp8", "gdn_causal_conv_update", "gdn_replay_strerror",
             "gdn_replay_version")
 
@@ -82,6 +83,9 @@ def load(path: str = LIB_PATH):
     lib.gdn_replay_verify_flush_varlen.restype = ctypes.c_int
     lib.gdn_replay_rollback_varlen.argtypes = [P, I32, VP, VP, I32, VP, VP]
     lib.gdn_replay_rollback_varlen.restype = ctypes.c_int
+    lib.gdn_replay_rollback_verify_flush.argtypes = [P, I32, VP, VP, VP, I32, VP, I32, I32, VP,
+                                                     VP, VP, VP, VP, VP, VP]
+    lib.gdn_replay_rollback_verify_flush.restype = ctypes.c_int
     lib.gdn_gated_rmsnorm_fp8.argtypes = [I32, I32, I32, VP, VP, VP, ctypes.c_float, VP, VP, VP]
     lib.gdn_gated_rmsnorm_fp8.restype = ctypes.c_int
     lib.gdn_causal_conv_update.argtypes = [P, VP, I32, I32, I32, VP, I32, VP, VP, VP, VP, VP]
@@ -147,6 +151,15 @@ def rollback_varlen_raw(cache: GdnReplayCache, num_reqs, slot_idx, draft_lens, m
                                              max_draft, num_accepted, stream)
 
 
+def rollback_verify_flush_raw(cache: GdnReplayCache, num_reqs, slot_idx, num_accepted,
+                              prev_draft_lens, prev_draft, draft_lens, draft_len, min_len, q, k,
+                              v, alpha, beta, out, stream) -> int:
+    return load().gdn_replay_rollback_verify_flush(ctypes.byref(cache), num_reqs, slot_idx,
+                                                   num_accepted, prev_draft_lens, prev_draft,
+                                                   draft_lens, draft_len, min_len, q, k, v, alpha,
+                                                   beta, out, stream)
+
+
 def verify(cache, num_reqs, slot_idx, draft_len, q, k, v, alpha, beta, out, stream) -> None:
     _check("gdn_replay_verify",
            verify_raw(cache, num_reqs, slot_idx, draft_len, q, k, v, alpha, beta, out, stream))
@@ -187,6 +200,15 @@ def rollback_varlen(cache, num_reqs, slot_idx, draft_lens, max_draft, num_accept
     _check("gdn_replay_rollback_varlen",
            rollback_varlen_raw(cache, num_reqs, slot_idx, draft_lens, max_draft, num_accepted,
                                stream))
+
+
+def rollback_verify_flush(cache, num_reqs, slot_idx, num_accepted, prev_draft_lens, prev_draft,
+                          draft_lens, draft_len, min_len, q, k, v, alpha, beta, out,
+                          stream) -> None:
+    _check("gdn_replay_rollback_verify_flush",
+           rollback_verify_flush_raw(cache, num_reqs, slot_idx, num_accepted, prev_draft_lens,
+                                     prev_draft, draft_lens, draft_len, min_len, q, k, v, alpha,
+                                     beta, out, stream))
 
 
 def gated_rmsnorm_fp8_raw(rows, num_heads, d_v, o, z, weight, eps, q, scale, stream) -> int:

@@ -161,6 +161,23 @@ class ReplayCache:
                                         draft_lens.data_ptr(), D, *args)
         return out
 
+    def rollback_verify_flush(self, slot_idx, num_accepted, prev_draft: int, min_len: int, q, k,
+                              v, alpha, beta, out=None, stream=None, prev_draft_lens=None,
+                              draft_lens=None) -> torch.Tensor:
+        """rollback(prev_draft, num_accepted) then verify_flush(min_len) of this
+        step's draft, in one call (gdn_replay_rollback_verify_flush)."""
+        R, D, out = self._draft_args(slot_idx, q, k, v, alpha, beta, out)
+        _need(num_accepted, "num_accepted", torch.int32, (R,), self.device)
+        lens = self._lens(draft_lens, R)
+        plens = self._lens(prev_draft_lens, R)
+        binding.rollback_verify_flush(
+            self.struct(), R, slot_idx.data_ptr(), num_accepted.data_ptr(),
+            None if plens is None else plens.data_ptr(), int(prev_draft),
+            None if lens is None else lens.data_ptr(), D, int(min_len), q.data_ptr(), k.data_ptr(),
+            v.data_ptr(), alpha.data_ptr(), beta.data_ptr(), out.data_ptr(),
+            _stream_handle(stream))
+        return out
+
     def rollback(self, slot_idx, draft_len: int, num_accepted, stream=None,
                  draft_lens=None) -> None:
         R = slot_idx.shape[0]

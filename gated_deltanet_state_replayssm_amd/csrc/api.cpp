@@ -77,6 +77,9 @@ int verify_args(const gdn_replay_cache *c, int32_t num_reqs, const int32_t *slot
   a->draft = draft_len;
   a->slot_idx = slot_idx;
   a->draft_lens = varlen ? draft_lens : nullptr;
+  a->prev_accepted = nullptr;
+  a->prev_draft_lens = nullptr;
+  a->prev_draft = 0;
   a->q = q;
   a->k = k;
   a->v = v;
@@ -203,6 +206,36 @@ int gdn_replay_verify_flush_varlen(const gdn_replay_cache *c, int32_t num_reqs,
                                    const float *beta, float *out, hipStream_t stream) {
   return verify_flush_impl(c, num_reqs, slot_idx, max_draft, min_len, q, k, v, alpha, beta, out,
                            stream, true, draft_lens);
+}
+
+int gdn_replay_rollback_verify_flush(const gdn_replay_cache *c, int32_t num_reqs,
+                                     const int32_t *slot_idx, const int32_t *num_accepted,
+                                     const int32_t *prev_draft_lens, int32_t prev_draft,
+                                     const int32_t *draft_lens, int32_t draft_len,
+                                     int32_t min_len, const void *q, const void *k, const void *v,
+                                     const float *alpha, const float *beta, float *out,
+                                     hipStream_t stream) {
+  gdnr::VerifyArgs a;
+  const bool varlen = draft_lens != nullptr;
+  int st = verify_args(c, num_reqs, slot_idx, draft_len, q, k, v, alpha, beta, out, &a, varlen,
+                       draft_lens);
+  if (st != GDN_OK || num_reqs == 0) return st;
+  if (prev_draft < 1 || prev_draft > c->ring_cap) return GDN_EINVAL;
+  if (!num_accepted || !aligned(num_accepted, 4)) return GDN_EINVAL;
+  if (prev_draft_lens && !aligned(prev_draft_lens, 4)) return GDN_EINVAL;
+  const bool f32 = c->in_dtype == GDN_F32;
+  if (gdnr::fused_supported(c->d_k, c->d_v, f32, draft_len, c->ring_cap)) {
+    a.prev_accepted = num_accepted;
+    a.prev_draft_lens = prev_draft_lens;
+    a.prev_draft = prev_draft;
+    return gdnr::launch_verify_flush_fused(a, min_len, stream) == hipSuccess ? GDN_OK : GDN_EHIP;
+  }
+  // Other shapes: the rollback, then verify_flush, as separate launches.
+  st = rollback_impl(c, num_reqs, slot_idx, prev_draft, num_accepted, stream,
+                     prev_draft_lens != nullptr, prev_draft_lens);
+  if (st != GDN_OK) return st;
+  return verify_flush_impl(c, num_reqs, slot_idx, draft_len, min_len, q, k, v, alpha, beta, out,
+                           stream, varlen, draft_lens);
 }
 
 int gdn_replay_rollback(const gdn_replay_cache *c, int32_t num_reqs, const int32_t *slot_idx,

@@ -1157,10 +1157,31 @@ __device__ __forceinline__ int nth_bit(uint64_t m, int n) {
 }
 
 struct Req {
-  int r, s, head, len;
-  int due;  // number of due requests in the call
+  int r, s, head, len;  // len: committed count after the folded rollback, if any
+  int raw_len;          // len as stored
+  int due;              // number of due requests in the call
 };
 
+// Committed count of request i once the accepted prefix of the previous draft
+// is committed (the rollback folded into this call): len + a when the previous
+// length is in [0, prev_draft], a in [0, that length] and len + a <= C;
+// otherwise len, with the rollback's error bit in *bad (as a separate rollback
+// call would skip the request and flag it).
+__device__ __forceinline__ int rolled_len(const VerifyArgs &va, int i, int len, int cap,
+                                          int *bad) {
+  const int bound = va.prev_draft_lens ? va.prev_draft_lens[i] : va.prev_draft;
+  const int a = va.prev_accepted[i];
+  *bad = 0;
+  if (bound < 0 || bound > va.prev_draft)
+    *bad = GDN_DERR_DRAFT;
+  else if (a < 0 || a > bound)
+    *bad = GDN_DERR_ACCEPT;
+  else if (len + a > cap)
+    *bad = GDN_DERR_CAPACITY;
+  return *bad ? len : len + a;
+}
+
+template <bool ROLLBACK>
 __device__ Req ordered_request(const VerifyArgs &va, int mn, int q, int lane) {
   const int R = va.num_reqs;
   const CacheView &c = va.c;
@@ -1168,27 +1189,35 @@ __device__ Req ordered_request(const VerifyArgs &va, int mn, int q, int lane) {
     const int m = min(64, R - 64 * j);
     return m == 64 ? ~0ull : ((1ull << m) - 1);
   };
+  // committed count the call works from: the stored len, or len + a with the
+  // previous draft's rollback folded in (when the pointers are valid)
+  auto eff = [&](int i, int h, int n) {
+    if (!ROLLBACK || h < 0 || h >= c.cap || n < 0 || n > c.cap) return n;
+    int bad;
+    return rolled_len(va, i, n, c.cap, &bad);
+  };
   if (R <= 64) {
-    int si = -1, hi = 0, ni = 0;
+    int si = -1, hi = 0, ni = 0, ne = 0;
     if (lane < R) {
       si = va.slot_idx[lane];
       if (si >= 0 && si < c.num_slots) {
         hi = c.head[si];
         ni = c.len[si];
+        ne = eff(lane, hi, ni);
       }
     }
-    const uint64_t dm = __ballot(si >= 0 && si < c.num_slots && ni >= mn);
+    const uint64_t dm = __ballot(si >= 0 && si < c.num_slots && ne >= mn);
     const int nd = __popcll(dm);
     const int r = q < nd ? nth_bit(dm, q) : nth_bit(~dm & lanes(0), q - nd);
     return Req{r, __builtin_amdgcn_readlane(si, r), __builtin_amdgcn_readlane(hi, r),
-               __builtin_amdgcn_readlane(ni, r), nd};
+               __builtin_amdgcn_readlane(ne, r), __builtin_amdgcn_readlane(ni, r), nd};
   }
   auto due_mask = [&](int j) -> uint64_t {
     const int i = 64 * j + lane;
     bool d = false;
     if (i < R) {
       const int si = va.slot_idx[i];
-      d = si >= 0 && si < c.num_slots && c.len[si] >= mn;
+      d = si >= 0 && si < c.num_slots && eff(i, c.head[si], c.len[si]) >= mn;
     }
     return __ballot(d);
   };
@@ -1208,10 +1237,11 @@ __device__ Req ordered_request(const VerifyArgs &va, int mn, int q, int lane) {
     }
     left -= cnt;
   }
-  Req o{r, va.slot_idx[r], 0, 0, nd};
+  Req o{r, va.slot_idx[r], 0, 0, 0, nd};
   if (o.s >= 0 && o.s < c.num_slots) {
     o.head = c.head[o.s];
-    o.len = c.len[o.s];
+    o.raw_len = c.len[o.s];
+    o.len = eff(r, o.head, o.raw_len);
   }
   return o;
 }
@@ -1237,7 +1267,7 @@ __device__ Req ordered_request(const VerifyArgs &va, int mn, int q, int lane) {
 // for their fold. So each workgroup of a due slot counts itself in at
 // sync[num_slots + s HK + kh] once its fold inputs are staged, and the last
 // one of the key head's group appends k and q (the others have read by then).
-template <int DK, int DV, int NT, bool VARLEN>
+template <int DK, int DV, int NT, bool VARLEN, bool ROLLBACK>
 __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyArgs va,
                                                                          int min_len) {
   constexpr int WAVES = DV / (16 * NT);
@@ -1265,7 +1295,7 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyA
     return (uint32_t)((4 * ((t & 63) >> 4) * DV + (t / 64) * 16 * NT + NT * (t & 15)) * 4);
   };
   const int mn = max(min_len, 1);
-  const Req rq = ordered_request(va, mn, blockIdx.x / HV, lane);
+  const Req rq = ordered_request<ROLLBACK>(va, mn, blockIdx.x / HV, lane);
   const int r = rq.r, h = blockIdx.x % HV;
   const bool lead = (h == 0 && tid == 0);
   int32_t *grid_ctr = c.sync + (int64_t)c.num_slots * (1 + c.hk);
@@ -1276,7 +1306,7 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyA
   // With no due request there is nothing to move and no count is taken (every
   // workgroup sees the same count, as no pointer changes during the call).
   auto finish = [&]() {
-    if (rq.due == 0) return;
+    if (!ROLLBACK && rq.due == 0) return;  // a folded rollback moves len in any case
     __syncthreads();
     if (tid == 0) {
       int last = 0;
@@ -1291,11 +1321,21 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyA
     for (int i = tid; i < va.num_reqs; i += blockDim.x) {
       const int si = va.slot_idx[i];
       if (si < 0 || si >= c.num_slots) continue;
-      const int hs = c.head[si], ns = c.len[si];
-      if (hs < 0 || hs >= c.cap || ns < mn || ns > c.cap) continue;
-      if (VARLEN && request_draft(va.draft_lens, i, va.draft) < 0) continue;  // skipped request
-      c.head[si] = hs + ns - (hs + ns >= c.cap ? c.cap : 0);
-      c.len[si] = 0;
+      const int hs = c.head[si], n0 = c.len[si];
+      if (hs < 0 || hs >= c.cap || n0 < 0 || n0 > c.cap) continue;
+      int ns = n0;
+      if constexpr (ROLLBACK) {
+        int bad;
+        ns = rolled_len(va, i, n0, c.cap, &bad);
+      }
+      // a request with a bad draft length is not flushed (its rollback stands)
+      const bool skip = VARLEN && request_draft(va.draft_lens, i, va.draft) < 0;
+      if (ns >= mn && !skip) {
+        c.head[si] = hs + ns - (hs + ns >= c.cap ? c.cap : 0);
+        c.len[si] = 0;
+      } else if (ROLLBACK && ns != n0) {
+        c.len[si] = ns;
+      }
     }
     if (tid == 0) *grid_ctr = 0;
   };
@@ -1308,10 +1348,15 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyA
   }
   const int C = c.cap;
   const int head = rq.head, n = rq.len;
-  if (head < 0 || head >= C || n < 0 || n > C) {
+  if (head < 0 || head >= C || rq.raw_len < 0 || rq.raw_len > C) {
     if (lead) raise_err(c.err, GDN_DERR_POINTER);
     finish();
     return;
+  }
+  if (ROLLBACK && lead) {  // the folded rollback's own error, as a rollback call would flag it
+    int bad;
+    rolled_len(va, r, rq.raw_len, C, &bad);
+    if (bad) raise_err(c.err, bad);
   }
   // this request's draft length (the per-request lengths are a separate
   // instantiation, so that the fixed-length kernel carries none of their code)
@@ -1433,19 +1478,24 @@ hipError_t launch_t(const VerifyArgs &va, const FlushArgs &fa, int num_reqs, int
 hipError_t launch_verify_flush_fused(const VerifyArgs &a, int min_len, hipStream_t stream) {
   constexpr int NT = 2;
   const dim3 grid(a.num_reqs * a.c.hv);
-  const bool varlen = a.draft_lens != nullptr;
+  const bool varlen = a.draft_lens != nullptr, rollback = a.prev_accepted != nullptr;
+  auto go = [&](auto kernel, int dv) {
+    hipLaunchKernelGGL(kernel, grid, dim3(64 * (dv / (16 * NT))), 0, stream, a, min_len);
+  };
   if (a.c.dk == 128) {
-    const dim3 block(64 * (128 / (16 * NT)));
-    if (varlen)
-      hipLaunchKernelGGL((replay_fused<128, 128, NT, true>), grid, block, 0, stream, a, min_len);
+    if (rollback)
+      varlen ? go(replay_fused<128, 128, NT, true, true>, 128)
+             : go(replay_fused<128, 128, NT, false, true>, 128);
     else
-      hipLaunchKernelGGL((replay_fused<128, 128, NT, false>), grid, block, 0, stream, a, min_len);
+      varlen ? go(replay_fused<128, 128, NT, true, false>, 128)
+             : go(replay_fused<128, 128, NT, false, false>, 128);
   } else if (a.c.dk == 64) {
-    const dim3 block(64 * (64 / (16 * NT)));
-    if (varlen)
-      hipLaunchKernelGGL((replay_fused<64, 64, NT, true>), grid, block, 0, stream, a, min_len);
+    if (rollback)
+      varlen ? go(replay_fused<64, 64, NT, true, true>, 64)
+             : go(replay_fused<64, 64, NT, false, true>, 64);
     else
-      hipLaunchKernelGGL((replay_fused<64, 64, NT, false>), grid, block, 0, stream, a, min_len);
+      varlen ? go(replay_fused<64, 64, NT, true, false>, 64)
+             : go(replay_fused<64, 64, NT, false, false>, 64);
   } else {
     return hipErrorInvalidValue;
   }

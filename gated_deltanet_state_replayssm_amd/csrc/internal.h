@@ -21,6 +21,12 @@ struct VerifyArgs {
   int32_t num_reqs, draft;       // draft: D, or D_max with per-request lengths
   const int32_t *slot_idx;
   const int32_t *draft_lens;     // per-request lengths in [0, draft], or null
+  // rollback of the previous draft folded into this call (verify_flush only):
+  // accepted counts (null: none), the previous draft's length or per-request
+  // lengths (null: prev_draft for every request)
+  const int32_t *prev_accepted;
+  const int32_t *prev_draft_lens;
+  int32_t prev_draft;
   const void *q, *k, *v;
   const float *alpha, *beta;
   float *out;
@@ -53,6 +59,7 @@ hipError_t launch_flush_chunked(const FlushArgs &a, hipStream_t stream);
 // needs sync sized [num_slots * (1 + HK) + 1].
 bool fused_supported(int dk, int dv, bool in_f32, int draft, int cap);
 hipError_t launch_verify_flush_fused(const VerifyArgs &a, int min_len, hipStream_t stream);
+// (a.prev_accepted non-null: the previous draft's rollback first, in the same kernel)
 // Token-by-token fp32 kernels (every built shape, bf16 or fp32 inputs):
 hipError_t launch_verify_recurrent(const VerifyArgs &a, bool in_f32, hipStream_t stream);
 hipError_t launch_flush_recurrent(const FlushArgs &a, bool in_f32, hipStream_t stream);

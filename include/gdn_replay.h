@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define GDN_REPLAY_VERSION 3
+#define GDN_REPLAY_VERSION 4
 
 typedef enum {
   GDN_OK = 0,
@@ -222,6 +222,41 @@ int gdn_replay_verify_flush_varlen(const gdn_replay_cache *c, int32_t num_reqs,
 int gdn_replay_rollback_varlen(const gdn_replay_cache *c, int32_t num_reqs,
                                const int32_t *slot_idx, const int32_t *draft_lens,
                                int32_t max_draft, const int32_t *num_accepted, hipStream_t stream);
+
+/*
+ * gdn_replay_rollback_verify_flush — the whole step of a layer in one call: the
+ * rollback of the previous draft (pointer only, "Making speculative
+ * verification cheaper"), then verify_flush of this step's draft. Its result
+ * (out, state, ring, head, len, err) is exactly that of
+ *     gdn_replay_rollback[_varlen](slot_idx, prev_draft[_lens], num_accepted)
+ *     gdn_replay_verify_flush[_varlen](slot_idx, draft_len[s], min_len, ...)
+ * on the same requests. Request i therefore both commits num_accepted[i]
+ * tokens of the draft it appended in the previous step and verifies its new
+ * draft; a request new to the batch passes num_accepted[i] = 0. With the
+ * rollback folded in, the pointer moves of both calls are made once, by the
+ * last workgroup of the kernel, and a due slot is flushed together with the
+ * tokens it has just accepted.
+ *
+ *   num_accepted    [num_reqs] int32 (device).
+ *   prev_draft_lens [num_reqs] int32 (device) lengths of the previous drafts,
+ *                   or NULL: every previous draft had prev_draft tokens.
+ *   prev_draft      1..C (host): the previous drafts' (maximum) length.
+ *   draft_lens      [num_reqs] int32 (device) lengths of this step's drafts,
+ *                   or NULL: every draft has draft_len tokens.
+ *   draft_len       1..C (host): this step's (maximum) draft length.
+ *   other arguments as for gdn_replay_verify_flush.
+ * Device errors: those of the two calls. A request whose rollback fails (DRAFT
+ * for a previous length out of range, ACCEPT, CAPACITY) keeps its len, as the
+ * rollback call would leave it, and goes on to verify_flush. Shapes the fused
+ * kernel does not take run the two calls back to back on the stream.
+ */
+int gdn_replay_rollback_verify_flush(const gdn_replay_cache *c, int32_t num_reqs,
+                                     const int32_t *slot_idx, const int32_t *num_accepted,
+                                     const int32_t *prev_draft_lens, int32_t prev_draft,
+                                     const int32_t *draft_lens, int32_t draft_len,
+                                     int32_t min_len, const void *q, const void *k, const void *v,
+                                     const float *alpha, const float *beta, float *out,
+                                     hipStream_t stream);
 
 /*
  * gdn_gated_rmsnorm_fp8 — the step after the recurrence: gated RMSNorm of the

@@ -145,6 +145,34 @@ class Pair:
         self._check_flushed(host, before, slot_idx, sel, min_len, len_before)
         return out
 
+    def rollback_verify_flush(self, slot_idx, acc, prev_draft, min_len, dr, label="",
+                              prev_lens=None, lens=None):
+        """The one-call step; the oracle side is its rollback, then its
+        verify_flush, on the same requests."""
+        say(f"  rollback_verify_flush {label} R={len(slot_idx)} D={dr['alpha'].shape[1]} "
+            f"prev={prev_draft} min_len={min_len} acc={list(acc)[:8]}"
+            + ("" if lens is None else f" lens={list(lens)[:8]}")
+            + ("" if prev_lens is None else f" prev_lens={list(prev_lens)[:8]}"))
+        before = self.gpu.state.cpu().numpy()
+        dev = {k: to_device(v) for k, v in dr.items()}
+        out = self.gpu.rollback_verify_flush(
+            to_device(slot_idx), to_device(np.asarray(acc, np.int32)), prev_draft, min_len,
+            dev["q"], dev["k"], dev["v"], dev["alpha"], dev["beta"], out=self._out_buffer(dr),
+            prev_draft_lens=self._lens_dev(prev_lens), draft_lens=self._lens_dev(lens))
+        torch.cuda.synchronize()
+        sel = self._sel(slot_idx)
+        self.orc.rollback(slot_idx[sel], prev_draft, np.asarray(acc)[sel],
+                          draft_lens=None if prev_lens is None else np.asarray(prev_lens)[sel])
+        len_before = self.orc.len.copy()
+        ref = self.orc.verify_flush(slot_idx[sel], min_len,
+                                    *(dr[x][sel] for x in ("q", "k", "v", "alpha", "beta")),
+                                    draft_lens=None if lens is None else np.asarray(lens)[sel])
+        self._check_out(out.cpu().numpy()[sel], ref, "rollback_verify_flush")
+        host = self.gpu.to_numpy()
+        self._check_common(host)
+        self._check_flushed(host, before, slot_idx, sel, min_len, len_before)
+        return out
+
     def rollback(self, slot_idx, draft_len, acc, label="", lens=None):
         say(f"  rollback {label}")
         before = self.gpu.state.clone()
@@ -171,24 +199,51 @@ class Pair:
 
 
 def run_schedule(wl: synth.Workload, steps: int, seed: int, layers: int = 1, with_q=True,
-                 oracle_slots=None, label="", fused=False):
+                 oracle_slots=None, label="", fused=False, one_call=False):
     """verify -> rollback -> flush for `steps` steps over `layers` independent caches
-    (fused: verify_flush -> rollback, the flush folded into the next verify)."""
+    (fused: verify_flush -> rollback, the flush folded into the next verify;
+    one_call: rollback_verify_flush, the previous step's rollback folded in too).
+
+    With one_call a request carries the accepted count of the draft it appended
+    in the previous step; a slot that had a draft and is not in this step's
+    batch gets a rollback call of its own first, a slot new to the batch
+    passes 0."""
     rng = np.random.default_rng(seed)
     pairs = []
     for L in range(layers):
         init = synth.make_cache_init(wl, rng)
         pairs.append(Pair(wl, init, with_q=with_q, oracle_slots=oracle_slots))
+    pending = {}   # slot -> (accepted, that draft's length), one_call only
     for step in range(steps):
         slots = synth.make_slot_idx(wl, rng)
         lens = synth.sample_draft_lens(wl, rng)   # None: every request drafts wl.draft
         acc = synth.sample_accepted(wl, rng, draft_lens=lens)
+        if one_call:
+            gone = np.array([s for s in pending if s not in set(int(x) for x in slots)], np.int32)
+            if len(gone):
+                ga = np.array([pending[int(s)][0] for s in gone], np.int32)
+                gl = np.array([pending[int(s)][1] for s in gone], np.int32)
+                for L, p in enumerate(pairs):
+                    p.rollback(gone, wl.draft, ga, f"{label} L{L} step{step} gone", lens=gl)
+            pa = np.array([pending.get(int(s), (0, 0))[0] for s in slots], np.int32)
+            pl = np.array([pending.get(int(s), (0, 0))[1] for s in slots], np.int32)
+            # fixed previous length when every request had one (and this is not the first step)
+            prev_lens = None if (lens is None and step > 0 and
+                                 all(int(s) in pending for s in slots)) else pl
         for L, p in enumerate(pairs):
             dr = synth.make_draft(wl, rng)
-            if fused:
-                p.verify_flush(slots, wl.flush_min_len, dr, f"{label} L{L} step{step}", lens=lens)
+            tag = f"{label} L{L} step{step}"
+            if one_call:
+                p.rollback_verify_flush(slots, pa, wl.draft, wl.flush_min_len, dr, tag,
+                                        prev_lens=prev_lens, lens=lens)
+            elif fused:
+                p.verify_flush(slots, wl.flush_min_len, dr, tag, lens=lens)
             else:
-                p.verify(slots, dr, f"{label} L{L} step{step}", lens=lens)
+                p.verify(slots, dr, tag, lens=lens)
+        if one_call:
+            pending = {int(s): (int(acc[i]), wl.draft if lens is None else int(lens[i]))
+                       for i, s in enumerate(slots)}
+            continue
         for L, p in enumerate(pairs):
             p.rollback(slots, wl.draft, acc, f"{label} L{L} step{step}", lens=lens)
         if not fused:

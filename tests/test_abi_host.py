@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert b.version() == 3
+    assert b.version() == 4
     for st in (b.GDN_OK, b.GDN_EINVAL, b.GDN_EUNSUPPORTED, b.GDN_EHIP):
         assert b.load().gdn_replay_strerror(st)
     assert b.load().gdn_replay_strerror(12345) == b"unknown status"
@@ -151,6 +151,36 @@ def test_varlen_call_validation():
     lib = b.load()
     assert lib.gdn_replay_verify_varlen(None, 1, FAKE, FAKE, 1, FAKE, FAKE, FAKE, FAKE, FAKE,
                                         FAKE, None) == b.GDN_EINVAL
+
+
+def _step(c, num_reqs=2, acc=FAKE, plens=None, pdraft=4, lens=None, draft=4, **ptrs):
+    p = dict(slot=FAKE, q=FAKE, k=FAKE, v=FAKE, a=FAKE, be=FAKE, out=FAKE)
+    p.update(ptrs)
+    return b.rollback_verify_flush_raw(c, num_reqs, p["slot"], acc, plens, pdraft, lens, draft, 1,
+                                       p["q"], p["k"], p["v"], p["a"], p["be"], p["out"], None)
+
+
+def test_step_call_validation():
+    """The one-call step checks what both of its calls check: the accepted
+    counts are required, the previous (maximum) length is in 1..C, optional
+    length arrays are 4-byte aligned; nothing is launched on a bad argument."""
+    c = _cache()
+    assert _step(c, acc=None) == b.GDN_EINVAL
+    assert _step(c, acc=FAKE + 2) == b.GDN_EINVAL
+    assert _step(c, pdraft=0) == b.GDN_EINVAL
+    assert _step(c, pdraft=9) == b.GDN_EINVAL             # previous draft > C
+    assert _step(c, plens=FAKE + 1) == b.GDN_EINVAL
+    assert _step(c, lens=FAKE + 2) == b.GDN_EINVAL
+    assert _step(c, draft=0) == b.GDN_EINVAL
+    assert _step(c, draft=9) == b.GDN_EINVAL
+    assert _step(c, num_reqs=5) == b.GDN_EINVAL
+    assert _step(c, k=None) == b.GDN_EINVAL
+    assert _step(c, out=FAKE + 4) == b.GDN_EINVAL
+    assert _step(_cache(d_k=48, d_v=48)) == b.GDN_EUNSUPPORTED
+    assert _step(c, num_reqs=0, acc=None, q=None) == b.GDN_OK
+    assert b.load().gdn_replay_rollback_verify_flush(None, 1, FAKE, FAKE, None, 4, None, 4, 1,
+                                                     FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                                     None) == b.GDN_EINVAL
 
 
 def test_norm_call_validation():

@@ -20,7 +20,7 @@ GDN_DERR_DRAFT = 16
 EXPORTED = ("gdn_replay_verify", "gdn_replay_rollback", "gdn_replay_flush",
             "gdn_replay_verify_flush", "gdn_replay_verify_varlen",
             "gdn_replay_verify_flush_varlen", "gdn_replay_rollback_varlen",
-            "gdn_replay_rollback_verify_flush",
+            "gdn_replay_rollback_verify_flush", "gdn_replay_sync_entries",
             "gdn_gated_rmsnorm_fp8", "gdn_causal_conv_update", "gdn_replay_strerror",
             "gdn_replay_version")
 
@@ -86,6 +86,8 @@ def load(path: str = LIB_PATH):
     lib.gdn_replay_rollback_verify_flush.argtypes = [P, I32, VP, VP, VP, I32, VP, I32, I32, VP,
                                                      VP, VP, VP, VP, VP, VP]
     lib.gdn_replay_rollback_verify_flush.restype = ctypes.c_int
+    lib.gdn_replay_sync_entries.argtypes = [I32, I32]
+    lib.gdn_replay_sync_entries.restype = ctypes.c_int64
     lib.gdn_gated_rmsnorm_fp8.argtypes = [I32, I32, I32, VP, VP, VP, ctypes.c_float, VP, VP, VP]
     lib.gdn_gated_rmsnorm_fp8.restype = ctypes.c_int
     lib.gdn_causal_conv_update.argtypes = [P, VP, I32, I32, I32, VP, I32, VP, VP, VP, VP, VP]
@@ -231,6 +233,11 @@ def causal_conv_update(cache, conv_ring, channels, width, num_reqs, slot_idx, dr
     _check("gdn_causal_conv_update",
            causal_conv_update_raw(cache, conv_ring, channels, width, num_reqs, slot_idx, draft_len,
                                   x, weight, bias, y, stream))
+
+
+def sync_entries(num_slots: int, num_k_heads: int) -> int:
+    """Entries of the cache's int32 arrival-counter buffer."""
+    return int(load().gdn_replay_sync_entries(num_slots, num_k_heads))
 
 
 def version() -> int:

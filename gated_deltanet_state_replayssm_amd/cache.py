@@ -76,7 +76,7 @@ class ReplayCache:
         self.head = z((num_slots,), torch.int32)
         self.len = z((num_slots,), torch.int32)
         # slot counters, then the per-(slot, key head) and grid counters of verify_flush
-        self.sync = z((num_slots * (1 + hk) + 1,), torch.int32)
+        self.sync = z((binding.sync_entries(num_slots, hk),), torch.int32)
         self.err = z((1,), torch.int32)
         self._struct = None
 

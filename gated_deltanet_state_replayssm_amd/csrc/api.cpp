@@ -314,6 +314,11 @@ int gdn_causal_conv_update(const gdn_replay_cache *c, void *conv_ring, int32_t c
   return gdnr::launch_causal_conv_update(a, width, stream) == hipSuccess ? GDN_OK : GDN_EHIP;
 }
 
+int64_t gdn_replay_sync_entries(int32_t num_slots, int32_t num_k_heads) {
+  if (num_slots < 0 || num_k_heads < 0) return 0;
+  return gdnr::sync_entries(num_slots, num_k_heads);
+}
+
 const char *gdn_replay_strerror(int status) {
   switch (status) {
     case GDN_OK: return "ok";

@@ -1017,11 +1017,11 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_chunked(Verif
     // (an agent-scope fence would write back this XCD's whole L2).
     __syncthreads();
     if (tid == 0) {
-      const int prev = atomicAdd(&c.sync[s], 1);
+      const int prev = atomicAdd(slot_counter(c, s), 1);
       if (prev == HV - 1) {
         c.head[s] = (head + n) % C;
         c.len[s] = 0;
-        c.sync[s] = 0;
+        *slot_counter(c, s) = 0;
       }
     }
   }
@@ -1131,11 +1131,11 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_single(Verify
     // (an agent-scope fence would write back this XCD's whole L2).
     __syncthreads();
     if (tid == 0) {
-      const int prev = atomicAdd(&c.sync[s], 1);
+      const int prev = atomicAdd(slot_counter(c, s), 1);
       if (prev == HV - 1) {
         c.head[s] = (head + n) % C;
         c.len[s] = 0;
-        c.sync[s] = 0;
+        *slot_counter(c, s) = 0;
       }
     }
   }
@@ -1181,8 +1181,20 @@ __device__ __forceinline__ int rolled_len(const VerifyArgs &va, int i, int len, 
   return *bad ? len : len + a;
 }
 
-template <bool ROLLBACK>
-__device__ Req ordered_request(const VerifyArgs &va, int mn, int q, int lane) {
+// The pointer move of one request at the end of the call: slot (-1: none), new
+// head (-1: unchanged) and new len.
+struct Move {
+  int slot, head, len;
+};
+
+// With at most 64 requests, the lanes of the ordering pass hold every
+// request's slot and pointers; wave 0 also works out each request's pointer
+// move from them (exactly as the end-of-grid loop below would) and leaves it in
+// moves[], so that the last workgroup only stores. The values are those at the
+// start of the call, which is what the end-of-grid loop reads too: no pointer
+// changes before the last workgroup.
+template <bool ROLLBACK, bool VARLEN>
+__device__ Req ordered_request(const VerifyArgs &va, int mn, int q, int lane, Move *moves) {
   const int R = va.num_reqs;
   const CacheView &c = va.c;
   auto lanes = [&](int j) -> uint64_t {
@@ -1207,6 +1219,18 @@ __device__ Req ordered_request(const VerifyArgs &va, int mn, int q, int lane) {
       }
     }
     const uint64_t dm = __ballot(si >= 0 && si < c.num_slots && ne >= mn);
+    if (moves && lane < R) {
+      Move mv{-1, -1, 0};
+      if (si >= 0 && si < c.num_slots && hi >= 0 && hi < c.cap && ni >= 0 && ni <= c.cap) {
+        // a request with a bad draft length is not flushed (a folded rollback stands)
+        const bool skip = VARLEN && request_draft(va.draft_lens, lane, va.draft) < 0;
+        if (ne >= mn && !skip)
+          mv = Move{si, hi + ne - (hi + ne >= c.cap ? c.cap : 0), 0};
+        else if (ROLLBACK && ne != ni)
+          mv = Move{si, -1, ne};
+      }
+      moves[lane] = mv;
+    }
     const int nd = __popcll(dm);
     const int r = q < nd ? nth_bit(dm, q) : nth_bit(~dm & lanes(0), q - nd);
     return Req{r, __builtin_amdgcn_readlane(si, r), __builtin_amdgcn_readlane(hi, r),
@@ -1259,13 +1283,13 @@ __device__ Req ordered_request(const VerifyArgs &va, int mn, int q, int lane) {
 // the pointers of the due slots (head += len, len = 0) are moved by the last
 // workgroup of the grid to finish. It is found in two levels, so that no
 // counter sees more than one arrival per workgroup of a request group: the
-// HV workgroups of request rank q count in at sync[q], the last of them at
-// sync[num_slots * (1 + HK)].
+// HV workgroups of request rank q count in at that rank's counter (a 128-byte
+// line of its own), the last of them at the grid counter.
 //
 // The draft is appended at (new head + j) mod C, which may wrap onto committed
 // key rows that the other value heads of the same key head are still reading
-// for their fold. So each workgroup of a due slot counts itself in at
-// sync[num_slots + s HK + kh] once its fold inputs are staged, and the last
+// for their fold. So each workgroup of a due slot counts itself in at the
+// (slot, key head) counter once its fold inputs are staged, and the last
 // one of the key head's group appends k and q (the others have read by then).
 template <int DK, int DV, int NT, bool VARLEN, bool ROLLBACK>
 __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyArgs va,
@@ -1276,6 +1300,7 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyA
   typedef typename Cols<NT>::F F;
   __shared__ Smem<DK, DV> sm;
   __shared__ int group_rank, grid_rank;
+  __shared__ Move moves[64];
 
   const CacheView &c = va.c;
   const int HV = c.hv, G = HV / c.hk;
@@ -1295,11 +1320,12 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyA
     return (uint32_t)((4 * ((t & 63) >> 4) * DV + (t / 64) * 16 * NT + NT * (t & 15)) * 4);
   };
   const int mn = max(min_len, 1);
-  const Req rq = ordered_request<ROLLBACK>(va, mn, blockIdx.x / HV, lane);
+  const Req rq = ordered_request<ROLLBACK, VARLEN>(va, mn, blockIdx.x / HV, lane,
+                                                  wave == 0 ? moves : nullptr);
   const int r = rq.r, h = blockIdx.x % HV;
   const bool lead = (h == 0 && tid == 0);
-  int32_t *grid_ctr = c.sync + (int64_t)c.num_slots * (1 + c.hk);
-  int32_t *rank_ctr = c.sync + blockIdx.x / HV;
+  int32_t *grid_ctr = c.sync;
+  int32_t *rank_ctr = slot_counter(c, blockIdx.x / HV);
 
   // Every workgroup counts itself in at its end (after a barrier, so that all
   // its waves have read the pointers); the last one moves the due slots' pointers.
@@ -1318,6 +1344,17 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyA
     }
     __syncthreads();
     if (!grid_rank) return;
+    if (va.num_reqs <= 64) {  // moves worked out by the ordering pass
+      if (tid < va.num_reqs) {
+        const Move mv = moves[tid];
+        if (mv.slot >= 0) {
+          if (mv.head >= 0) c.head[mv.slot] = mv.head;
+          c.len[mv.slot] = mv.len;
+        }
+      }
+      if (tid == 0) *grid_ctr = 0;
+      return;
+    }
     for (int i = tid; i < va.num_reqs; i += blockDim.x) {
       const int si = va.slot_idx[i];
       if (si < 0 || si >= c.num_slots) continue;
@@ -1374,7 +1411,7 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyA
   }
   const int kh = h / G;
   const Rsrc st = make_rsrc(c.state + ((int64_t)s * HV + h) * DK * DV, DK * DV * 4);
-  int32_t *group_ctr = c.sync + c.num_slots + (int64_t)s * c.hk + kh;
+  int32_t *group_ctr = group_counter(c, s, kh);
 
   // Waves SW.. issue their state loads first; waves 0..SW-1 stage the inputs of
   // the first replay, then load their state columns (loads complete in issue

@@ -16,6 +16,25 @@ struct CacheView {
   int32_t *head, *len, *sync, *err;
 };
 
+// Arrival counters in CacheView::sync (int32, zero between calls): [0] the
+// grid counter, [kSyncStride * (1 + i)] the counter of slot i (flush) or of the
+// i-th request in the fused kernel's order, each on a 128-byte line of its own
+// (atomics on one line are served one after another), then the per-(slot, key
+// head) counters at [kSyncStride * (1 + num_slots) + s * HK + kh].
+constexpr int kSyncStride = 32;
+
+__host__ __device__ inline int64_t sync_entries(int num_slots, int hk) {
+  return (int64_t)kSyncStride * (num_slots + 1) + (int64_t)num_slots * hk;
+}
+
+__device__ inline int32_t *slot_counter(const CacheView &c, int i) {
+  return c.sync + (int64_t)kSyncStride * (1 + i);
+}
+
+__device__ inline int32_t *group_counter(const CacheView &c, int s, int kh) {
+  return c.sync + (int64_t)kSyncStride * (1 + c.num_slots) + (int64_t)s * c.hk + kh;
+}
+
 struct VerifyArgs {
   CacheView c;
   int32_t num_reqs, draft;       // draft: D, or D_max with per-request lengths
@@ -55,8 +74,7 @@ struct FlushArgs {
 bool chunked_supported(int dk, int dv, bool in_f32, int draft);
 hipError_t launch_verify_chunked(const VerifyArgs &a, hipStream_t stream);
 hipError_t launch_flush_chunked(const FlushArgs &a, hipStream_t stream);
-// Flush fused into verify in one kernel (chunked shapes, ring capacity <= 32);
-// needs sync sized [num_slots * (1 + HK) + 1].
+// Flush fused into verify in one kernel (chunked shapes, ring capacity <= 32).
 bool fused_supported(int dk, int dv, bool in_f32, int draft, int cap);
 hipError_t launch_verify_flush_fused(const VerifyArgs &a, int min_len, hipStream_t stream);
 // (a.prev_accepted non-null: the previous draft's rollback first, in the same kernel)

@@ -175,11 +175,11 @@ __global__ __launch_bounds__(kLanes) void flush_recurrent(FlushArgs a) {
   __syncthreads();
   if (lane == 0) {
     const int total = HV * (int)gridDim.z;
-    const int prev = atomicAdd(&c.sync[s], 1);
+    const int prev = atomicAdd(slot_counter(c, s), 1);
     if (prev == total - 1) {
       c.head[s] = (head + n) % C;
       c.len[s] = 0;
-      c.sync[s] = 0;
+      *slot_counter(c, s) = 0;
     }
   }
 }

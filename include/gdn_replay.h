@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define GDN_REPLAY_VERSION 4
+#define GDN_REPLAY_VERSION 5
 
 typedef enum {
   GDN_OK = 0,
@@ -80,12 +80,14 @@ enum {
  *   len        [num_slots] int32: committed tokens not yet in the checkpoint.
  *              The committed tokens sit at (head + t) mod C, t < len.
  *   sync       int32 arrival counters, zero when created; every completed call
- *              leaves them zero. sync[s] (s < num_slots) lets flush move the
- *              pointers after every workgroup of slot s has read them. Calls of
- *              gdn_replay_verify_flush also use sync[num_slots + s * HK + kh]
- *              and sync[num_slots * (1 + HK)], so give it
- *              num_slots * (1 + HK) + 1 entries if that call is used, num_slots
- *              entries otherwise.
+ *              leaves them zero. They let the last workgroup of a slot (flush)
+ *              or of the grid (verify_flush) move the pointers once every
+ *              workgroup has read them. gdn_replay_sync_entries(num_slots, HK)
+ *              entries (32 * (num_slots + 1) + num_slots * HK: the counters that
+ *              many workgroups hit sit 128 bytes apart, since atomics on one
+ *              cache line are served one after another); 128-byte alignment
+ *              keeps each on a line of its own. The library cannot check the
+ *              size of this buffer: a smaller one is written out of bounds.
  *   err        [1] int32 sticky error word, or NULL to drop device errors.
  *
  * Value head h reads key head h / (HV / HK) (consecutive grouping, HV % HK == 0).
@@ -178,10 +180,9 @@ int gdn_replay_flush(const gdn_replay_cache *c, int32_t num_reqs, const int32_t 
  * len[s] committed tokens into state[s], head[s] = (head[s] + len[s]) mod C and
  * len[s] = 0 (exactly as gdn_replay_flush); then verify the draft exactly as
  * gdn_replay_verify, from the resulting checkpoint, pointers and ring. Arguments
- * as for gdn_replay_verify plus min_len; sync must hold num_slots * (1 + HK) + 1
- * counters (see gdn_replay_cache). Ring capacity <= 32 with bf16 inputs and
- * d_k = d_v in {64, 128} runs as one kernel; other shapes run the two calls back
- * to back on the stream.
+ * as for gdn_replay_verify plus min_len. Ring capacity <= 32 with bf16 inputs
+ * and d_k = d_v in {64, 128} runs as one kernel; other shapes run the two calls
+ * back to back on the stream.
  * Device errors: slot out of range -> SLOT; head or len out of range -> POINTER;
  * a slot that is not due with len + D > C -> CAPACITY. The request is skipped
  * with no writes at all (no flush either).
@@ -322,6 +323,10 @@ int gdn_causal_conv_update(const gdn_replay_cache *c, void *conv_ring, int32_t c
 
 /* Human-readable text of a gdn_status (static storage). */
 const char *gdn_replay_strerror(int status);
+
+/* Number of int32 entries of gdn_replay_cache::sync for num_slots slots and
+ * num_k_heads key heads (0 for a negative argument). */
+int64_t gdn_replay_sync_entries(int32_t num_slots, int32_t num_k_heads);
 
 /* GDN_REPLAY_VERSION of the built library. */
 int gdn_replay_version(void);

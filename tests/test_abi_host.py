@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert b.version() == 4
+    assert b.version() == 5
     for st in (b.GDN_OK, b.GDN_EINVAL, b.GDN_EUNSUPPORTED, b.GDN_EHIP):
         assert b.load().gdn_replay_strerror(st)
     assert b.load().gdn_replay_strerror(12345) == b"unknown status"

@@ -9,7 +9,11 @@ are timed, each on its own caches built from the same seeded inputs:
             verify of the next step), then rollback on all layers;
   separate  verify on all layers, rollback on all layers, flush on all layers;
   step      rollback_verify_flush on all layers: one call per layer and step,
-            the previous step's rollback and the flush folded into the verify.
+            the previous step's rollback and the flush folded into the verify;
+  step_norm gdn_replay_step_norm_fp8 on all layers: the step with the gated
+            RMSNorm + FP8 of its outputs in the same kernel (codes and scales
+            only: the fp32 outputs are not stored), against the step followed
+            by the separate norm kernel.
 
 Each layer has its own cache (state + ring + pointers), so the 24 states (1.5 GiB
 at 32 requests) do not fit in the 256 MB Infinity Cache and every call streams
@@ -24,7 +28,7 @@ model below, evaluated with the actual buffer lengths of every call (tracked on
 the host from the known schedule).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
-                    [--path all|fused|separate|step]
+                    [--path all|fused|separate|step|step_norm]
     python bench.py --sweep [--steps K] [--warmup W]   (replay cost vs buffer length)
 """
 from __future__ import annotations
@@ -334,7 +338,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="r32_hv32_hk16_d128_f16")
     ap.add_argument("--layers", type=int, default=None)
-    ap.add_argument("--path", choices=("all", "fused", "separate", "step"), default="all")
+    ap.add_argument("--path", choices=("all", "fused", "separate", "step", "step_norm"),
+                    default="all")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the step benchmark: verify at fixed committed-buffer "
@@ -364,7 +369,7 @@ def main():
     wl = synth.WORKLOADS[args.workload]
     layers = args.layers or wl.layers
     stream = torch.cuda.current_stream()
-    paths = ("fused", "separate", "step") if args.path == "all" else (args.path,)
+    paths = (("fused", "separate", "step", "step_norm") if args.path == "all" else (args.path,))
 
     inits = []
     for L in range(layers):
@@ -402,7 +407,7 @@ def main():
         p_len = np.zeros(wl.num_slots, np.int32)
         for slots, acc, dl in steps:
             extra = {}
-            if path == "step":
+            if path in ("step", "step_norm"):
                 pa, pl = p_acc[slots].copy(), p_len[slots].copy()
                 extra = dict(pacc=to_device(pa), plens=None if dl is None else to_device(pl))
                 lens[slots] += pa
@@ -411,7 +416,7 @@ def main():
                 p_acc[slots] = acc
                 p_len[slots] = wl.draft if dl is None else dl
             lv = lens[slots].copy()
-            if path in ("fused", "step"):
+            if path in ("fused", "step", "step_norm"):
                 due = lv >= F
                 folded = lv[due].copy()
                 lens[slots] = np.where(due, 0, lv) + acc
@@ -420,7 +425,7 @@ def main():
                 due = lens[slots] >= F
                 folded = lens[slots][due].copy()
                 lens[slots[due]] = 0
-            if path == "step":
+            if path in ("step", "step_norm"):
                 lens[slots] = np.where(due, 0, lv)
             sched.append(dict(slots=to_device(slots), acc=to_device(acc), lv=lv, folded=folded,
                               dl=None if dl is None else to_device(dl), drafts=dl, **extra))
@@ -436,6 +441,19 @@ def main():
         dptr = [[tuple(d[x].data_ptr() for x in ("q", "k", "v", "alpha", "beta")) for d in ds]
                 for ds in drafts]
         R, D, FM, outp = wl.num_reqs, wl.draft, wl.flush_min_len, out.data_ptr()
+        norms = []
+        if path == "step_norm":   # per-layer gate, codes and scales; one weight
+            g = torch.Generator(device="cuda").manual_seed(synth.seed_for(wl.name, 0, 94))
+            w = torch.rand(wl.dv, device="cuda", generator=g) + 0.5
+            for L in range(layers):
+                z = torch.randn((R, D, wl.hv, wl.dv), device="cuda",
+                                generator=g).to(torch.bfloat16)
+                q8 = torch.empty((R, D, wl.hv, wl.dv), dtype=torch.uint8, device="cuda")
+                sc = torch.empty((R, D, wl.hv), dtype=torch.float32, device="cuda")
+                st = binding.GdnNormFp8(z.data_ptr(), w.data_ptr(), 1e-6, q8.data_ptr(),
+                                        sc.data_ptr())
+                norms.append((z, q8, sc, st, ctypes.byref(st)))
+            norms.append(w)
 
         def prepared(step):
             sc = sched[step]
@@ -452,11 +470,15 @@ def main():
                     main.append((lib.gdn_replay_rollback_verify_flush,
                                  (refs[L], R, sl, ptr(sc["pacc"]), ptr(sc["plens"]), D, dl, D,
                                   FM) + dp))
+                elif path == "step_norm":
+                    main.append((lib.gdn_replay_step_norm_fp8,
+                                 (refs[L], R, sl, ptr(sc["pacc"]), ptr(sc["plens"]), D, dl, D,
+                                  FM) + dptr[L][step % 2] + (None, norms[L][4], sh)))
                 else:
                     main.append((lib.gdn_replay_verify, (refs[L], R, sl, D) + dp)
                                 if dl is None else
                                 (lib.gdn_replay_verify_varlen, (refs[L], R, sl, dl, D) + dp))
-                if path != "step":
+                if path not in ("step", "step_norm"):
                     rb.append((lib.gdn_replay_rollback, (refs[L], R, sl, D, ptr(sc["acc"]), sh))
                               if dl is None else
                               (lib.gdn_replay_rollback_varlen,
@@ -498,14 +520,18 @@ def main():
             tr += e[1].elapsed_time(e[2])
             tf += e[2].elapsed_time(e[3])
             sc = sched[step]
-            if path in ("fused", "step"):
+            if path in ("fused", "step", "step_norm"):
                 b_v, b_f = byte_model_fused(wl, sc["lv"], sc["folded"], sc["drafts"]), 0
+                if path == "step_norm":   # no fp32 outputs; gate read, codes + scales written
+                    nd = wl.num_reqs * wl.draft if sc["drafts"] is None else int(sc["drafts"].sum())
+                    b_v += nd * wl.hv * (wl.dv * (2 + 1 - 4) + 4) + wl.dv * 4
             else:
                 b_v, b_f = byte_model(wl, sc["lv"], sc["folded"], sc["drafts"])
             vb += b_v * layers          # every layer sees the same lengths
             fb += b_f * layers
         graph_ms = graph_leg(caches, sched, path) if path in ("fused", "step") else None
         assert not any(status), f"{path}: call status {sorted(set(status))}"
+        del norms
         errs = [int(c.err.item()) for c in caches]
         assert not any(errs), f"{path}: device error bits set: {errs}"
         del caches
@@ -577,7 +603,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    order = next(p for p in ("fused", "separate", "step") if p in res)
+    order = next(p for p in ("fused", "separate", "step", "step_norm") if p in res)
     head = res[order]
     kernels = {}
     if "fused" in res:
@@ -585,6 +611,10 @@ def main():
         kernels["verify_flush"] = {"us": round(f["us_verify"], 2), "bytes": int(f["v_bytes"]),
                                    "gbps": round(f["v_gbps"], 1)}
         kernels["rollback_fused_order"] = {"us": round(f["us_rollback"], 2)}
+    if "step_norm" in res:
+        sn = res["step_norm"]
+        kernels["step_norm_fp8"] = {"us": round(sn["us_verify"], 2), "bytes": int(sn["v_bytes"]),
+                                    "gbps": round(sn["v_gbps"], 1)}
     if "step" in res:
         st = res["step"]
         kernels["rollback_verify_flush"] = {"us": round(st["us_verify"], 2),
@@ -601,8 +631,10 @@ def main():
         dominant = "verify_flush"
     elif order == "separate":
         dominant = "verify" if kernels["verify"]["us"] >= kernels["flush"]["us"] else "flush"
-    else:
+    elif order == "step":
         dominant = "rollback_verify_flush"
+    else:
+        dominant = "step_norm_fp8"
     dom = kernels[dominant]
     line = {
         "metric": METRIC,
@@ -652,6 +684,13 @@ def main():
                                  "graph_ms_per_step": round(st["graph_ms"], 4),
                                  "what": "rollback_verify_flush on every layer: the previous "
                                          "step's rollback and the flush folded into the verify"}
+    if "step_norm" in res and "step" in res:
+        line["step_with_norm"] = {
+            "fused_us_per_layer": round(res["step_norm"]["us_layer"], 2),
+            "separate_us_per_layer": round(res["step"]["us_layer"] + kernels["gated_rmsnorm_fp8"]["us"],
+                                           2),
+            "what": "gdn_replay_step_norm_fp8 (codes and scales only) against "
+                    "rollback_verify_flush followed by gdn_gated_rmsnorm_fp8"}
     if "separate" in res:
         sp = res["separate"]
         line["separate_order"] = {"us_per_layer": round(sp["us_layer"], 2),

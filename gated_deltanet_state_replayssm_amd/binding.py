@@ -21,8 +21,15 @@ EXPORTED = ("gdn_replay_verify", "gdn_replay_rollback", "gdn_replay_flush",
             "gdn_replay_verify_flush", "gdn_replay_verify_varlen",
             "gdn_replay_verify_flush_varlen", "gdn_replay_rollback_varlen",
             "gdn_replay_rollback_verify_flush", "gdn_replay_sync_entries",
+            "gdn_replay_step_norm_fp8",
             "gdn_gated_rmsnorm_fp8", "gdn_causal_conv_update", "gdn_replay_strerror",
             "gdn_replay_version")
+
+
+class GdnNormFp8(ctypes.Structure):
+    """Mirror of gdn_norm_fp8."""
+    _fields_ = [("z", ctypes.c_void_p), ("weight", ctypes.c_void_p), ("eps", ctypes.c_float),
+                ("q", ctypes.c_void_p), ("scale", ctypes.c_void_p)]
 
 
 class GdnReplayCache(ctypes.Structure):
@@ -86,6 +93,9 @@ def load(path: str = LIB_PATH):
     lib.gdn_replay_rollback_verify_flush.argtypes = [P, I32, VP, VP, VP, I32, VP, I32, I32, VP,
                                                      VP, VP, VP, VP, VP, VP]
     lib.gdn_replay_rollback_verify_flush.restype = ctypes.c_int
+    lib.gdn_replay_step_norm_fp8.argtypes = [P, I32, VP, VP, VP, I32, VP, I32, I32, VP, VP, VP,
+                                             VP, VP, VP, ctypes.POINTER(GdnNormFp8), VP]
+    lib.gdn_replay_step_norm_fp8.restype = ctypes.c_int
     lib.gdn_replay_sync_entries.argtypes = [I32, I32]
     lib.gdn_replay_sync_entries.restype = ctypes.c_int64
     lib.gdn_gated_rmsnorm_fp8.argtypes = [I32, I32, I32, VP, VP, VP, ctypes.c_float, VP, VP, VP]
@@ -162,6 +172,15 @@ def rollback_verify_flush_raw(cache: GdnReplayCache, num_reqs, slot_idx, num_acc
                                                    beta, out, stream)
 
 
+def step_norm_fp8_raw(cache: GdnReplayCache, num_reqs, slot_idx, num_accepted, prev_draft_lens,
+                      prev_draft, draft_lens, draft_len, min_len, q, k, v, alpha, beta, out,
+                      norm: GdnNormFp8 | None, stream) -> int:
+    return load().gdn_replay_step_norm_fp8(ctypes.byref(cache), num_reqs, slot_idx, num_accepted,
+                                           prev_draft_lens, prev_draft, draft_lens, draft_len,
+                                           min_len, q, k, v, alpha, beta, out,
+                                           None if norm is None else ctypes.byref(norm), stream)
+
+
 def verify(cache, num_reqs, slot_idx, draft_len, q, k, v, alpha, beta, out, stream) -> None:
     _check("gdn_replay_verify",
            verify_raw(cache, num_reqs, slot_idx, draft_len, q, k, v, alpha, beta, out, stream))
@@ -211,6 +230,15 @@ def rollback_verify_flush(cache, num_reqs, slot_idx, num_accepted, prev_draft_le
            rollback_verify_flush_raw(cache, num_reqs, slot_idx, num_accepted, prev_draft_lens,
                                      prev_draft, draft_lens, draft_len, min_len, q, k, v, alpha,
                                      beta, out, stream))
+
+
+def step_norm_fp8(cache, num_reqs, slot_idx, num_accepted, prev_draft_lens, prev_draft,
+                  draft_lens, draft_len, min_len, q, k, v, alpha, beta, out, norm,
+                  stream) -> None:
+    _check("gdn_replay_step_norm_fp8",
+           step_norm_fp8_raw(cache, num_reqs, slot_idx, num_accepted, prev_draft_lens, prev_draft,
+                             draft_lens, draft_len, min_len, q, k, v, alpha, beta, out, norm,
+                             stream))
 
 
 def gated_rmsnorm_fp8_raw(rows, num_heads, d_v, o, z, weight, eps, q, scale, stream) -> int:

@@ -178,6 +178,49 @@ class ReplayCache:
             _stream_handle(stream))
         return out
 
+    def step_norm_fp8(self, slot_idx, num_accepted, prev_draft: int, min_len: int, q, k, v,
+                      alpha, beta, z, weight, eps: float, out=None, codes=None, scale=None,
+                      write_out=True, stream=None, prev_draft_lens=None, draft_lens=None):
+        """rollback_verify_flush with the gated RMSNorm + FP8 of its outputs in the
+        same kernel (gdn_replay_step_norm_fp8). z [R, D, HV, dv] bf16 gate, weight
+        [dv] fp32. Returns (out or None when write_out is False, codes uint8
+        [R, D, HV, dv], scale fp32 [R, D, HV])."""
+        R = slot_idx.shape[0]
+        D = alpha.shape[1] if alpha.dim() == 3 else 0
+        dev = self.device
+        if write_out:
+            R, D, out = self._draft_args(slot_idx, q, k, v, alpha, beta, out)
+        else:
+            tin = _TORCH_IN[self.in_dtype]
+            _need(slot_idx, "slot_idx", torch.int32, (R,), dev)
+            for t, name, dt, shape in ((q, "q", tin, (R, D, self.hk, self.dk)),
+                                       (k, "k", tin, (R, D, self.hk, self.dk)),
+                                       (v, "v", tin, (R, D, self.hv, self.dv)),
+                                       (alpha, "alpha", torch.float32, (R, D, self.hv)),
+                                       (beta, "beta", torch.float32, (R, D, self.hv))):
+                _need(t, name, dt, shape, dev)
+            out = None
+        _need(num_accepted, "num_accepted", torch.int32, (R,), dev)
+        _need(z, "z", torch.bfloat16, (R, D, self.hv, self.dv), dev)
+        _need(weight, "weight", torch.float32, (self.dv,), dev)
+        if codes is None:
+            codes = torch.empty((R, D, self.hv, self.dv), dtype=torch.uint8, device=dev)
+        if scale is None:
+            scale = torch.empty((R, D, self.hv), dtype=torch.float32, device=dev)
+        _need(codes, "codes", torch.uint8, (R, D, self.hv, self.dv), dev)
+        _need(scale, "scale", torch.float32, (R, D, self.hv), dev)
+        lens = self._lens(draft_lens, R)
+        plens = self._lens(prev_draft_lens, R)
+        norm = binding.GdnNormFp8(z.data_ptr(), weight.data_ptr(), float(eps), codes.data_ptr(),
+                                  scale.data_ptr())
+        binding.step_norm_fp8(
+            self.struct(), R, slot_idx.data_ptr(), num_accepted.data_ptr(),
+            None if plens is None else plens.data_ptr(), int(prev_draft),
+            None if lens is None else lens.data_ptr(), D, int(min_len), q.data_ptr(), k.data_ptr(),
+            v.data_ptr(), alpha.data_ptr(), beta.data_ptr(),
+            None if out is None else out.data_ptr(), norm, _stream_handle(stream))
+        return out, codes, scale
+
     def rollback(self, slot_idx, draft_len: int, num_accepted, stream=None,
                  draft_lens=None) -> None:
         R = slot_idx.shape[0]

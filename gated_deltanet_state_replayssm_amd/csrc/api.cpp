@@ -61,13 +61,14 @@ CacheView view_of(const gdn_replay_cache *c) {
 int verify_args(const gdn_replay_cache *c, int32_t num_reqs, const int32_t *slot_idx,
                 int32_t draft_len, const void *q, const void *k, const void *v, const float *alpha,
                 const float *beta, float *out, gdnr::VerifyArgs *a, bool varlen = false,
-                const int32_t *draft_lens = nullptr) {
+                const int32_t *draft_lens = nullptr, bool out_optional = false) {
   int st = check_cache(c);
   if (st != GDN_OK) return st;
   if (num_reqs < 0 || num_reqs > c->num_slots) return GDN_EINVAL;
   if (draft_len < 1 || draft_len > c->ring_cap) return GDN_EINVAL;
   if (num_reqs == 0) return GDN_OK;
-  if (!slot_idx || !q || !k || !v || !alpha || !beta || !out) return GDN_EINVAL;
+  if (!slot_idx || !q || !k || !v || !alpha || !beta || (!out && !out_optional))
+    return GDN_EINVAL;
   if (varlen && (!draft_lens || !aligned(draft_lens, 4))) return GDN_EINVAL;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(alpha, 4) ||
       !aligned(beta, 4) || !aligned(out, 16) || !aligned(slot_idx, 4))
@@ -80,6 +81,11 @@ int verify_args(const gdn_replay_cache *c, int32_t num_reqs, const int32_t *slot
   a->prev_accepted = nullptr;
   a->prev_draft_lens = nullptr;
   a->prev_draft = 0;
+  a->norm_z = nullptr;
+  a->norm_w = nullptr;
+  a->norm_eps = 0.f;
+  a->norm_q = nullptr;
+  a->norm_scale = nullptr;
   a->q = q;
   a->k = k;
   a->v = v;
@@ -236,6 +242,40 @@ int gdn_replay_rollback_verify_flush(const gdn_replay_cache *c, int32_t num_reqs
   if (st != GDN_OK) return st;
   return verify_flush_impl(c, num_reqs, slot_idx, draft_len, min_len, q, k, v, alpha, beta, out,
                            stream, varlen, draft_lens);
+}
+
+int gdn_replay_step_norm_fp8(const gdn_replay_cache *c, int32_t num_reqs,
+                             const int32_t *slot_idx, const int32_t *num_accepted,
+                             const int32_t *prev_draft_lens, int32_t prev_draft,
+                             const int32_t *draft_lens, int32_t draft_len, int32_t min_len,
+                             const void *q, const void *k, const void *v, const float *alpha,
+                             const float *beta, float *out, const gdn_norm_fp8 *norm,
+                             hipStream_t stream) {
+  gdnr::VerifyArgs a;
+  const bool varlen = draft_lens != nullptr;
+  int st = verify_args(c, num_reqs, slot_idx, draft_len, q, k, v, alpha, beta, out, &a, varlen,
+                       draft_lens, /*out_optional=*/true);
+  if (st != GDN_OK) return st;
+  if (!gdnr::fused_supported(c->d_k, c->d_v, c->in_dtype == GDN_F32, draft_len, c->ring_cap))
+    return GDN_EUNSUPPORTED;
+  if (!norm || !(norm->eps > 0.f) || norm->eps > 1.f) return GDN_EINVAL;  // also rejects NaN
+  if (num_reqs == 0) return GDN_OK;
+  if (prev_draft < 1 || prev_draft > c->ring_cap) return GDN_EINVAL;
+  if (!num_accepted || !aligned(num_accepted, 4)) return GDN_EINVAL;
+  if (prev_draft_lens && !aligned(prev_draft_lens, 4)) return GDN_EINVAL;
+  if (!norm->z || !norm->weight || !norm->q || !norm->scale) return GDN_EINVAL;
+  if (!aligned(norm->z, 4) || !aligned(norm->weight, 8) || !aligned(norm->q, 2) ||
+      !aligned(norm->scale, 4))
+    return GDN_EINVAL;
+  a.prev_accepted = num_accepted;
+  a.prev_draft_lens = prev_draft_lens;
+  a.prev_draft = prev_draft;
+  a.norm_z = norm->z;
+  a.norm_w = norm->weight;
+  a.norm_eps = norm->eps;
+  a.norm_q = norm->q;
+  a.norm_scale = norm->scale;
+  return gdnr::launch_verify_flush_fused(a, min_len, stream) == hipSuccess ? GDN_OK : GDN_EHIP;
 }
 
 int gdn_replay_rollback(const gdn_replay_cache *c, int32_t num_reqs, const int32_t *slot_idx,

@@ -31,6 +31,8 @@
 // B operand of K H: k-step s takes rows 32 s + 4 g + {0..3} and
 // 32 s + 16 + 4 g + {0..3}, and the key rows are read from LDS in that order.
 // Token-indexed accumulators (Y, W) chain the same way into the next product.
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -164,7 +166,9 @@ __device__ __forceinline__ T bload(Rsrc r, uint32_t voff, uint32_t soff = 0) {
 
 template <typename T, int AUX = kWriteOut>
 __device__ __forceinline__ void bstore(const T &v, Rsrc r, uint32_t voff, uint32_t soff = 0) {
-  if constexpr (sizeof(T) == 4)
+  if constexpr (sizeof(T) == 2)
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, v), r, voff, soff, AUX);
+  else if constexpr (sizeof(T) == 4)
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, voff, soff, AUX);
   else if constexpr (sizeof(T) == 8)
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, voff, soff, AUX);
@@ -817,6 +821,190 @@ __device__ __forceinline__ void emit_outputs(const Smem<DK, DV> &sm, const f32x4
   }
 }
 
+// The gate and weight a lane needs for the gated RMSNorm + FP8 of its draft
+// rows (t = 16 a + 4 g + i, columns col, col + 1), loaded ahead of the outputs.
+struct Gate {
+  uint32_t z[2][4];  // bf16 pairs (zero for rows that are not draft rows)
+  float w[2];
+};
+
+// Per-request resources of the norm's gate, codes and scales (rows of request
+// r, value head h, at most D rows).
+struct NormRsrc {
+  Rsrc z, q, scale;
+};
+
+__device__ __forceinline__ NormRsrc norm_rsrc(const VerifyArgs &va, int r, int h, int DV, int D) {
+  const int HV = va.c.hv;
+  const int64_t row0 = (int64_t)r * va.draft * HV + h;  // (row r * draft, head h)
+  NormRsrc n;
+  n.z = make_rsrc(static_cast<const uint16_t *>(va.norm_z) + row0 * DV,
+                  ((D - 1) * HV * DV + DV) * 2);
+  n.q = make_rsrc(va.norm_q + row0 * DV, (D - 1) * HV * DV + DV);
+  n.scale = make_rsrc(va.norm_scale + row0, ((D - 1) * HV + 1) * 4);
+  return n;
+}
+
+template <int DV, int NT>
+__device__ __forceinline__ Gate load_gate(const VerifyArgs &va, const NormRsrc &nr, int col, int g,
+                                          int B, int Treal) {
+  static_assert(NT == 2, "a lane's two columns are one bf16 pair");
+  Gate gt;
+  const uint32_t row_bytes = va.c.hv * DV * 2;
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * a + 4 * g + i;
+      gt.z[a][i] = bload<uint32_t, kStream>(
+          nr.z, (t < Treal && t >= B) ? (uint32_t)(t - B) * row_bytes + col * 2 : kOOB);
+    }
+  const float2 w = *reinterpret_cast<const float2 *>(va.norm_w + col);
+  gt.w[0] = w.x;
+  gt.w[1] = w.y;
+  return gt;
+}
+
+// Sum / maximum over the 16 lanes of a DPP row (lanes 16 g .. 16 g + 15): the
+// total ends in the row's last lane.
+template <bool MAX>
+__device__ __forceinline__ float row16_reduce(float v) {
+  auto op = [](float x, float y) { return MAX ? fmaxf(x, y) : x + y; };
+  v = op(v, dpp_or<0x111, 0xf>(0.f, v));  // row_shr:1
+  v = op(v, dpp_or<0x112, 0xf>(0.f, v));  // row_shr:2
+  v = op(v, dpp_or<0x114, 0xf>(0.f, v));  // row_shr:4
+  v = op(v, dpp_or<0x118, 0xf>(0.f, v));  // row_shr:8
+  return v;
+}
+
+// Draft outputs as emit_outputs (stored to out unless its resource is empty),
+// then the gated RMSNorm + FP8 of each draft row (token, value head), per
+// "The inference stack behind OCRia" (section on fusing kernels: the gated
+// RMSNorm and the FP8 quantisation of its result in one kernel), here fused
+// with the recurrence that produces the row as well:
+//     r = sqrt(mean_j o_j^2 + eps),  y_j = o_j / r * w_j * silu(z_j),
+//     s = max_j |y_j| / 448 (1 for an all-zero row),  c_j = E4M3(y_j / s)
+// (OCP E4M3, round to nearest even, saturating). A row's DV values lie in one
+// DPP row (16 lanes) of each wave: sums and maxima are reduced over the lanes
+// with DPP moves, then across the waves through red[2][32][4] in LDS.
+template <int DK, int DV, int NT>
+__device__ __forceinline__ void emit_outputs_norm(const Smem<DK, DV> &sm,
+                                                  const f32x4 (&Z)[2][NT],
+                                                  const f32x4 (&Wm)[2][NT], int g, int l16,
+                                                  int wave, int Treal, int B, Rsrc out, int col,
+                                                  const VerifyArgs &va, const NormRsrc &nr,
+                                                  const Gate &gt, float (*red)[kCh][4]) {
+  typedef typename Cols<NT>::F F;
+  constexpr int WAVES = DV / (16 * NT);
+  constexpr float kE4M3Max = 448.f;
+  const uint32_t out_row = va.c.hv * DV * 4, q_row = va.c.hv * DV, s_row = va.c.hv * 4;
+  bf16x8 wh[NT], wl[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) tok_operand(Wm[0][nt], Wm[1][nt], wh[nt], wl[nt]);
+  f32x4 O[2][NT];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    float crow[8], ga[4];
+    rd_frow(sm.Cm, 16 * a + l16, g, crow);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ga[i] = sm.gam[16 * a + 4 * g + i];
+    bf16x8 chh, chl;
+    split8(crow, chh, chl);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      f32x4 acc;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = ga[i] * Z[a][nt][i];
+      acc = mfma(chh, wh[nt], acc);
+      acc = mfma(chh, wl[nt], acc);
+      acc = mfma(chl, wh[nt], acc);
+      O[a][nt] = acc;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * a + 4 * g + i;
+      F o;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) o[nt] = O[a][nt][i];
+      bstore(o, out, (t < Treal && t >= B) ? (uint32_t)(t - B) * out_row + col * 4 : kOOB);
+    }
+  }
+  // Row slot (a, i) of a lane holds rows 16 a + 4 g + i, g = 0..3: a slot with
+  // no draft row in any of them (the same in every wave) is skipped whole.
+  auto slot_live = [&](int a, int i) {
+    const int t0 = 16 * a + i;
+    return (t0 + 12 >= B) && (t0 < Treal) &&
+           ((t0 >= B && t0 < Treal) || (t0 + 4 >= B && t0 + 4 < Treal) ||
+            (t0 + 8 >= B && t0 + 8 < Treal) || (t0 + 12 >= B && t0 + 12 < Treal));
+  };
+  // Mean square of each row: the rows' reductions are independent chains. 1/r
+  // comes from the hardware reciprocal square root (1 ulp) and the gate's
+  // 1/(1 + e^-z) and 1/max|y| from the hardware reciprocal: r only sets the
+  // scale (the codes are y / max|y|, where it cancels), and all three sit far
+  // inside the scale's and the codes' tolerance.
+  float acc[2][4];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (!slot_live(a, i)) continue;
+      float ss = 0.f;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) ss = fmaf(O[a][nt][i], O[a][nt][i], ss);
+      acc[a][i] = row16_reduce<false>(ss);
+      if (l16 == 15) red[0][16 * a + 4 * g + i][wave] = acc[a][i];
+    }
+  __syncthreads();
+  float y[2][NT][4];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (!slot_live(a, i)) continue;
+      const float4 p = *reinterpret_cast<const float4 *>(red[0][16 * a + 4 * g + i]);
+      const float tot = WAVES == 4 ? (p.x + p.y) + (p.z + p.w) : p.x + p.y;
+      const float rinv =
+          __builtin_amdgcn_rsqf(fmaxf(fmaf(tot, 1.f / DV, va.norm_eps), 1.17549435e-38f));
+      float amax = 0.f;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const uint32_t zb = gt.z[a][i];
+        const float zf = __uint_as_float(nt == 0 ? zb << 16 : zb & 0xffff0000u);
+        const float gate = zf * __builtin_amdgcn_rcpf(1.f + __expf(-zf));
+        y[a][nt][i] = O[a][nt][i] * rinv * gt.w[nt] * gate;
+        amax = fmaxf(amax, fabsf(y[a][nt][i]));
+      }
+      acc[a][i] = row16_reduce<true>(amax);
+      if (l16 == 15) red[1][16 * a + 4 * g + i][wave] = acc[a][i];
+    }
+  __syncthreads();
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (!slot_live(a, i)) continue;
+      const int t = 16 * a + 4 * g + i;
+      const bool row = t < Treal && t >= B;
+      const float4 p = *reinterpret_cast<const float4 *>(red[1][t]);
+      const float amax = WAVES == 4 ? fmaxf(fmaxf(p.x, p.y), fmaxf(p.z, p.w)) : fmaxf(p.x, p.y);
+      float scale = 1.f, inv = 1.f;
+      if (amax >= 0x1p-126f) {
+        scale = amax * (1.f / kE4M3Max);
+        inv = kE4M3Max * __builtin_amdgcn_rcpf(amax);
+      } else if (amax > 0.f) {  // a subnormal maximum: exact quotients
+        scale = amax / kE4M3Max;
+        inv = kE4M3Max / amax;
+      }
+      // clamp first: the conversion then never sees a value past the largest code
+      const float c0 = fminf(fmaxf(y[a][0][i] * inv, -kE4M3Max), kE4M3Max);
+      const float c1 = fminf(fmaxf(y[a][1][i] * inv, -kE4M3Max), kE4M3Max);
+      const uint32_t packed = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c0, c1, 0, false);
+      bstore((uint16_t)(packed & 0xffff), nr.q, row ? (uint32_t)(t - B) * q_row + col : kOOB);
+      if (wave == 0 && l16 == 0)
+        bstore(scale, nr.scale, row ? (uint32_t)(t - B) * s_row : kOOB);
+    }
+}
+
 // Fold the chunk into the state: H <- gamma_T H + K^T (L[T-1] o W).
 template <int DK, int DV, int NT>
 __device__ __forceinline__ void fold_state(const Smem<DK, DV> &sm, const f32x4 (&Wm)[2][NT], int g,
@@ -1291,7 +1479,7 @@ __device__ Req ordered_request(const VerifyArgs &va, int mn, int q, int lane, Mo
 // for their fold. So each workgroup of a due slot counts itself in at the
 // (slot, key head) counter once its fold inputs are staged, and the last
 // one of the key head's group appends k and q (the others have read by then).
-template <int DK, int DV, int NT, bool VARLEN, bool ROLLBACK>
+template <int DK, int DV, int NT, bool VARLEN, bool ROLLBACK, bool NORM>
 __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyArgs va,
                                                                          int min_len) {
   constexpr int WAVES = DV / (16 * NT);
@@ -1484,9 +1672,21 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyA
 
   f32x4 Y[2][NT], Z[2][NT], Wm[2][NT];
   contract<DK, DV, NT, kY | kZ>(sm, H, g, l16, Y, Z);
-  solve_w<DK, DV, NT>(sm, Y, col_of(), g, l16, Wm);
-  emit_outputs<DK, DV, NT>(sm, Z, Wm, g, l16, 0, u.T, u.B, out_rsrc(va, r, h, DV, max(D, 1)), col_of() * 4,
-                           HV * DV * 4);
+  if constexpr (NORM) {
+    // the gate and weight load while W is solved; out may be absent
+    const NormRsrc nr = norm_rsrc(va, r, h, DV, max(D, 1));
+    const Gate gt = load_gate<DV, NT>(va, nr, col_of(), g, u.B, u.T);
+    solve_w<DK, DV, NT>(sm, Y, col_of(), g, l16, Wm);
+    __shared__ __align__(16) float nred[2][kCh][4];
+    emit_outputs_norm<DK, DV, NT>(
+        sm, Z, Wm, g, l16, wave, u.T, u.B,
+        va.out ? out_rsrc(va, r, h, DV, max(D, 1)) : make_rsrc(nullptr, 0), col_of(), va, nr, gt,
+        nred);
+  } else {
+    solve_w<DK, DV, NT>(sm, Y, col_of(), g, l16, Wm);
+    emit_outputs<DK, DV, NT>(sm, Z, Wm, g, l16, 0, u.T, u.B, out_rsrc(va, r, h, DV, max(D, 1)),
+                             col_of() * 4, HV * DV * 4);
+  }
   const bool kq_writer = due ? group_rank == G - 1 : h % G == 0;
   if (due)
     sga.append(sm, sr, u, 0, u.T, kq_writer);
@@ -1516,26 +1716,31 @@ hipError_t launch_verify_flush_fused(const VerifyArgs &a, int min_len, hipStream
   constexpr int NT = 2;
   const dim3 grid(a.num_reqs * a.c.hv);
   const bool varlen = a.draft_lens != nullptr, rollback = a.prev_accepted != nullptr;
+  const bool norm = a.norm_q != nullptr;
+  if (norm && !rollback) return hipErrorInvalidValue;  // the norm rides on the one-call step
   auto go = [&](auto kernel, int dv) {
     hipLaunchKernelGGL(kernel, grid, dim3(64 * (dv / (16 * NT))), 0, stream, a, min_len);
   };
-  if (a.c.dk == 128) {
-    if (rollback)
-      varlen ? go(replay_fused<128, 128, NT, true, true>, 128)
-             : go(replay_fused<128, 128, NT, false, true>, 128);
+  // (VARLEN, ROLLBACK, NORM) instantiations; the kernel without the rollback
+  // and the norm keeps its own code
+  auto pick = [&](auto dk) {
+    constexpr int D = decltype(dk)::value;
+    if (norm)
+      varlen ? go(replay_fused<D, D, NT, true, true, true>, D)
+             : go(replay_fused<D, D, NT, false, true, true>, D);
+    else if (rollback)
+      varlen ? go(replay_fused<D, D, NT, true, true, false>, D)
+             : go(replay_fused<D, D, NT, false, true, false>, D);
     else
-      varlen ? go(replay_fused<128, 128, NT, true, false>, 128)
-             : go(replay_fused<128, 128, NT, false, false>, 128);
-  } else if (a.c.dk == 64) {
-    if (rollback)
-      varlen ? go(replay_fused<64, 64, NT, true, true>, 64)
-             : go(replay_fused<64, 64, NT, false, true>, 64);
-    else
-      varlen ? go(replay_fused<64, 64, NT, true, false>, 64)
-             : go(replay_fused<64, 64, NT, false, false>, 64);
-  } else {
+      varlen ? go(replay_fused<D, D, NT, true, false, false>, D)
+             : go(replay_fused<D, D, NT, false, false, false>, D);
+  };
+  if (a.c.dk == 128)
+    pick(std::integral_constant<int, 128>());
+  else if (a.c.dk == 64)
+    pick(std::integral_constant<int, 64>());
+  else
     return hipErrorInvalidValue;
-  }
   return hipGetLastError();
 }
 

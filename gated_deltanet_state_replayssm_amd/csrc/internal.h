@@ -46,6 +46,13 @@ struct VerifyArgs {
   const int32_t *prev_accepted;
   const int32_t *prev_draft_lens;
   int32_t prev_draft;
+  // gated RMSNorm + FP8 of the draft outputs in the same kernel (fused kernel
+  // with the rollback only; norm_q null: none). out may then be null.
+  const void *norm_z;            // [R][draft][HV][d_v] bf16 gate
+  const float *norm_w;           // [d_v]
+  float norm_eps;
+  uint8_t *norm_q;               // [R][draft][HV][d_v] E4M3 codes
+  float *norm_scale;             // [R][draft][HV]
   const void *q, *k, *v;
   const float *alpha, *beta;
   float *out;

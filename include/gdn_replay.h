@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define GDN_REPLAY_VERSION 5
+#define GDN_REPLAY_VERSION 6
 
 typedef enum {
   GDN_OK = 0,
@@ -258,6 +258,49 @@ int gdn_replay_rollback_verify_flush(const gdn_replay_cache *c, int32_t num_reqs
                                      int32_t min_len, const void *q, const void *k, const void *v,
                                      const float *alpha, const float *beta, float *out,
                                      hipStream_t stream);
+
+/*
+ * gdn_replay_step_norm_fp8 — gdn_replay_rollback_verify_flush with the gated
+ * RMSNorm + FP8 of its outputs in the same kernel: the draft outputs go
+ * through the norm while still in registers ("The inference stack behind
+ * OCRia", section on fusing kernels: avoid HBM round trips between the
+ * producer of a tensor and its normalisation and quantisation), so the fp32
+ * outputs need not be written or read back.
+ *
+ * Result: out (if not NULL), state, ring, head, len and err exactly as
+ * gdn_replay_rollback_verify_flush with the same arguments; norm->q and
+ * norm->scale as gdn_gated_rmsnorm_fp8 over the draft rows of out (the
+ * [num_reqs * D][HV] groups, D = draft_len), i.e. for request i, draft token
+ * j < D_i, value head h: the group out[i][j][h][:] with gate z[i][j][h][:].
+ * Rows j >= D_i and skipped requests (device errors) are left untouched in
+ * q and scale, as in out. Arithmetic in fp32 as gdn_gated_rmsnorm_fp8 (the sums
+ * are taken in another order, so a code can differ from that call's where the
+ * value lies at a rounding midpoint).
+ *
+ *   out   [num_reqs][D][HV][d_v] fp32, or NULL: outputs not stored.
+ *   norm  z [num_reqs][D][HV][d_v] bf16 (4-byte aligned), weight [d_v] fp32
+ *         (8-byte aligned), eps in (0, 1], q [num_reqs][D][HV][d_v] uint8
+ *         (2-byte aligned), scale [num_reqs][D][HV] fp32.
+ *   other arguments as for gdn_replay_rollback_verify_flush.
+ * Only the one-kernel shapes (bf16 inputs, d_k = d_v in {64, 128}, ring
+ * capacity <= 32, D <= 32) are taken: GDN_EUNSUPPORTED otherwise (the
+ * library allocates no scratch for a fallback; use the separate calls).
+ */
+typedef struct gdn_norm_fp8 {
+  const void *z;
+  const float *weight;
+  float eps;
+  uint8_t *q;
+  float *scale;
+} gdn_norm_fp8;
+
+int gdn_replay_step_norm_fp8(const gdn_replay_cache *c, int32_t num_reqs,
+                             const int32_t *slot_idx, const int32_t *num_accepted,
+                             const int32_t *prev_draft_lens, int32_t prev_draft,
+                             const int32_t *draft_lens, int32_t draft_len, int32_t min_len,
+                             const void *q, const void *k, const void *v, const float *alpha,
+                             const float *beta, float *out, const gdn_norm_fp8 *norm,
+                             hipStream_t stream);
 
 /*
  * gdn_gated_rmsnorm_fp8 — the step after the recurrence: gated RMSNorm of the

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert b.version() == 5
+    assert b.version() == 6
     for st in (b.GDN_OK, b.GDN_EINVAL, b.GDN_EUNSUPPORTED, b.GDN_EHIP):
         assert b.load().gdn_replay_strerror(st)
     assert b.load().gdn_replay_strerror(12345) == b"unknown status"
@@ -183,6 +183,42 @@ def test_step_call_validation():
                                                      None) == b.GDN_EINVAL
 
 
+def _step_norm(c, num_reqs=2, acc=FAKE, pdraft=4, draft=4, out=FAKE, norm="ok", **ptrs):
+    p = dict(slot=FAKE, q=FAKE, k=FAKE, v=FAKE, a=FAKE, be=FAKE)
+    p.update(ptrs)
+    if norm == "ok":
+        norm = b.GdnNormFp8(FAKE, FAKE, 1e-6, FAKE, FAKE)
+    return b.step_norm_fp8_raw(c, num_reqs, p["slot"], acc, None, pdraft, None, draft, 1, p["q"],
+                               p["k"], p["v"], p["a"], p["be"], out, norm, None)
+
+
+def test_step_norm_call_validation():
+    """The one-kernel shapes only (no fallback, no scratch); out may be NULL;
+    the norm's arguments are checked as gdn_gated_rmsnorm_fp8 checks them."""
+    c = _cache(d_k=64, d_v=64, ring_cap=32)
+    assert _step_norm(c, num_reqs=0, acc=None, q=None) == b.GDN_OK
+    assert _step_norm(_cache(), num_reqs=0) == b.GDN_EUNSUPPORTED          # d = 16
+    assert _step_norm(_cache(d_k=64, d_v=64, ring_cap=40)) == b.GDN_EUNSUPPORTED   # C > 32
+    assert _step_norm(_cache(d_k=64, d_v=64, ring_cap=32, in_dtype=b.GDN_F32)) == b.GDN_EUNSUPPORTED
+    assert _step_norm(c, norm=None) == b.GDN_EINVAL
+    for eps in (0.0, -1.0, float("nan"), 2.0):
+        assert _step_norm(c, norm=b.GdnNormFp8(FAKE, FAKE, eps, FAKE, FAKE)) == b.GDN_EINVAL, eps
+    for i in range(4):
+        ptrs = [FAKE, FAKE, FAKE, FAKE]
+        ptrs[i] = None
+        assert _step_norm(c, norm=b.GdnNormFp8(ptrs[0], ptrs[1], 1e-6, ptrs[2], ptrs[3])) \
+            == b.GDN_EINVAL, i
+    assert _step_norm(c, norm=b.GdnNormFp8(FAKE + 2, FAKE, 1e-6, FAKE, FAKE)) == b.GDN_EINVAL
+    assert _step_norm(c, norm=b.GdnNormFp8(FAKE, FAKE + 4, 1e-6, FAKE, FAKE)) == b.GDN_EINVAL
+    assert _step_norm(c, norm=b.GdnNormFp8(FAKE, FAKE, 1e-6, FAKE + 1, FAKE)) == b.GDN_EINVAL
+    assert _step_norm(c, norm=b.GdnNormFp8(FAKE, FAKE, 1e-6, FAKE, FAKE + 2)) == b.GDN_EINVAL
+    assert _step_norm(c, acc=None) == b.GDN_EINVAL
+    assert _step_norm(c, pdraft=0) == b.GDN_EINVAL
+    assert _step_norm(c, draft=33) == b.GDN_EINVAL
+    assert _step_norm(c, out=FAKE + 4) == b.GDN_EINVAL
+    assert _step_norm(c, k=None) == b.GDN_EINVAL
+
+
 def test_norm_call_validation():
     """gdn_gated_rmsnorm_fp8: sizes, supported head dims, eps, NULL and
     misaligned pointers are rejected before any launch; zero rows is a no-op."""
@@ -248,6 +284,12 @@ def test_zero_requests_is_a_noop_without_launch():
     assert b.rollback_raw(c, 0, None, 4, None, None) == b.GDN_OK
     assert b.flush_raw(c, 0, None, 1, None) == b.GDN_OK
     assert _verify_flush(c, num_reqs=0, q=None, out=None) == b.GDN_OK
+
+
+def test_norm_struct_layout_matches_header():
+    # two pointers, a float (padded to 8), two pointers
+    assert ctypes.sizeof(b.GdnNormFp8) == 40
+    assert b.GdnNormFp8.eps.offset == 16 and b.GdnNormFp8.q.offset == 24
 
 
 def test_struct_layout_matches_header():

@@ -255,11 +255,12 @@ def sweep(args, workload="r32_hv32_hk16_d128_f64", buffer_lens=(0, 8, 16, 32, 48
     """Replay cost against the committed-buffer length (32 requests, ring capacity
     80, D = 16, 24 layer caches): (i) verify with every request's buffer at B,
     (ii) flush alone folding n tokens of every slot. HIP events around each
-    group of 24 launches (verify) or each launch (flush, whose pointers are
-    reset by a fill before every call); bytes from the byte model."""
+    group of 24 launches, made through the C entry points with arguments
+    marshalled beforehand (flush: every layer's len is reset to n before the
+    group); bytes from the byte model."""
     import torch
 
-    from gated_deltanet_state_replayssm_amd import synth
+    from gated_deltanet_state_replayssm_amd import binding, synth
     from gated_deltanet_state_replayssm_amd.cache import ReplayCache, to_device
 
     wl = synth.WORKLOADS[workload]
@@ -293,19 +294,26 @@ def sweep(args, workload="r32_hv32_hk16_d128_f64", buffer_lens=(0, 8, 16, 32, 48
                        "ring_cap": wl.cap, "layers": layers, "inputs": wl.in_dtype}}),
             flush=True)
 
+    lib = binding.load()
+    sh = stream.cuda_stream
+    dp = tuple(d[x].data_ptr() for x in ("q", "k", "v", "alpha", "beta")) + (out.data_ptr(), sh)
+    R, D = wl.num_reqs, wl.draft
+
     for B in buffer_lens:
         caches = caches_with(B)
-        marks = []
+        refs = [ctypes.byref(c.struct()) for c in caches]
+        marks, status = [], []
         for step in range(args.warmup + args.steps):
             e0, e1 = ev(), ev()
             e0.record(stream)
-            for c in caches:   # verify leaves state and pointers as they are
-                c.verify(slots, d["q"], d["k"], d["v"], d["alpha"], d["beta"], out=out)
+            # verify leaves state and pointers as they are
+            status.extend([lib.gdn_replay_verify(ref, R, slots.data_ptr(), D, *dp)
+                           for ref in refs])
             e1.record(stream)
             if step >= args.warmup:
                 marks.append((e0, e1))
         torch.cuda.synchronize()
-        assert not any(int(c.err.item()) for c in caches)
+        assert not any(status) and not any(int(c.err.item()) for c in caches)
         us = sum(a.elapsed_time(b) for a, b in marks) * 1e3 / (len(marks) * layers)
         v_bytes, _ = byte_model(wl, np.full(wl.num_reqs, B), [])
         emit("verify", B, us, v_bytes)
@@ -313,19 +321,20 @@ def sweep(args, workload="r32_hv32_hk16_d128_f64", buffer_lens=(0, 8, 16, 32, 48
 
     for n in fold_lens:
         caches = caches_with(n)
-        marks = []
+        refs = [ctypes.byref(c.struct()) for c in caches]
+        marks, status = [], []
         for step in range(args.warmup + args.steps):
             for c in caches:
                 c.len.fill_(n)   # every slot folds n tokens again (head moves on)
-                e0, e1 = ev(), ev()
-                e0.record(stream)
-                c.flush(slots, 1)
-                e1.record(stream)
-                if step >= args.warmup:
-                    marks.append((e0, e1))
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            status.extend([lib.gdn_replay_flush(ref, R, slots.data_ptr(), 1, sh) for ref in refs])
+            e1.record(stream)
+            if step >= args.warmup:
+                marks.append((e0, e1))
         torch.cuda.synchronize()
-        assert not any(int(c.err.item()) for c in caches)
-        us = sum(a.elapsed_time(b) for a, b in marks) * 1e3 / len(marks)
+        assert not any(status) and not any(int(c.err.item()) for c in caches)
+        us = sum(a.elapsed_time(b) for a, b in marks) * 1e3 / (len(marks) * layers)
         _, f_bytes = byte_model(wl, np.zeros(wl.num_reqs), [n] * wl.num_reqs)
         emit("flush", n, us, f_bytes)
         del caches

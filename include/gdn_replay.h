@@ -285,6 +285,9 @@ int gdn_replay_rollback_verify_flush(const gdn_replay_cache *c, int32_t num_reqs
  * Only the one-kernel shapes (bf16 inputs, d_k = d_v in {64, 128}, ring
  * capacity <= 32, D <= 32) are taken: GDN_EUNSUPPORTED otherwise (the
  * library allocates no scratch for a fallback; use the separate calls).
+ * Performance: the norm lengthens every workgroup's life, so this pays off
+ * when the launch is one generation of workgroups (num_reqs * HV up to about
+ * 4 per CU); for larger batches the two separate calls are faster.
  */
 typedef struct gdn_norm_fp8 {
   const void *z;

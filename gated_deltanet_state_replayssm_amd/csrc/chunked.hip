@@ -1424,6 +1424,53 @@ __device__ Req ordered_request(const VerifyArgs &va, int mn, int q, int lane, Mo
     return Req{r, __builtin_amdgcn_readlane(si, r), __builtin_amdgcn_readlane(hi, r),
                __builtin_amdgcn_readlane(ne, r), __builtin_amdgcn_readlane(ni, r), nd};
   }
+  // Up to 4 rounds of 64: every lane keeps its requests' slot and pointers, so
+  // the chosen request's come from a readlane instead of reloads, and each
+  // round's loads are issued once.
+  constexpr int kRounds = 4;
+  if (R <= 64 * kRounds) {
+    int si[kRounds], hi[kRounds], ni[kRounds], ne[kRounds];
+    uint64_t dm[kRounds];
+    int nd = 0;
+#pragma unroll
+    for (int j = 0; j < kRounds; ++j) {
+      const int i = 64 * j + lane;
+      si[j] = -1;
+      hi[j] = ni[j] = ne[j] = 0;
+      if (i < R) {
+        si[j] = va.slot_idx[i];
+        if (si[j] >= 0 && si[j] < c.num_slots) {
+          hi[j] = c.head[si[j]];
+          ni[j] = c.len[si[j]];
+          ne[j] = eff(i, hi[j], ni[j]);
+        }
+      }
+      dm[j] = __ballot(si[j] >= 0 && si[j] < c.num_slots && ne[j] >= mn);
+      nd += __popcll(dm[j]);
+    }
+    const bool want_due = q < nd;
+    int left = want_due ? q : q - nd;
+    Req o{0, -1, 0, 0, 0, nd};
+    bool found = false;
+#pragma unroll
+    for (int j = 0; j < kRounds; ++j) {
+      const uint64_t all = 64 * j < R ? lanes(j) : 0ull;
+      const uint64_t m = want_due ? dm[j] : (~dm[j] & all);
+      const int cnt = __popcll(m);
+      if (!found && left < cnt) {
+        const int l = nth_bit(m, left);
+        o.r = 64 * j + l;
+        o.s = __builtin_amdgcn_readlane(si[j], l);
+        o.head = __builtin_amdgcn_readlane(hi[j], l);
+        o.len = __builtin_amdgcn_readlane(ne[j], l);
+        o.raw_len = __builtin_amdgcn_readlane(ni[j], l);
+        found = true;
+      } else if (!found) {
+        left -= cnt;
+      }
+    }
+    return o;
+  }
   auto due_mask = [&](int j) -> uint64_t {
     const int i = 64 * j + lane;
     bool d = false;

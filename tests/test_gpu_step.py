@@ -132,3 +132,55 @@ def test_step_equals_rollback_then_verify_flush_bitwise(varlen):
         assert torch.equal(x, y), name
     assert not a.sync.any()
     assert int((a.len == 0).sum()) > 0       # some slots were flushed
+
+
+@pytest.mark.parametrize("R", [65, 200, 300])
+def test_step_ordering_rounds(R):
+    """More than 64 requests: the ordering pass in rounds of 64 with every
+    round's values kept in lanes (up to 256 requests), and in reloaded rounds
+    beyond; bad slots and pointers in the batch."""
+    wl = synth.Workload("rounds", R, R + 20, 2, 1, 64, 64, 32, 8, synth.BF16, 16, 1,
+                        "clipnormal:6:3", "uniform:0:23")
+    say(f"case step ordering rounds R={R}")
+    rng = np.random.default_rng(740 + R)
+    init = synth.make_cache_init(wl, rng)
+    init["head"][3] = 77                       # POINTER for whoever gets slot 3
+    p = Pair(wl, init)
+    prev = {}
+    for step in range(3):
+        slots = synth.make_slot_idx(wl, rng)
+        if step == 1:
+            slots[R // 2] = wl.num_slots + 5   # SLOT
+        acc = synth.sample_accepted(wl, rng)
+        pa = np.array([prev.get(int(s), 0) for s in slots], np.int32)
+        p.rollback_verify_flush(slots, pa, wl.draft, wl.flush_min_len, synth.make_draft(wl, rng),
+                                f"rounds{R} step{step}")
+        prev = {int(s): int(acc[i]) for i, s in enumerate(slots)}
+    assert p.flushed_count > 0
+
+
+def test_step_equals_rollback_then_verify_flush_bitwise_r128():
+    wl = W["r128_hv32_hk16_d128_f16"]
+    say("case step vs rollback + verify_flush, bitwise, r128")
+    rng = np.random.default_rng(750)
+    init = synth.make_cache_init(wl, rng, init_len=rng.integers(0, 17, wl.num_slots))
+    a = ReplayCache.from_numpy(init, wl.hv, wl.hk, wl.dk, wl.dv, wl.cap, wl.in_dtype)
+    b = ReplayCache.from_numpy(init, wl.hv, wl.hk, wl.dk, wl.dv, wl.cap, wl.in_dtype)
+    dr = {k: to_device(v) for k, v in synth.make_draft(wl, rng).items()}
+    slots = to_device(synth.make_slot_idx(wl, rng))
+    acc = to_device(rng.integers(0, wl.draft + 1, wl.num_reqs).astype(np.int32))
+    oa = a.rollback_verify_flush(slots, acc, wl.draft, 16, dr["q"], dr["k"], dr["v"], dr["alpha"],
+                                 dr["beta"])
+    b.rollback(slots, wl.draft, acc)
+    ob = b.verify_flush(slots, 16, dr["q"], dr["k"], dr["v"], dr["alpha"], dr["beta"])
+    torch.cuda.synchronize()
+    assert int(a.err.item()) == 0 and int(b.err.item()) == 0
+    assert torch.equal(oa.view(torch.int32), ob.view(torch.int32))
+    for name in ("state", "head", "len", "ring_k", "ring_v", "ring_alpha", "ring_beta", "ring_q"):
+        x, y = getattr(a, name), getattr(b, name)
+        if x.dtype == torch.float32:
+            x, y = x.view(torch.int32), y.view(torch.int32)
+        elif x.dtype == torch.bfloat16:
+            x, y = x.view(torch.int16), y.view(torch.int16)
+        assert torch.equal(x, y), name
+    assert not a.sync.any()

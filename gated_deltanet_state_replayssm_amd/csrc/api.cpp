@@ -162,6 +162,8 @@ int verify_flush_impl(const gdn_replay_cache *c, int32_t num_reqs, const int32_t
   const bool f32 = c->in_dtype == GDN_F32;
   if (gdnr::fused_supported(c->d_k, c->d_v, f32, draft_len, c->ring_cap))
     return gdnr::launch_verify_flush_fused(a, min_len, stream) == hipSuccess ? GDN_OK : GDN_EHIP;
+  if (gdnr::fused_long_supported(c->d_k, c->d_v, f32, draft_len, c->ring_cap))
+    return gdnr::launch_verify_flush_long(a, min_len, stream) == hipSuccess ? GDN_OK : GDN_EHIP;
   // Other shapes: the same result from the two calls back to back. With
   // per-request lengths a request whose length is out of range must not be
   // flushed, so the flush checks the lengths too.

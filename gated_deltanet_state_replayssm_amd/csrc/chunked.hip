@@ -1505,6 +1505,64 @@ __device__ Req ordered_request(const VerifyArgs &va, int mn, int q, int lane, Mo
   return o;
 }
 
+// End of a fused launch. Every workgroup counts itself in (after a barrier, so
+// that all its waves have read the pointers): HV per request rank on that
+// rank's counter, then the last of those on the grid counter. The grid's last
+// workgroup moves the pointers: a due slot's head += len, len = 0; with a
+// folded rollback, len += a for the others. With no due request and no
+// rollback nothing moves and no count is taken (every workgroup sees the same
+// count, as no pointer changes during the call).
+template <bool ROLLBACK, bool VARLEN>
+__device__ __forceinline__ void end_of_grid(const VerifyArgs &va, const Req &rq, int mn,
+                                            int32_t *rank_ctr, int32_t *grid_ctr,
+                                            const Move *moves, int *grid_rank, int tid) {
+  const CacheView &c = va.c;
+  const int HV = c.hv;
+  if (!ROLLBACK && rq.due == 0) return;  // a folded rollback moves len in any case
+  __syncthreads();
+  if (tid == 0) {
+    int last = 0;
+    if (atomicAdd(rank_ctr, 1) == HV - 1) {
+      *rank_ctr = 0;
+      last = atomicAdd(grid_ctr, 1) == va.num_reqs - 1;
+    }
+    *grid_rank = last;
+  }
+  __syncthreads();
+  if (!*grid_rank) return;
+  if (va.num_reqs <= 64) {  // moves worked out by the ordering pass
+    if (tid < va.num_reqs) {
+      const Move mv = moves[tid];
+      if (mv.slot >= 0) {
+        if (mv.head >= 0) c.head[mv.slot] = mv.head;
+        c.len[mv.slot] = mv.len;
+      }
+    }
+    if (tid == 0) *grid_ctr = 0;
+    return;
+  }
+  for (int i = tid; i < va.num_reqs; i += blockDim.x) {
+    const int si = va.slot_idx[i];
+    if (si < 0 || si >= c.num_slots) continue;
+    const int hs = c.head[si], n0 = c.len[si];
+    if (hs < 0 || hs >= c.cap || n0 < 0 || n0 > c.cap) continue;
+    int ns = n0;
+    if constexpr (ROLLBACK) {
+      int bad;
+      ns = rolled_len(va, i, n0, c.cap, &bad);
+    }
+    // a request with a bad draft length is not flushed (its rollback stands)
+    const bool skip = VARLEN && request_draft(va.draft_lens, i, va.draft) < 0;
+    if (ns >= mn && !skip) {
+      c.head[si] = hs + ns - (hs + ns >= c.cap ? c.cap : 0);
+      c.len[si] = 0;
+    } else if (ROLLBACK && ns != n0) {
+      c.len[si] = ns;
+    }
+  }
+  if (tid == 0) *grid_ctr = 0;
+}
+
 // Flush fused into verify, ring capacity <= 32. A slot with len >= max(min_len,
 // 1) first folds its len committed tokens into the checkpoint and writes it
 // back, then verifies the draft from the new checkpoint; other slots verify as
@@ -1562,54 +1620,9 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyA
   int32_t *grid_ctr = c.sync;
   int32_t *rank_ctr = slot_counter(c, blockIdx.x / HV);
 
-  // Every workgroup counts itself in at its end (after a barrier, so that all
-  // its waves have read the pointers); the last one moves the due slots' pointers.
-  // With no due request there is nothing to move and no count is taken (every
-  // workgroup sees the same count, as no pointer changes during the call).
+  // every workgroup counts itself in at its end; the grid's last moves the pointers
   auto finish = [&]() {
-    if (!ROLLBACK && rq.due == 0) return;  // a folded rollback moves len in any case
-    __syncthreads();
-    if (tid == 0) {
-      int last = 0;
-      if (atomicAdd(rank_ctr, 1) == HV - 1) {
-        *rank_ctr = 0;
-        last = atomicAdd(grid_ctr, 1) == va.num_reqs - 1;
-      }
-      grid_rank = last;
-    }
-    __syncthreads();
-    if (!grid_rank) return;
-    if (va.num_reqs <= 64) {  // moves worked out by the ordering pass
-      if (tid < va.num_reqs) {
-        const Move mv = moves[tid];
-        if (mv.slot >= 0) {
-          if (mv.head >= 0) c.head[mv.slot] = mv.head;
-          c.len[mv.slot] = mv.len;
-        }
-      }
-      if (tid == 0) *grid_ctr = 0;
-      return;
-    }
-    for (int i = tid; i < va.num_reqs; i += blockDim.x) {
-      const int si = va.slot_idx[i];
-      if (si < 0 || si >= c.num_slots) continue;
-      const int hs = c.head[si], n0 = c.len[si];
-      if (hs < 0 || hs >= c.cap || n0 < 0 || n0 > c.cap) continue;
-      int ns = n0;
-      if constexpr (ROLLBACK) {
-        int bad;
-        ns = rolled_len(va, i, n0, c.cap, &bad);
-      }
-      // a request with a bad draft length is not flushed (its rollback stands)
-      const bool skip = VARLEN && request_draft(va.draft_lens, i, va.draft) < 0;
-      if (ns >= mn && !skip) {
-        c.head[si] = hs + ns - (hs + ns >= c.cap ? c.cap : 0);
-        c.len[si] = 0;
-      } else if (ROLLBACK && ns != n0) {
-        c.len[si] = ns;
-      }
-    }
-    if (tid == 0) *grid_ctr = 0;
+    end_of_grid<ROLLBACK, VARLEN>(va, rq, mn, rank_ctr, grid_ctr, moves, &grid_rank, tid);
   };
 
   const int s = rq.s;
@@ -1743,6 +1756,175 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyA
   finish();
 }
 
+// Flush fused into verify when a replay takes several chunks (ring capacity
+// above 32). A due slot folds its n committed tokens chunk by chunk, writes the
+// folded state once and verifies the draft from it (one chunk, B = 0); any
+// other slot replays its committed tokens and the draft as replay_chunked's
+// verify does. The work order (due requests first), the draft append of a due
+// slot's key and query rows (by the last workgroup of the key head to have
+// staged all its fold inputs) and the end-of-grid pointer move are those of
+// replay_fused.
+template <int DK, int DV, int NT, bool VARLEN>
+__global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused_long(VerifyArgs va,
+                                                                              int min_len) {
+  constexpr int WAVES = DV / (16 * NT);
+  constexpr int MT = DK / 16;
+  static_assert(DK % 32 == 0 && DV % (16 * NT) == 0 && (NT == 2 || NT == 4), "tile shape");
+  static_assert(WAVES >= 2, "the T x T matrices are built by waves 0 and 1");
+  typedef typename Cols<NT>::F F;
+  __shared__ Smem<DK, DV> sm;
+  __shared__ int group_rank, grid_rank;
+  __shared__ Move moves[64];
+
+  const CacheView &c = va.c;
+  const int HV = c.hv, G = HV / c.hk;
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+  const int g = lane >> 4, l16 = lane & 15;
+  auto col_of = [&]() {
+    int t = tid;
+    asm volatile("" : "+v"(t));
+    return (t / 64) * 16 * NT + NT * (t & 15);
+  };
+  auto st_off_of = [&]() {
+    int t = tid;
+    asm volatile("" : "+v"(t));
+    return (uint32_t)((4 * ((t & 63) >> 4) * DV + (t / 64) * 16 * NT + NT * (t & 15)) * 4);
+  };
+  const int mn = max(min_len, 1);
+  const Req rq = ordered_request<false, VARLEN>(va, mn, blockIdx.x / HV, lane,
+                                                wave == 0 ? moves : nullptr);
+  const int r = rq.r, h = blockIdx.x % HV;
+  const bool lead = (h == 0 && tid == 0);
+  int32_t *grid_ctr = c.sync;
+  int32_t *rank_ctr = slot_counter(c, blockIdx.x / HV);
+  auto finish = [&]() {
+    end_of_grid<false, VARLEN>(va, rq, mn, rank_ctr, grid_ctr, moves, &grid_rank, tid);
+  };
+
+  const int s = rq.s;
+  if (s < 0 || s >= c.num_slots) {
+    if (lead) raise_err(c.err, GDN_DERR_SLOT);
+    finish();
+    return;
+  }
+  const int C = c.cap;
+  const int head = rq.head, n = rq.len;
+  if (head < 0 || head >= C || n < 0 || n > C) {
+    if (lead) raise_err(c.err, GDN_DERR_POINTER);
+    finish();
+    return;
+  }
+  const int D = VARLEN ? request_draft(va.draft_lens, r, va.draft) : va.draft;
+  if (VARLEN && D < 0) {
+    if (lead) raise_err(c.err, GDN_DERR_DRAFT);
+    finish();
+    return;
+  }
+  const bool due = n >= mn;
+  if (!due && ((VARLEN && D == 0) || n + D > C)) {  // capacity error, or nothing to do
+    if (lead && D > 0) raise_err(c.err, GDN_DERR_CAPACITY);
+    finish();
+    return;
+  }
+  const int kh = h / G;
+  const Rsrc st = make_rsrc(c.state + ((int64_t)s * HV + h) * DK * DV, DK * DV * 4);
+  int32_t *group_ctr = group_counter(c, s, kh);
+  constexpr int SW = WAVES >= 4 ? 2 : WAVES;
+  F H[MT][4];
+  float al;  // staged alpha of token lane % 32 of the current chunk
+
+  // One chunk loop and one output stage serve both kinds of slot (two copies of
+  // the register-bound body do not fit the registers). The stream u1 starts at
+  // head with the n committed tokens: a due slot's stream is those n tokens,
+  // all folded (its state is then written and the draft verified from it as a
+  // stream of its own, B = 0); any other slot's is the n tokens and the draft,
+  // whose last chunk is the output chunk.
+  const Unit u1{r, h, s, kh, head, n, due ? n : n + D, C};
+  const Srcs s1 = due ? make_srcs<DK, DV>(c, u1, nullptr, false)
+                      : make_srcs<DK, DV>(c, u1, &va, true);
+  const int nch = (u1.T + kCh - 1) / kCh, T0 = u1.T - kCh * (nch - 1);
+  const int nfold = due ? nch : nch - 1;
+  const bool out0 = !due && nch == 1;  // chunk 0 is the output chunk
+  {
+    // waves SW.. load their state first; waves 0..SW-1 stage chunk 0, then load
+    Stage<DK, DV, NT, true, 64 * SW> sg0;
+    if (wave >= SW) {
+      load_state<DK, DV, NT>(st, st_off_of(), H);
+      al = 1.f;
+    } else {
+      sg0.load(s1, u1, 0, T0, out0);
+      sg0.store(sm, T0, out0);
+      al = sg0.al;
+      __builtin_amdgcn_sched_barrier(0);
+      load_state<DK, DV, NT>(st, st_off_of(), H);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+  }
+  // The thread index comes through an opaque copy so that the per-thread row
+  // offsets are recomputed in every iteration rather than held in registers.
+#pragma nounroll
+  for (int ch = 0; ch < nfold; ++ch) {
+    const int lane = opaque_tid() % 64, g = lane >> 4, l16 = lane & 15;
+    if (ch > 0) {
+      Stage<DK, DV, NT, true> sg;
+      sg.load(s1, u1, T0 + kCh * (ch - 1), kCh, false);
+      sg.store(sm, kCh, false);
+      al = sg.al;
+      __syncthreads();
+    }
+    // a due slot's fold inputs are all read: count in for the key rows' append
+    if (due && ch == nfold - 1 && tid == 0) group_rank = atomicAdd(group_ctr, 1);
+    if (wave == 0) build_tt<DK, DV>(sm, al, lane, g, l16);
+    __syncthreads();  // T x T matrices complete
+    f32x4 Y[2][NT], Z[2][NT], Wm[2][NT];
+    contract<DK, DV, NT, kY>(sm, H, g, l16, Y, Z);
+    solve_w<DK, DV, NT>(sm, Y, col_of(), g, l16, Wm);
+    fold_state<DK, DV, NT>(sm, Wm, g, l16, H);
+    __syncthreads();  // LDS is rewritten by the next chunk
+  }
+
+  // ---- the output chunk
+  Unit uo = u1;
+  int t0 = nch == 1 ? 0 : T0 + kCh * (nch - 2), Treal = nch == 1 ? T0 : kCh;
+  if (due) {
+    store_state<DK, DV, NT>(st, st_off_of(), H);
+    const int hd = head + n - (head + n >= C ? C : 0);
+    uo = Unit{r, h, s, kh, hd, 0, D, C};
+    t0 = 0;
+    Treal = D;
+  }
+  const Srcs so = due ? make_srcs<DK, DV>(c, uo, &va, true) : s1;
+  if (!out0) {
+    Stage<DK, DV, NT, true> sg;
+    sg.load(so, uo, t0, Treal, true);
+    sg.store(sm, Treal, true);
+    al = sg.al;
+    __syncthreads();
+  }
+  if (wave == 0)
+    build_tt<DK, DV>(sm, al, lane, g, l16);
+  else if (wave == 1)
+    build_c<DK, DV>(sm, al, lane, g, l16);
+  __syncthreads();  // T x T matrices complete
+  {
+    f32x4 Y[2][NT], Z[2][NT], Wm[2][NT];
+    contract<DK, DV, NT, kY | kZ>(sm, H, g, l16, Y, Z);
+    solve_w<DK, DV, NT>(sm, Y, col_of(), g, l16, Wm);
+    emit_outputs<DK, DV, NT>(sm, Z, Wm, g, l16, t0, Treal, uo.B,
+                             out_rsrc(va, r, h, DV, max(D, 1)), col_of() * 4, HV * DV * 4);
+  }
+  const bool kq_writer = due ? group_rank == G - 1 : h % G == 0;
+  // the draft rows, from LDS, with the thread mapping of the stage that wrote them
+  if (out0) {
+    if (wave < SW) Stage<DK, DV, NT, true, 64 * SW>{}.append(sm, so, uo, t0, Treal, kq_writer);
+  } else {
+    Stage<DK, DV, NT, true>{}.append(sm, so, uo, t0, Treal, kq_writer);
+  }
+  if (due && kq_writer && tid == 0) *group_ctr = 0;  // every member has counted in
+  finish();
+}
+
 template <int DK, int DV, bool VERIFY, bool VARLEN>
 hipError_t launch_t(const VerifyArgs &va, const FlushArgs &fa, int num_reqs, int hv, int cap,
                     hipStream_t stream) {
@@ -1789,6 +1971,29 @@ hipError_t launch_verify_flush_fused(const VerifyArgs &a, int min_len, hipStream
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+hipError_t launch_verify_flush_long(const VerifyArgs &a, int min_len, hipStream_t stream) {
+  constexpr int NT = 2;
+  const dim3 grid(a.num_reqs * a.c.hv);
+  const bool varlen = a.draft_lens != nullptr;
+  if (a.prev_accepted || a.norm_q) return hipErrorInvalidValue;  // not taken here
+  auto go = [&](auto kernel, int dv) {
+    hipLaunchKernelGGL(kernel, grid, dim3(64 * (dv / (16 * NT))), 0, stream, a, min_len);
+  };
+  if (a.c.dk == 128)
+    varlen ? go(replay_fused_long<128, 128, NT, true>, 128)
+           : go(replay_fused_long<128, 128, NT, false>, 128);
+  else if (a.c.dk == 64)
+    varlen ? go(replay_fused_long<64, 64, NT, true>, 64)
+           : go(replay_fused_long<64, 64, NT, false>, 64);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+bool fused_long_supported(int dk, int dv, bool in_f32, int draft, int cap) {
+  return chunked_supported(dk, dv, in_f32, draft) && cap > kCh;
 }
 
 bool fused_supported(int dk, int dv, bool in_f32, int draft, int cap) {

@@ -83,6 +83,9 @@ hipError_t launch_verify_chunked(const VerifyArgs &a, hipStream_t stream);
 hipError_t launch_flush_chunked(const FlushArgs &a, hipStream_t stream);
 // Flush fused into verify in one kernel (chunked shapes, ring capacity <= 32).
 bool fused_supported(int dk, int dv, bool in_f32, int draft, int cap);
+// The same for replays of several chunks (ring capacity above 32).
+bool fused_long_supported(int dk, int dv, bool in_f32, int draft, int cap);
+hipError_t launch_verify_flush_long(const VerifyArgs &a, int min_len, hipStream_t stream);
 hipError_t launch_verify_flush_fused(const VerifyArgs &a, int min_len, hipStream_t stream);
 // (a.prev_accepted non-null: the previous draft's rollback first, in the same kernel)
 // Token-by-token fp32 kernels (every built shape, bf16 or fp32 inputs):

@@ -180,8 +180,9 @@ int gdn_replay_flush(const gdn_replay_cache *c, int32_t num_reqs, const int32_t 
  * len[s] committed tokens into state[s], head[s] = (head[s] + len[s]) mod C and
  * len[s] = 0 (exactly as gdn_replay_flush); then verify the draft exactly as
  * gdn_replay_verify, from the resulting checkpoint, pointers and ring. Arguments
- * as for gdn_replay_verify plus min_len. Ring capacity <= 32 with bf16 inputs
- * and d_k = d_v in {64, 128} runs as one kernel; other shapes run the two calls
+ * as for gdn_replay_verify plus min_len. bf16 inputs with d_k = d_v in
+ * {64, 128} and D <= 32 run as one kernel (a replay of one chunk of 32 tokens
+ * for ring capacity <= 32, of several above); other shapes run the two calls
  * back to back on the stream.
  * Device errors: slot out of range -> SLOT; head or len out of range -> POINTER;
  * a slot that is not due with len + D > C -> CAPACITY. The request is skipped

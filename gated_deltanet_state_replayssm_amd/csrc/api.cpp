@@ -232,11 +232,14 @@ int gdn_replay_rollback_verify_flush(const gdn_replay_cache *c, int32_t num_reqs
   if (!num_accepted || !aligned(num_accepted, 4)) return GDN_EINVAL;
   if (prev_draft_lens && !aligned(prev_draft_lens, 4)) return GDN_EINVAL;
   const bool f32 = c->in_dtype == GDN_F32;
-  if (gdnr::fused_supported(c->d_k, c->d_v, f32, draft_len, c->ring_cap)) {
+  const bool one_chunk = gdnr::fused_supported(c->d_k, c->d_v, f32, draft_len, c->ring_cap);
+  if (one_chunk || gdnr::fused_long_supported(c->d_k, c->d_v, f32, draft_len, c->ring_cap)) {
     a.prev_accepted = num_accepted;
     a.prev_draft_lens = prev_draft_lens;
     a.prev_draft = prev_draft;
-    return gdnr::launch_verify_flush_fused(a, min_len, stream) == hipSuccess ? GDN_OK : GDN_EHIP;
+    const hipError_t e = one_chunk ? gdnr::launch_verify_flush_fused(a, min_len, stream)
+                                   : gdnr::launch_verify_flush_long(a, min_len, stream);
+    return e == hipSuccess ? GDN_OK : GDN_EHIP;
   }
   // Other shapes: the rollback, then verify_flush, as separate launches.
   st = rollback_impl(c, num_reqs, slot_idx, prev_draft, num_accepted, stream,

@@ -1764,7 +1764,7 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyA
 // slot's key and query rows (by the last workgroup of the key head to have
 // staged all its fold inputs) and the end-of-grid pointer move are those of
 // replay_fused.
-template <int DK, int DV, int NT, bool VARLEN>
+template <int DK, int DV, int NT, bool VARLEN, bool ROLLBACK>
 __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused_long(VerifyArgs va,
                                                                               int min_len) {
   constexpr int WAVES = DV / (16 * NT);
@@ -1791,14 +1791,14 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused_long(Ve
     return (uint32_t)((4 * ((t & 63) >> 4) * DV + (t / 64) * 16 * NT + NT * (t & 15)) * 4);
   };
   const int mn = max(min_len, 1);
-  const Req rq = ordered_request<false, VARLEN>(va, mn, blockIdx.x / HV, lane,
-                                                wave == 0 ? moves : nullptr);
+  const Req rq = ordered_request<ROLLBACK, VARLEN>(va, mn, blockIdx.x / HV, lane,
+                                                   wave == 0 ? moves : nullptr);
   const int r = rq.r, h = blockIdx.x % HV;
   const bool lead = (h == 0 && tid == 0);
   int32_t *grid_ctr = c.sync;
   int32_t *rank_ctr = slot_counter(c, blockIdx.x / HV);
   auto finish = [&]() {
-    end_of_grid<false, VARLEN>(va, rq, mn, rank_ctr, grid_ctr, moves, &grid_rank, tid);
+    end_of_grid<ROLLBACK, VARLEN>(va, rq, mn, rank_ctr, grid_ctr, moves, &grid_rank, tid);
   };
 
   const int s = rq.s;
@@ -1808,11 +1808,16 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused_long(Ve
     return;
   }
   const int C = c.cap;
-  const int head = rq.head, n = rq.len;
-  if (head < 0 || head >= C || n < 0 || n > C) {
+  const int head = rq.head, n = rq.len;  // n: after the folded rollback, if any
+  if (head < 0 || head >= C || rq.raw_len < 0 || rq.raw_len > C) {
     if (lead) raise_err(c.err, GDN_DERR_POINTER);
     finish();
     return;
+  }
+  if (ROLLBACK && lead) {  // the folded rollback's own error, as a rollback call would flag it
+    int bad;
+    rolled_len(va, r, rq.raw_len, C, &bad);
+    if (bad) raise_err(c.err, bad);
   }
   const int D = VARLEN ? request_draft(va.draft_lens, r, va.draft) : va.draft;
   if (VARLEN && D < 0) {
@@ -1976,17 +1981,24 @@ hipError_t launch_verify_flush_fused(const VerifyArgs &a, int min_len, hipStream
 hipError_t launch_verify_flush_long(const VerifyArgs &a, int min_len, hipStream_t stream) {
   constexpr int NT = 2;
   const dim3 grid(a.num_reqs * a.c.hv);
-  const bool varlen = a.draft_lens != nullptr;
-  if (a.prev_accepted || a.norm_q) return hipErrorInvalidValue;  // not taken here
+  const bool varlen = a.draft_lens != nullptr, rollback = a.prev_accepted != nullptr;
+  if (a.norm_q) return hipErrorInvalidValue;  // the norm rides on single-chunk replays only
   auto go = [&](auto kernel, int dv) {
     hipLaunchKernelGGL(kernel, grid, dim3(64 * (dv / (16 * NT))), 0, stream, a, min_len);
   };
+  auto pick = [&](auto dk) {
+    constexpr int D = decltype(dk)::value;
+    if (rollback)
+      varlen ? go(replay_fused_long<D, D, NT, true, true>, D)
+             : go(replay_fused_long<D, D, NT, false, true>, D);
+    else
+      varlen ? go(replay_fused_long<D, D, NT, true, false>, D)
+             : go(replay_fused_long<D, D, NT, false, false>, D);
+  };
   if (a.c.dk == 128)
-    varlen ? go(replay_fused_long<128, 128, NT, true>, 128)
-           : go(replay_fused_long<128, 128, NT, false>, 128);
+    pick(std::integral_constant<int, 128>());
   else if (a.c.dk == 64)
-    varlen ? go(replay_fused_long<64, 64, NT, true>, 64)
-           : go(replay_fused_long<64, 64, NT, false>, 64);
+    pick(std::integral_constant<int, 64>());
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

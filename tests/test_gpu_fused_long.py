@@ -115,3 +115,43 @@ def test_long_equals_flush_then_verify_bitwise():
         assert torch.equal(x, y), name
     assert not a.sync.any()
     assert int((a.len == 0).sum()) > 0
+
+
+@pytest.mark.parametrize("varlen", [False, True])
+def test_long_one_call_step(varlen):
+    """rollback_verify_flush at C = 80 (one kernel: the previous draft's
+    rollback, the chunked fold and the verify) against the oracle's rollback
+    then verify_flush; requests leaving and joining the batch."""
+    wl = synth.Workload("lstep", 6, 9, 8, 4, 128, 128, 80, 16, synth.BF16, 48, 2,
+                        "clipnormal:12:3", "uniform:0:64",
+                        "uniform:0:16" if varlen else "fixed")
+    say(f"case long one-call step varlen={varlen}")
+    pairs = run_schedule(wl, 6, 640 + varlen, layers=2, label="lstep", one_call=True)
+    assert sum(p.flushed_count for p in pairs) > 0
+
+
+def test_long_one_call_step_bitwise():
+    wl = W["r32_hv32_hk16_d128_f64"]
+    say("case long one-call step vs rollback + verify_flush, bitwise, C = 80")
+    rng = np.random.default_rng(650)
+    init = synth.make_cache_init(wl, rng, init_len=rng.integers(0, 49, wl.num_slots))
+    a = ReplayCache.from_numpy(init, wl.hv, wl.hk, wl.dk, wl.dv, wl.cap, wl.in_dtype)
+    b = ReplayCache.from_numpy(init, wl.hv, wl.hk, wl.dk, wl.dv, wl.cap, wl.in_dtype)
+    dr = {k: to_device(v) for k, v in synth.make_draft(wl, rng).items()}
+    slots = to_device(synth.make_slot_idx(wl, rng))
+    acc = to_device(rng.integers(0, wl.draft + 1, wl.num_reqs).astype(np.int32))
+    oa = a.rollback_verify_flush(slots, acc, wl.draft, 56, dr["q"], dr["k"], dr["v"],
+                                 dr["alpha"], dr["beta"])
+    b.rollback(slots, wl.draft, acc)
+    ob = b.verify_flush(slots, 56, dr["q"], dr["k"], dr["v"], dr["alpha"], dr["beta"])
+    torch.cuda.synchronize()
+    assert int(a.err.item()) == 0 and int(b.err.item()) == 0
+    assert torch.equal(oa.view(torch.int32), ob.view(torch.int32))
+    for name in ("state", "head", "len", "ring_k", "ring_v", "ring_alpha", "ring_beta", "ring_q"):
+        x, y = getattr(a, name), getattr(b, name)
+        if x.dtype == torch.float32:
+            x, y = x.view(torch.int32), y.view(torch.int32)
+        elif x.dtype == torch.bfloat16:
+            x, y = x.view(torch.int16), y.view(torch.int16)
+        assert torch.equal(x, y), name
+    assert not a.sync.any()

@@ -2,6 +2,8 @@
 // asynchronous launches on the caller's stream. No allocation, no host/device sync.
 #include <stdint.h>
 
+#include <climits>
+
 #include "internal.h"
 
 namespace {
@@ -10,6 +12,13 @@ using gdnr::CacheView;
 
 constexpr int32_t kMaxRingCap = 256;
 constexpr int32_t kMaxHeads = 4096;  // grid.y limit headroom
+// A dispatch counts the work-items of each grid dimension in 32 bits: the
+// replay kernels launch num_reqs * HV workgroups of (at most) 256 threads.
+constexpr int64_t kMaxWorkItems = INT32_MAX;
+
+bool replay_grid_ok(int64_t num_reqs, const gdn_replay_cache *c) {
+  return num_reqs * c->num_v_heads * 256 <= kMaxWorkItems;
+}
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -66,6 +75,7 @@ int verify_args(const gdn_replay_cache *c, int32_t num_reqs, const int32_t *slot
   if (st != GDN_OK) return st;
   if (num_reqs < 0 || num_reqs > c->num_slots) return GDN_EINVAL;
   if (draft_len < 1 || draft_len > c->ring_cap) return GDN_EINVAL;
+  if (!replay_grid_ok(num_reqs, c)) return GDN_EUNSUPPORTED;
   if (num_reqs == 0) return GDN_OK;
   if (!slot_idx || !q || !k || !v || !alpha || !beta || (!out && !out_optional))
     return GDN_EINVAL;
@@ -299,6 +309,7 @@ int gdn_replay_flush(const gdn_replay_cache *c, int32_t num_reqs, const int32_t 
   int st = check_cache(c);
   if (st != GDN_OK) return st;
   if (num_reqs < 0 || num_reqs > c->num_slots) return GDN_EINVAL;
+  if (!replay_grid_ok(num_reqs, c)) return GDN_EUNSUPPORTED;
   if (num_reqs == 0) return GDN_OK;
   if (!slot_idx || !aligned(slot_idx, 4)) return GDN_EINVAL;
   return launch_flush(c, flush_args(c, num_reqs, slot_idx, min_len), stream);
@@ -309,7 +320,8 @@ int gdn_gated_rmsnorm_fp8(int32_t rows, int32_t num_heads, int32_t d_v, const fl
                           hipStream_t stream) {
   if (rows < 0 || num_heads < 1 || d_v < 1) return GDN_EINVAL;
   if (!gdnr::norm_supported(d_v)) return GDN_EUNSUPPORTED;
-  if ((int64_t)rows * num_heads > (int64_t(1) << 33)) return GDN_EUNSUPPORTED;  // grid size
+  // 8 groups per workgroup of 256 threads: 32 work-items per group
+  if ((int64_t)rows * num_heads * 32 > kMaxWorkItems) return GDN_EUNSUPPORTED;
   if (!(eps > 0.f) || eps > 1.f) return GDN_EINVAL;  // also rejects NaN
   if (rows == 0) return GDN_OK;
   if (!o || !z || !weight || !q || !scale) return GDN_EINVAL;

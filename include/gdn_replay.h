@@ -32,6 +32,9 @@
  * can see (they depend on device-resident pointers) skip the offending
  * request with no writes at all and OR a GDN_DERR_* bit into *err (a sticky
  * word the caller clears). A failed kernel launch returns GDN_EHIP.
+ * Calls whose launch would exceed a dispatch's 32-bit work-item count return
+ * GDN_EUNSUPPORTED: num_reqs * HV * 256 must stay below 2^31 for the replay
+ * calls, rows * num_heads * 32 for gdn_gated_rmsnorm_fp8.
  */
 #ifndef GDN_REPLAY_H
 #define GDN_REPLAY_H

@@ -278,6 +278,19 @@ def test_conv_call_validation():
     assert call(num_reqs=0, x=None, conv_ring=None) == b.GDN_OK
 
 
+def test_grids_past_the_dispatch_limit_are_refused():
+    """num_reqs * HV workgroups of 256 threads must fit a dispatch's 32-bit
+    work-item count; the norm takes 32 work-items per (row, head) group."""
+    c = _cache(num_slots=1 << 20, num_v_heads=4096, num_k_heads=4096, d_k=64, d_v=64,
+               ring_cap=32)
+    assert _verify(c, num_reqs=2048) == b.GDN_EUNSUPPORTED      # 2048 * 4096 * 256 = 2^31
+    assert _verify_flush(c, num_reqs=2048) == b.GDN_EUNSUPPORTED
+    assert b.flush_raw(c, 2048, FAKE, 1, None) == b.GDN_EUNSUPPORTED
+    assert _verify(c, num_reqs=2047, q=None) == b.GDN_EINVAL    # within the limit: next check
+    assert b.gated_rmsnorm_fp8_raw(1 << 23, 8, 128, FAKE, FAKE, FAKE, 1e-6, FAKE, FAKE,
+                                   None) == b.GDN_EUNSUPPORTED  # 2^26 groups * 32 = 2^31
+
+
 def test_zero_requests_is_a_noop_without_launch():
     c = _cache()
     assert _verify(c, num_reqs=0, q=None, k=None) == b.GDN_OK

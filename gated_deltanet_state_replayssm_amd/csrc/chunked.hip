@@ -125,6 +125,17 @@ __device__ __forceinline__ void tok_operand(const f32x4 &m0, const f32x4 &m1, bf
   split8(x, hi, lo);
 }
 
+// Value head of the j-th workgroup of a request's HV consecutive workgroups.
+// Workgroups are dealt to the 8 XCDs in turn (block b on XCD b mod 8), and the G
+// value heads of a key head read the same key and query rows: when HV is a
+// multiple of 8 G they take positions 8 apart, so that they run on one XCD and
+// share its L2 (j = 8 (G a + b) + x -> key head 8 a + x, value head G kh + b).
+__device__ __forceinline__ int head_of(int j, int HV, int G) {
+  if (HV % (8 * G) != 0) return j;
+  const int x = j & 7, m = j >> 3, a = m / G, b = m - a * G;
+  return G * (8 * a + x) + b;
+}
+
 struct Unit {
   int r, h, s, kh, head, B, T, C;
 };
@@ -1067,7 +1078,7 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_chunked(Verif
 
   const CacheView &c = VERIFY ? va.c : fa.c;
   const int HV = c.hv;
-  const int r = blockIdx.x / HV, h = blockIdx.x % HV;
+  const int r = blockIdx.x / HV, h = head_of(blockIdx.x % HV, HV, HV / c.hk);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = (tid >> 4) & 3, l16 = tid & 15;  // bit fields of the thread index: cheap to recompute
   const bool lead = (h == 0 && tid == 0);
@@ -1232,7 +1243,7 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_single(Verify
 
   const CacheView &c = VERIFY ? va.c : fa.c;
   const int HV = c.hv;
-  const int r = blockIdx.x / HV, h = blockIdx.x % HV;
+  const int r = blockIdx.x / HV, h = head_of(blockIdx.x % HV, HV, HV / c.hk);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = (tid >> 4) & 3, l16 = tid & 15;  // bit fields of the thread index: cheap to recompute
   const int colL = wave * 16 * NT + NT * l16;
@@ -1615,7 +1626,7 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyA
   const int mn = max(min_len, 1);
   const Req rq = ordered_request<ROLLBACK, VARLEN>(va, mn, blockIdx.x / HV, lane,
                                                   wave == 0 ? moves : nullptr);
-  const int r = rq.r, h = blockIdx.x % HV;
+  const int r = rq.r, h = head_of(blockIdx.x % HV, HV, G);
   const bool lead = (h == 0 && tid == 0);
   int32_t *grid_ctr = c.sync;
   int32_t *rank_ctr = slot_counter(c, blockIdx.x / HV);
@@ -1793,7 +1804,7 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused_long(Ve
   const int mn = max(min_len, 1);
   const Req rq = ordered_request<ROLLBACK, VARLEN>(va, mn, blockIdx.x / HV, lane,
                                                    wave == 0 ? moves : nullptr);
-  const int r = rq.r, h = blockIdx.x % HV;
+  const int r = rq.r, h = head_of(blockIdx.x % HV, HV, G);
   const bool lead = (h == 0 && tid == 0);
   int32_t *grid_ctr = c.sync;
   int32_t *rank_ctr = slot_counter(c, blockIdx.x / HV);

@@ -137,3 +137,15 @@ def test_fused_stress_batch_sampled():
     pairs = run_schedule(wl, 4, synth.seed_for(wl.name, 0, 1), oracle_slots=sample,
                          label="c4f", fused=True)
     say(f"  worst {pairs[0].worst}")
+
+
+@pytest.mark.parametrize("hv,hk", [(64, 8), (64, 32), (16, 2)])
+def test_fused_gva_shapes_and_xcd_placement(hv, hk):
+    """Value heads per key head G = 8, 2, 8 at HV = 64, 64, 16: the workgroups of
+    a key head's value heads are placed 8 apart (one XCD) when HV is a multiple
+    of 8 G, in order otherwise; the fused and separate orders both checked."""
+    wl = synth.Workload("gva", 3, 4, hv, hk, 64, 64, 32, 8, synth.BF16, 16, 1,
+                        "clipnormal:6:2", "uniform:0:23")
+    say(f"case gva HV={hv} HK={hk}")
+    run_schedule(wl, 4, 660 + hv + hk, label=f"gva{hv}_{hk}", fused=True)
+    run_schedule(wl, 3, 670 + hv + hk, label=f"gvas{hv}_{hk}", fused=False)

@@ -36,8 +36,10 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
 // draft) with the loads issued together, then writes kTok outputs and appends
 // its kTok inputs. The K - 1 rows before a group are read by two groups (the
 // repeats are served by L2); the ring positions read (before the draft) never
-// meet those written (D + K - 1 <= C).
-constexpr int kTok = 8;
+// meet those written (D + K - 1 <= C). Groups of 4 tokens: measured against 2,
+// 8 and 16 (and against 2 or 4 channel pairs per thread), the most threads in
+// flight for the fewest repeated history reads.
+constexpr int kTok = 4;
 
 template <int K>
 __global__ __launch_bounds__(256) void causal_conv_update_kernel(ConvArgs a) {

@@ -1359,6 +1359,7 @@ struct Req {
   int r, s, head, len;  // len: committed count after the folded rollback, if any
   int raw_len;          // len as stored
   int due;              // number of due requests in the call
+  int roll_err;         // the folded rollback's error bit for this request (0: none)
 };
 
 // Committed count of request i once the accepted prefix of the previous draft
@@ -1366,18 +1367,22 @@ struct Req {
 // length is in [0, prev_draft], a in [0, that length] and len + a <= C;
 // otherwise len, with the rollback's error bit in *bad (as a separate rollback
 // call would skip the request and flag it).
-__device__ __forceinline__ int rolled_len(const VerifyArgs &va, int i, int len, int cap,
-                                          int *bad) {
-  const int bound = va.prev_draft_lens ? va.prev_draft_lens[i] : va.prev_draft;
-  const int a = va.prev_accepted[i];
+__device__ __forceinline__ int rolled_from(int len, int a, int bound, int prev_draft, int cap,
+                                           int *bad) {
   *bad = 0;
-  if (bound < 0 || bound > va.prev_draft)
+  if (bound < 0 || bound > prev_draft)
     *bad = GDN_DERR_DRAFT;
   else if (a < 0 || a > bound)
     *bad = GDN_DERR_ACCEPT;
   else if (len + a > cap)
     *bad = GDN_DERR_CAPACITY;
   return *bad ? len : len + a;
+}
+
+__device__ __forceinline__ int rolled_len(const VerifyArgs &va, int i, int len, int cap,
+                                          int *bad) {
+  const int bound = va.prev_draft_lens ? va.prev_draft_lens[i] : va.prev_draft;
+  return rolled_from(len, va.prev_accepted[i], bound, va.prev_draft, cap, bad);
 }
 
 // The pointer move of one request at the end of the call: slot (-1: none), new
@@ -1407,14 +1412,26 @@ __device__ Req ordered_request(const VerifyArgs &va, int mn, int q, int lane, Mo
     int bad;
     return rolled_len(va, i, n, c.cap, &bad);
   };
+  // the folded rollback's inputs of request i, loaded beside slot_idx[i] (they
+  // do not depend on the slot), and the committed count they give
+  auto roll_in = [&](int i, int *a, int *bound) {
+    *a = va.prev_accepted[i];
+    *bound = va.prev_draft_lens ? va.prev_draft_lens[i] : va.prev_draft;
+  };
+  auto eff_from = [&](int h, int n, int a, int bound, int *bad) {
+    *bad = 0;
+    if (!ROLLBACK || h < 0 || h >= c.cap || n < 0 || n > c.cap) return n;
+    return rolled_from(n, a, bound, va.prev_draft, c.cap, bad);
+  };
   if (R <= 64) {
-    int si = -1, hi = 0, ni = 0, ne = 0;
+    int si = -1, hi = 0, ni = 0, ne = 0, ai = 0, bi = 0, bad = 0;
     if (lane < R) {
+      if constexpr (ROLLBACK) roll_in(lane, &ai, &bi);
       si = va.slot_idx[lane];
       if (si >= 0 && si < c.num_slots) {
         hi = c.head[si];
         ni = c.len[si];
-        ne = eff(lane, hi, ni);
+        ne = eff_from(hi, ni, ai, bi, &bad);
       }
     }
     const uint64_t dm = __ballot(si >= 0 && si < c.num_slots && ne >= mn);
@@ -1432,28 +1449,35 @@ __device__ Req ordered_request(const VerifyArgs &va, int mn, int q, int lane, Mo
     }
     const int nd = __popcll(dm);
     const int r = q < nd ? nth_bit(dm, q) : nth_bit(~dm & lanes(0), q - nd);
-    return Req{r, __builtin_amdgcn_readlane(si, r), __builtin_amdgcn_readlane(hi, r),
-               __builtin_amdgcn_readlane(ne, r), __builtin_amdgcn_readlane(ni, r), nd};
+    return Req{r,
+               __builtin_amdgcn_readlane(si, r),
+               __builtin_amdgcn_readlane(hi, r),
+               __builtin_amdgcn_readlane(ne, r),
+               __builtin_amdgcn_readlane(ni, r),
+               nd,
+               ROLLBACK ? __builtin_amdgcn_readlane(bad, r) : 0};
   }
   // Up to 4 rounds of 64: every lane keeps its requests' slot and pointers, so
   // the chosen request's come from a readlane instead of reloads, and each
   // round's loads are issued once.
   constexpr int kRounds = 4;
   if (R <= 64 * kRounds) {
-    int si[kRounds], hi[kRounds], ni[kRounds], ne[kRounds];
+    int si[kRounds], hi[kRounds], ni[kRounds], ne[kRounds], bad[kRounds];
     uint64_t dm[kRounds];
     int nd = 0;
 #pragma unroll
     for (int j = 0; j < kRounds; ++j) {
       const int i = 64 * j + lane;
       si[j] = -1;
-      hi[j] = ni[j] = ne[j] = 0;
+      hi[j] = ni[j] = ne[j] = bad[j] = 0;
       if (i < R) {
+        int ai = 0, bi = 0;
+        if constexpr (ROLLBACK) roll_in(i, &ai, &bi);
         si[j] = va.slot_idx[i];
         if (si[j] >= 0 && si[j] < c.num_slots) {
           hi[j] = c.head[si[j]];
           ni[j] = c.len[si[j]];
-          ne[j] = eff(i, hi[j], ni[j]);
+          ne[j] = eff_from(hi[j], ni[j], ai, bi, &bad[j]);
         }
       }
       dm[j] = __ballot(si[j] >= 0 && si[j] < c.num_slots && ne[j] >= mn);
@@ -1461,7 +1485,7 @@ __device__ Req ordered_request(const VerifyArgs &va, int mn, int q, int lane, Mo
     }
     const bool want_due = q < nd;
     int left = want_due ? q : q - nd;
-    Req o{0, -1, 0, 0, 0, nd};
+    Req o{0, -1, 0, 0, 0, nd, 0};
     bool found = false;
 #pragma unroll
     for (int j = 0; j < kRounds; ++j) {
@@ -1475,6 +1499,7 @@ __device__ Req ordered_request(const VerifyArgs &va, int mn, int q, int lane, Mo
         o.head = __builtin_amdgcn_readlane(hi[j], l);
         o.len = __builtin_amdgcn_readlane(ne[j], l);
         o.raw_len = __builtin_amdgcn_readlane(ni[j], l);
+        if constexpr (ROLLBACK) o.roll_err = __builtin_amdgcn_readlane(bad[j], l);
         found = true;
       } else if (!found) {
         left -= cnt;
@@ -1507,11 +1532,13 @@ __device__ Req ordered_request(const VerifyArgs &va, int mn, int q, int lane, Mo
     }
     left -= cnt;
   }
-  Req o{r, va.slot_idx[r], 0, 0, 0, nd};
+  Req o{r, va.slot_idx[r], 0, 0, 0, nd, 0};
   if (o.s >= 0 && o.s < c.num_slots) {
     o.head = c.head[o.s];
     o.raw_len = c.len[o.s];
-    o.len = eff(r, o.head, o.raw_len);
+    o.len = o.raw_len;
+    if (ROLLBACK && o.head >= 0 && o.head < c.cap && o.raw_len >= 0 && o.raw_len <= c.cap)
+      o.len = rolled_len(va, r, o.raw_len, c.cap, &o.roll_err);
   }
   return o;
 }
@@ -1649,11 +1676,8 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyA
     finish();
     return;
   }
-  if (ROLLBACK && lead) {  // the folded rollback's own error, as a rollback call would flag it
-    int bad;
-    rolled_len(va, r, rq.raw_len, C, &bad);
-    if (bad) raise_err(c.err, bad);
-  }
+  // the folded rollback's own error, as a rollback call would flag it
+  if (ROLLBACK && lead && rq.roll_err) raise_err(c.err, rq.roll_err);
   // this request's draft length (the per-request lengths are a separate
   // instantiation, so that the fixed-length kernel carries none of their code)
   const int D = VARLEN ? request_draft(va.draft_lens, r, va.draft) : va.draft;
@@ -1825,11 +1849,8 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused_long(Ve
     finish();
     return;
   }
-  if (ROLLBACK && lead) {  // the folded rollback's own error, as a rollback call would flag it
-    int bad;
-    rolled_len(va, r, rq.raw_len, C, &bad);
-    if (bad) raise_err(c.err, bad);
-  }
+  // the folded rollback's own error, as a rollback call would flag it
+  if (ROLLBACK && lead && rq.roll_err) raise_err(c.err, rq.roll_err);
   const int D = VARLEN ? request_draft(va.draft_lens, r, va.draft) : va.draft;
   if (VARLEN && D < 0) {
     if (lead) raise_err(c.err, GDN_DERR_DRAFT);

@@ -45,14 +45,16 @@ def _eager_work():
     torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("workload", ["r32_hv32_hk16_d128_f16", "r32_hv32_hk16_d128_f64"])
 @pytest.mark.parametrize("path", ["fused", "step"])
-def test_replay_graph_matches_eager(path):
+def test_replay_graph_matches_eager(path, workload):
     """32 requests x 32 heads, 6 replays: the draft, the slot permutation and
-    the accept counts change at every replay; flushes fall due on the way."""
-    wl = W["r32_hv32_hk16_d128_f16"]
+    the accept counts change at every replay; flushes fall due on the way
+    (ring capacity 32: one-chunk replays; 80: several chunks)."""
+    wl = W[workload]
     D, F = wl.draft, wl.flush_min_len
-    say(f"case graph replay {path}, r32")
-    rng = np.random.default_rng(800 + (path == "step"))
+    say(f"case graph replay {path}, {workload}")
+    rng = np.random.default_rng(800 + (path == "step") + 10 * (wl.cap > 32))
     init = synth.make_cache_init(wl, rng)
     a = ReplayCache.from_numpy(init, wl.hv, wl.hk, wl.dk, wl.dv, wl.cap, wl.in_dtype)
     b = ReplayCache.from_numpy(init, wl.hv, wl.hk, wl.dk, wl.dv, wl.cap, wl.in_dtype)

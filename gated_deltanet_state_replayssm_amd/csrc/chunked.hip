@@ -499,6 +499,8 @@ __device__ __forceinline__ void decay_tiles(const float *lg, int g, int l16, flo
 // in sm.lgc), so the two run side by side; it writes only sm.Cm and sm.lgc.
 template <int DK, int DV>
 __device__ __forceinline__ void build_c(Smem<DK, DV> &sm, float al_staged, int lane, int g, int l16) {
+  // issue priority meanwhile, as build_tt
+  __builtin_amdgcn_s_setprio(3);
   {
     const Decay d = chunk_decay(al_staged);
     if (lane < kCh) sm.lgc[lane] = d.lg;
@@ -518,6 +520,7 @@ __device__ __forceinline__ void build_c(Smem<DK, DV> &sm, float al_staged, int l
       if (b < 3) c = Lv[b < 3 ? b : 0][i] * Pm[b < 3 ? b : 0][i];
       sm.Cm[t][j] = c;
     }
+  __builtin_amdgcn_s_setprio(0);
 }
 
 // A = beta L o (K K^T) strictly lower, then (I + A)^-1 in sm.T, plus the decay vectors
@@ -526,6 +529,9 @@ __device__ __forceinline__ void build_c(Smem<DK, DV> &sm, float al_staged, int l
 // alpha, of token lane % 32.
 template <int DK, int DV>
 __device__ __forceinline__ void build_tt(Smem<DK, DV> &sm, float al_staged, int lane, int g, int l16) {
+  // The T x T matrices are one wave's work on every workgroup's critical path;
+  // the wave takes issue priority over the other waves of its SIMD meanwhile.
+  __builtin_amdgcn_s_setprio(3);
   {
     const Decay d = chunk_decay(al_staged);
     if (lane < kCh) {
@@ -679,6 +685,7 @@ __device__ __forceinline__ void build_tt(Smem<DK, DV> &sm, float al_staged, int 
     for (int i = 0; i < 4; ++i) sm.T[16 + 4 * g + i][l16] = -T1[i];
   }
   
+  __builtin_amdgcn_s_setprio(0);
 }
 
 

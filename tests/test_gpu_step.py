@@ -134,14 +134,16 @@ def test_step_equals_rollback_then_verify_flush_bitwise(varlen):
     assert int((a.len == 0).sum()) > 0       # some slots were flushed
 
 
+@pytest.mark.parametrize("C", [32, 48])
 @pytest.mark.parametrize("R", [65, 200, 300])
-def test_step_ordering_rounds(R):
+def test_step_ordering_rounds(R, C):
     """More than 64 requests: the ordering pass in rounds of 64 with every
     round's values kept in lanes (up to 256 requests), and in reloaded rounds
-    beyond; bad slots and pointers in the batch."""
-    wl = synth.Workload("rounds", R, R + 20, 2, 1, 64, 64, 32, 8, synth.BF16, 16, 1,
+    beyond; bad slots and pointers in the batch; one-chunk (C = 32) and
+    multi-chunk (C = 48) replays."""
+    wl = synth.Workload("rounds", R, R + 20, 2, 1, 64, 64, C, 8, synth.BF16, 16, 1,
                         "clipnormal:6:3", "uniform:0:23")
-    say(f"case step ordering rounds R={R}")
+    say(f"case step ordering rounds R={R} C={C}")
     rng = np.random.default_rng(740 + R)
     init = synth.make_cache_init(wl, rng)
     init["head"][3] = 77                       # POINTER for whoever gets slot 3

@@ -48,7 +48,9 @@ if ROOT not in sys.path:
 
 METRIC = "GDN replay verify+flush us/layer and HBM GB/s (% roofline) at 32 reqs"
 HBM_PEAK_GBPS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "gated_deltanet_state_replayssm_amd", "csrc", "chunked.hip")
+# the sources of the replay kernels whose HBM bytes a profile summary records
+KERNEL_SRCS = [os.path.join(ROOT, "gated_deltanet_state_replayssm_amd", "csrc", f)
+               for f in ("chunk_ops.h", "chunked.hip", "fused.hip")]
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -60,7 +62,10 @@ def measured_traffic(kernel: str):
     import glob
     import hashlib
     import re
-    sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        h.update(open(path, "rb").read())
+    sha = h.hexdigest()[:16]
     for path in sorted(glob.glob(os.path.join(PROFILES, "*.md"))):
         for line in open(path):
             m = re.search(r"traffic source_sha=(\w+)((?: \w+_mb_per_launch=[\d.]+)+)", line)

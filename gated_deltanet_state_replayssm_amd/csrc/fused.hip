@@ -716,6 +716,10 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused_long(Ve
     finish();
     return;
   }
+  // opaque past the checks: value facts drawn from them made the register
+  // allocation of the chunk loop spill
+  int Dq = D;
+  asm volatile("" : "+s"(Dq));
   const int kh = h / G;
   const Rsrc st = make_rsrc(c.state + ((int64_t)s * HV + h) * DK * DV, DK * DV * 4);
   int32_t *group_ctr = group_counter(c, s, kh);
@@ -729,7 +733,7 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused_long(Ve
   // all folded (its state is then written and the draft verified from it as a
   // stream of its own, B = 0); any other slot's is the n tokens and the draft,
   // whose last chunk is the output chunk.
-  const Unit u1{r, h, s, kh, head, n, due ? n : n + D, C};
+  const Unit u1{r, h, s, kh, head, n, due ? n : n + Dq, C};
   const Srcs s1 = due ? make_srcs<DK, DV>(c, u1, nullptr, false)
                       : make_srcs<DK, DV>(c, u1, &va, true);
   const int nch = (u1.T + kCh - 1) / kCh, T0 = u1.T - kCh * (nch - 1);
@@ -780,9 +784,9 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused_long(Ve
   if (due) {
     store_state<DK, DV, NT>(st, st_off_of(), H);
     const int hd = head + n - (head + n >= C ? C : 0);
-    uo = Unit{r, h, s, kh, hd, 0, D, C};
+    uo = Unit{r, h, s, kh, hd, 0, Dq, C};
     t0 = 0;
-    Treal = D;
+    Treal = Dq;
   }
   const Srcs so = due ? make_srcs<DK, DV>(c, uo, &va, true) : s1;
   if (!out0) {
@@ -802,7 +806,7 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused_long(Ve
     contract<DK, DV, NT, kY | kZ>(sm, H, g, l16, Y, Z);
     solve_w<DK, DV, NT>(sm, Y, col_of(), g, l16, Wm);
     emit_outputs<DK, DV, NT>(sm, Z, Wm, g, l16, t0, Treal, uo.B,
-                             out_rsrc(va, r, h, DV, max(D, 1)), col_of() * 4, HV * DV * 4);
+                             out_rsrc(va, r, h, DV, max(Dq, 1)), col_of() * 4, HV * DV * 4);
   }
   const bool kq_writer = due ? group_rank == G - 1 : h % G == 0;
   // the draft rows, from LDS, with the thread mapping of the stage that wrote them

@@ -1,5 +1,6 @@
 """HIP-graph capture of the calls that are replayed from graphs (verify_flush +
-rollback, rollback_verify_flush, gated RMSNorm + FP8, the causal convolution):
+rollback, rollback_verify_flush, the step with the gated RMSNorm + FP8 in its
+epilogue, gated RMSNorm + FP8, the causal convolution):
 each graph is replayed several times with new inputs copied into its buffers,
 with eager work and synchronisations between the replays, and every replay is
 compared bit for bit with the same calls made eagerly on a twin."""
@@ -97,6 +98,69 @@ def test_replay_graph_matches_eager(path, workload):
         _eager_work()
         flushed += int((a.head != head_before).sum())   # a flush moves head
         _same(out_a, out_b, f"out, replay {step}")
+        for name in CACHE_FIELDS:
+            _same(getattr(a, name), getattr(b, name), f"{name}, replay {step}")
+        assert int(a.err.item()) == 0
+    assert flushed > 0
+    del g
+
+
+@pytest.mark.parametrize("write_out", [True, False])
+def test_step_norm_graph_matches_eager(write_out):
+    """gdn_replay_step_norm_fp8 at 32 requests x 32 heads, 5 replays with a new
+    draft, gate, slot permutation and accept counts each time; out written or
+    left out (codes and scales only)."""
+    wl = W["r32_hv32_hk16_d128_f16"]
+    D, F = wl.draft, wl.flush_min_len
+    say(f"case graph replay step_norm, write_out={write_out}")
+    rng = np.random.default_rng(805 + write_out)
+    init = synth.make_cache_init(wl, rng)
+    a = ReplayCache.from_numpy(init, wl.hv, wl.hk, wl.dk, wl.dv, wl.cap, wl.in_dtype)
+    b = ReplayCache.from_numpy(init, wl.hv, wl.hk, wl.dk, wl.dv, wl.cap, wl.in_dtype)
+    names = ("q", "k", "v", "alpha", "beta")
+    R, HV, dv = wl.num_reqs, wl.hv, wl.dv
+    buf = {k: to_device(v) for k, v in synth.make_draft(wl, rng).items()}
+    slots_buf = to_device(synth.make_slot_idx(wl, rng))
+    acc_buf = torch.zeros(R, dtype=torch.int32, device="cuda")
+    z_buf = torch.zeros((R, D, HV, dv), dtype=torch.bfloat16, device="cuda")
+    w = to_device(rng.uniform(0.5, 1.5, dv).astype(np.float32))
+    mk = lambda: (torch.empty((R, D, HV, dv), dtype=torch.float32, device="cuda"),
+                  torch.empty((R, D, HV, dv), dtype=torch.uint8, device="cuda"),
+                  torch.empty((R, D, HV), dtype=torch.float32, device="cuda"))
+    out_a, q_a, s_a = mk()
+    out_b, q_b, s_b = mk()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        b.step_norm_fp8(slots_buf, acc_buf, D, F, *(buf[x] for x in names), z_buf, w, 1e-6,
+                        out=out_b if write_out else None, codes=q_b, scale=s_b,
+                        write_out=write_out)
+    torch.cuda.synchronize()
+    prev = {}
+    flushed = 0
+    for step in range(5):
+        slots = synth.make_slot_idx(wl, rng)
+        acc = synth.sample_accepted(wl, rng)
+        acc_now = np.array([prev.get(int(s), 0) for s in slots], np.int32)
+        dr = {k: to_device(v) for k, v in synth.make_draft(wl, rng).items()}
+        z = torch.randn((R, D, HV, dv), device="cuda").to(torch.bfloat16)
+        sd = to_device(slots)
+        head_before = a.head.clone()
+        a.step_norm_fp8(sd, to_device(acc_now), D, F, *(dr[x] for x in names), z, w, 1e-6,
+                        out=out_a if write_out else None, codes=q_a, scale=s_a,
+                        write_out=write_out)
+        prev = {int(s): int(acc[i]) for i, s in enumerate(slots)}
+        slots_buf.copy_(sd)
+        acc_buf.copy_(to_device(acc_now))
+        z_buf.copy_(z)
+        for x in names:
+            buf[x].copy_(dr[x])
+        g.replay()
+        _eager_work()
+        flushed += int((a.head != head_before).sum())
+        if write_out:
+            _same(out_a, out_b, f"out, replay {step}")
+        _same(q_a, q_b, f"codes, replay {step}")
+        _same(s_a, s_b, f"scales, replay {step}")
         for name in CACHE_FIELDS:
             _same(getattr(a, name), getattr(b, name), f"{name}, replay {step}")
         assert int(a.err.item()) == 0

@@ -105,6 +105,62 @@ def test_replay_graph_matches_eager(path, workload):
     del g
 
 
+def test_step_varlen_graph_matches_eager():
+    """rollback_verify_flush with per-request lengths for the previous and the
+    current draft (zeros included), both read from device buffers that change
+    between replays; 32 requests x 32 heads, 6 replays."""
+    wl = W["r32_hv32_hk16_d128_f16"]
+    D, F = wl.draft, wl.flush_min_len
+    say("case graph replay step, per-request lengths")
+    rng = np.random.default_rng(807)
+    init = synth.make_cache_init(wl, rng)
+    a = ReplayCache.from_numpy(init, wl.hv, wl.hk, wl.dk, wl.dv, wl.cap, wl.in_dtype)
+    b = ReplayCache.from_numpy(init, wl.hv, wl.hk, wl.dk, wl.dv, wl.cap, wl.in_dtype)
+    names = ("q", "k", "v", "alpha", "beta")
+    R = wl.num_reqs
+    buf = {k: to_device(v) for k, v in synth.make_draft(wl, rng).items()}
+    slots_buf = to_device(synth.make_slot_idx(wl, rng))
+    acc_buf = torch.zeros(R, dtype=torch.int32, device="cuda")
+    plen_buf = torch.zeros(R, dtype=torch.int32, device="cuda")
+    len_buf = torch.zeros(R, dtype=torch.int32, device="cuda")
+    out_a = torch.zeros((R, D, wl.hv, wl.dv), dtype=torch.float32, device="cuda")
+    out_b = torch.zeros_like(out_a)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        b.rollback_verify_flush(slots_buf, acc_buf, D, F, *(buf[x] for x in names), out=out_b,
+                                prev_draft_lens=plen_buf, draft_lens=len_buf)
+    torch.cuda.synchronize()
+    prev = {}                      # slot -> (accepted, length) of its last draft
+    flushed = 0
+    for step in range(6):
+        slots = synth.make_slot_idx(wl, rng)
+        lens = rng.integers(0, D + 1, R).astype(np.int32)
+        acc = synth.sample_accepted(wl, rng, draft_lens=lens)
+        pa = np.array([prev.get(int(s), (0, 0))[0] for s in slots], np.int32)
+        pl = np.array([prev.get(int(s), (0, 0))[1] for s in slots], np.int32)
+        dr = {k: to_device(v) for k, v in synth.make_draft(wl, rng).items()}
+        sd = to_device(slots)
+        head_before = a.head.clone()
+        a.rollback_verify_flush(sd, to_device(pa), D, F, *(dr[x] for x in names), out=out_a,
+                                prev_draft_lens=to_device(pl), draft_lens=to_device(lens))
+        prev = {int(s): (int(acc[i]), int(lens[i])) for i, s in enumerate(slots)}
+        slots_buf.copy_(sd)
+        acc_buf.copy_(to_device(pa))
+        plen_buf.copy_(to_device(pl))
+        len_buf.copy_(to_device(lens))
+        for x in names:
+            buf[x].copy_(dr[x])
+        g.replay()
+        _eager_work()
+        flushed += int((a.head != head_before).sum())
+        _same(out_a, out_b, f"out, replay {step}")
+        for name in CACHE_FIELDS:
+            _same(getattr(a, name), getattr(b, name), f"{name}, replay {step}")
+        assert int(a.err.item()) == 0
+    assert flushed > 0
+    del g
+
+
 @pytest.mark.parametrize("write_out", [True, False])
 def test_step_norm_graph_matches_eager(write_out):
     """gdn_replay_step_norm_fp8 at 32 requests x 32 heads, 5 replays with a new

@@ -740,19 +740,20 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused_long(Ve
   const int nfold = due ? nch : nch - 1;
   const bool out0 = !due && nch == 1;  // chunk 0 is the output chunk
   {
-    // waves SW.. load their state first; waves 0..SW-1 stage chunk 0, then load
-    Stage<DK, DV, NT, true, 64 * SW> sg0;
-    if (wave >= SW) {
-      load_state<DK, DV, NT>(st, st_off_of(), H);
-      al = 1.f;
-    } else {
+    // waves SW.. load their state first; waves 0..SW-1 stage chunk 0, then load.
+    // One load_state for both, so that the state is assigned its registers once
+    // (two call sites met at the chunk loop with two assignments, and the
+    // copies between them spilled).
+    al = 1.f;
+    if (wave < SW) {
+      Stage<DK, DV, NT, true, 64 * SW> sg0;
       sg0.load(s1, u1, 0, T0, out0);
       sg0.store(sm, T0, out0);
       al = sg0.al;
-      __builtin_amdgcn_sched_barrier(0);
-      load_state<DK, DV, NT>(st, st_off_of(), H);
-      __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    load_state<DK, DV, NT>(st, st_off_of(), H);
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
   }
   // The thread index comes through an opaque copy so that the per-thread row

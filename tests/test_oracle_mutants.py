@@ -8,7 +8,10 @@ grouping, a wrong pointer move at flush.
 import numpy as np
 import pytest
 
+from gated_deltanet_state_replayssm_amd import synth
+from oracle import conv_oracle as co
 from oracle import gdn_oracle as go
+from tests import test_bf16_format as fmtpins
 from tests import test_bookkeeping as bkpins
 from tests import test_oracle as pins
 
@@ -34,6 +37,11 @@ PIN_TESTS = [
     lambda: pins.test_error_bits_and_skips(),
     lambda: bkpins.test_pointer_walk_on_oracle(),
     lambda: bkpins.test_committed_window_holds_accepted_tokens_in_order(),
+    lambda: fmtpins.test_bf16_decode_table(),
+    lambda: fmtpins.test_bf16_decode_exhaustive(),
+    lambda: fmtpins.test_bf16_encode_ties_and_carries(),
+    lambda: fmtpins.test_bf16_encode_is_nearest_even_brute_force(),
+    lambda: fmtpins.test_conv_silu_closed_forms(),
 ]
 
 
@@ -100,6 +108,38 @@ def _verify_output_before_update(self, slot_idx, q, k, v, alpha, beta, draft_len
     return np.concatenate([out[:, :1] * 0.0 + out[:, :1], out[:, :-1]], axis=1)
 
 
+def _bf16_shift15(bits):
+    u32 = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(15)
+    return u32.view(np.float32).astype(np.float64)
+
+
+def _bf16_as_fp16(bits):
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def _rne_ties_away(x):
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((b + 0x8000) >> 16).astype(np.uint16)
+
+
+def _rne_truncate(x):
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    return (b >> 16).astype(np.uint16)
+
+
+def _silu_sign(x):
+    return x / (1.0 + np.exp(x))
+
+
+# (module, attribute, replacement) of the number-format helpers
+FORMAT_MUTANTS = {
+    "bf16_decode_shift15": (go, "bf16_bits_to_f64", _bf16_shift15),
+    "bf16_decode_as_fp16": (go, "bf16_bits_to_f64", _bf16_as_fp16),
+    "bf16_encode_ties_away": (synth, "f32_to_bf16_bits", _rne_ties_away),
+    "bf16_encode_truncates": (synth, "f32_to_bf16_bits", _rne_truncate),
+    "conv_silu_sign": (co, "silu", _silu_sign),
+}
+
 MUTANTS = {
     "output_transposed": ("gdn_output", _output_transposed, None),
     "rank1_drops_alpha": ("gdn_step", _step_no_alpha_in_correction, None),
@@ -124,6 +164,20 @@ def test_mutant_is_caught(name, monkeypatch):
     for t in PIN_TESTS:
         try:
             t()
+        except AssertionError:
+            failures += 1
+    assert failures > 0, f"mutant {name} passed every pin"
+
+
+@pytest.mark.parametrize("name", sorted(FORMAT_MUTANTS))
+def test_format_mutant_is_caught(name, monkeypatch):
+    mod, attr, fn = FORMAT_MUTANTS[name]
+    monkeypatch.setattr(mod, attr, fn)
+    failures = 0
+    for t in PIN_TESTS:
+        try:
+            with np.errstate(all="ignore"):
+                t()
         except AssertionError:
             failures += 1
     assert failures > 0, f"mutant {name} passed every pin"

@@ -42,7 +42,7 @@ class GdnReplayCache(ctypes.Structure):
         ("d_v", ctypes.c_int32),
         ("ring_cap", ctypes.c_int32),
         ("in_dtype", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("sync_len", ctypes.c_int32),
         ("state", ctypes.c_void_p),
         ("ring_q", ctypes.c_void_p),
         ("ring_k", ctypes.c_void_p),

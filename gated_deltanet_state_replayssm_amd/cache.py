@@ -105,7 +105,8 @@ class ReplayCache:
             p = lambda t: None if t is None else t.data_ptr()
             self._struct = binding.GdnReplayCache(
                 self.num_slots, self.hv, self.hk, self.dk, self.dv, self.cap,
-                binding.GDN_BF16 if self.in_dtype == BF16 else binding.GDN_F32, 0,
+                binding.GDN_BF16 if self.in_dtype == BF16 else binding.GDN_F32,
+                self.sync.numel(),
                 p(self.state), p(self.ring_q), p(self.ring_k), p(self.ring_v),
                 p(self.ring_alpha), p(self.ring_beta), p(self.head), p(self.len),
                 p(self.sync), p(self.err))

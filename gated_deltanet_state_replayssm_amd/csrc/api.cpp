@@ -36,6 +36,10 @@ int check_cache(const gdn_replay_cache *c) {
   if (!c->state || !c->ring_k || !c->ring_v || !c->ring_alpha || !c->ring_beta || !c->head ||
       !c->len || !c->sync)
     return GDN_EINVAL;
+  // the counter buffer must hold every counter a launch may touch
+  const int64_t need = gdnr::sync_entries(c->num_slots, c->num_k_heads);
+  if (need > INT32_MAX) return GDN_EUNSUPPORTED;
+  if (c->sync_len < need) return GDN_EINVAL;
   if (!aligned(c->state, 16) || !aligned(c->ring_k, 16) || !aligned(c->ring_v, 16) ||
       (c->ring_q && !aligned(c->ring_q, 16)) || !aligned(c->ring_alpha, 4) ||
       !aligned(c->ring_beta, 4) || !aligned(c->head, 4) || !aligned(c->len, 4) ||

@@ -43,7 +43,7 @@ namespace gdnr {
 namespace {
 
 
-constexpr int kCh = 32;    // tokens per chunk
+constexpr int kCh = kChunkTokens;  // tokens per chunk
 constexpr int kPadK = 8;   // bf16 padding per token row of K / Q in LDS
 constexpr int kPadT = 8;   // bf16 padding per row of K^T
 constexpr int kPadF = 4;   // fp32 padding per row of the 32 x 32 matrices

@@ -310,10 +310,6 @@ hipError_t launch_t(const VerifyArgs &va, const FlushArgs &fa, int num_reqs, int
 
 }  // namespace
 
-bool chunked_supported(int dk, int dv, bool in_f32, int draft) {
-  return !in_f32 && dk == dv && (dk == 64 || dk == 128) && draft <= kCh;
-}
-
 hipError_t launch_verify_chunked(const VerifyArgs &a, hipStream_t stream) {
   FlushArgs none{};
   const int R = a.num_reqs, HV = a.c.hv, C = a.c.cap;

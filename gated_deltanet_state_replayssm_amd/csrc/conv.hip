@@ -22,7 +22,7 @@ namespace gdnr {
 
 namespace {
 
-constexpr int kMaxWidth = 8;
+constexpr int kMaxWidth = kMaxConvWidth;
 
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
   const uint32_t u = __float_as_uint(f);
@@ -123,8 +123,6 @@ hipError_t launch_k(const ConvArgs &a, hipStream_t stream) {
 }
 
 }  // namespace
-
-bool conv_width_supported(int k) { return k >= 1 && k <= kMaxWidth; }
 
 hipError_t launch_causal_conv_update(const ConvArgs &a, int width, hipStream_t stream) {
   switch (width) {

@@ -880,12 +880,4 @@ hipError_t launch_verify_flush_long(const VerifyArgs &a, int min_len, hipStream_
   return hipGetLastError();
 }
 
-bool fused_long_supported(int dk, int dv, bool in_f32, int draft, int cap) {
-  return chunked_supported(dk, dv, in_f32, draft) && cap > kCh;
-}
-
-bool fused_supported(int dk, int dv, bool in_f32, int draft, int cap) {
-  return chunked_supported(dk, dv, in_f32, draft) && cap <= kCh;
-}
-
 }  // namespace gdnr

@@ -76,15 +76,26 @@ struct FlushArgs {
   int32_t max_draft;
 };
 
+// Tokens per chunk of the chunked (MFMA) replay kernels, and the widest causal
+// convolution built.
+constexpr int kChunkTokens = 32;
+constexpr int kMaxConvWidth = 8;
+
 // Launchers return hipSuccess or the launch error. in_f32 selects fp32 inputs.
 // Chunked MFMA kernels (bf16 inputs, d_k = d_v in {64, 128}, draft <= 32):
-bool chunked_supported(int dk, int dv, bool in_f32, int draft);
+inline bool chunked_supported(int dk, int dv, bool in_f32, int draft) {
+  return !in_f32 && dk == dv && (dk == 64 || dk == 128) && draft <= kChunkTokens;
+}
 hipError_t launch_verify_chunked(const VerifyArgs &a, hipStream_t stream);
 hipError_t launch_flush_chunked(const FlushArgs &a, hipStream_t stream);
 // Flush fused into verify in one kernel (chunked shapes, ring capacity <= 32).
-bool fused_supported(int dk, int dv, bool in_f32, int draft, int cap);
+inline bool fused_supported(int dk, int dv, bool in_f32, int draft, int cap) {
+  return chunked_supported(dk, dv, in_f32, draft) && cap <= kChunkTokens;
+}
 // The same for replays of several chunks (ring capacity above 32).
-bool fused_long_supported(int dk, int dv, bool in_f32, int draft, int cap);
+inline bool fused_long_supported(int dk, int dv, bool in_f32, int draft, int cap) {
+  return chunked_supported(dk, dv, in_f32, draft) && cap > kChunkTokens;
+}
 hipError_t launch_verify_flush_long(const VerifyArgs &a, int min_len, hipStream_t stream);
 hipError_t launch_verify_flush_fused(const VerifyArgs &a, int min_len, hipStream_t stream);
 // (a.prev_accepted non-null: the previous draft's rollback first, in the same kernel)
@@ -103,7 +114,7 @@ struct NormArgs {
   uint8_t *q;            // [groups][d_v] OCP E4M3 codes
   float *scale;          // [groups] fp32
 };
-bool norm_supported(int dv);
+inline bool norm_supported(int dv) { return dv == 16 || dv == 32 || dv == 64 || dv == 128; }
 hipError_t launch_gated_rmsnorm_fp8(const NormArgs &a, int dv, hipStream_t stream);
 
 // Causal convolution of a draft block with its input ring (conv.hip); the ring
@@ -118,7 +129,7 @@ struct ConvArgs {
   const float *bias;     // [channels] or null
   void *y;               // [num_reqs][draft][channels] bf16
 };
-bool conv_width_supported(int k);
+inline bool conv_width_supported(int k) { return k >= 1 && k <= kMaxConvWidth; }
 hipError_t launch_causal_conv_update(const ConvArgs &a, int width, hipStream_t stream);
 
 // head dims with a compiled kernel

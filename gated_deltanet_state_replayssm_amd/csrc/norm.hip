@@ -124,8 +124,6 @@ hipError_t launch_dv(const NormArgs &a, hipStream_t stream) {
 
 }  // namespace
 
-bool norm_supported(int dv) { return dv == 16 || dv == 32 || dv == 64 || dv == 128; }
-
 hipError_t launch_gated_rmsnorm_fp8(const NormArgs &a, int dv, hipStream_t stream) {
   switch (dv) {
     case 16: return launch_dv<16>(a, stream);

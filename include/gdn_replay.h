@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define GDN_REPLAY_VERSION 6
+#define GDN_REPLAY_VERSION 7
 
 typedef enum {
   GDN_OK = 0,
@@ -85,12 +85,16 @@ enum {
  *   sync       int32 arrival counters, zero when created; every completed call
  *              leaves them zero. They let the last workgroup of a slot (flush)
  *              or of the grid (verify_flush) move the pointers once every
- *              workgroup has read them. gdn_replay_sync_entries(num_slots, HK)
- *              entries (32 * (num_slots + 1) + num_slots * HK: the counters that
- *              many workgroups hit sit 128 bytes apart, since atomics on one
- *              cache line are served one after another); 128-byte alignment
- *              keeps each on a line of its own. The library cannot check the
- *              size of this buffer: a smaller one is written out of bounds.
+ *              workgroup has read them. At least
+ *              gdn_replay_sync_entries(num_slots, HK) entries (32 * (num_slots
+ *              + 1) + num_slots * HK: the counters that many workgroups hit sit
+ *              128 bytes apart, since atomics on one cache line are served one
+ *              after another); 128-byte alignment keeps each on a line of its
+ *              own.
+ *   sync_len   number of int32 entries the caller allocated at sync. Every call
+ *              returns GDN_EINVAL, with nothing enqueued, when it is below
+ *              gdn_replay_sync_entries(num_slots, HK); GDN_EUNSUPPORTED when
+ *              that count does not fit in an int32.
  *   err        [1] int32 sticky error word, or NULL to drop device errors.
  *
  * Value head h reads key head h / (HV / HK) (consecutive grouping, HV % HK == 0).
@@ -104,7 +108,7 @@ typedef struct {
   int32_t d_v;
   int32_t ring_cap;     /* C */
   int32_t in_dtype;     /* gdn_dtype */
-  int32_t reserved;
+  int32_t sync_len;     /* entries of sync */
   float *state;
   void *ring_q;
   void *ring_k;

@@ -41,6 +41,18 @@ int main(void) {
   c.ring_k = c.ring_v = fake;
   c.ring_alpha = c.ring_beta = ffake;
   c.head = c.len = c.sync = c.err = (int32_t *)fake;
+  c.sync_len = (int32_t)gdn_replay_sync_entries(c.num_slots, c.num_k_heads);
+
+  /* a counter buffer declared one entry short is refused by every call */
+  c.sync_len -= 1;
+  CHECK(gdn_replay_verify(&c, 1, ifake, 4, fake, fake, fake, ffake, ffake, ffake, 0) ==
+        GDN_EINVAL);
+  CHECK(gdn_replay_flush(&c, 1, ifake, 1, 0) == GDN_EINVAL);
+  CHECK(gdn_replay_verify_flush(&c, 1, ifake, 4, 16, fake, fake, fake, ffake, ffake, ffake, 0) ==
+        GDN_EINVAL);
+  CHECK(gdn_replay_rollback_verify_flush(&c, 1, ifake, ifake, NULL, 4, NULL, 4, 16, fake, fake,
+                                         fake, ffake, ffake, ffake, 0) == GDN_EINVAL);
+  c.sync_len += 1;
 
   /* verify: no cache, bad counts and lengths, zero requests */
   CHECK(gdn_replay_verify(NULL, 1, ifake, 4, fake, fake, fake, ffake, ffake, ffake, 0) ==

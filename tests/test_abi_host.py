@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert b.version() == 6
+    assert b.version() == 7
     for st in (b.GDN_OK, b.GDN_EINVAL, b.GDN_EUNSUPPORTED, b.GDN_EHIP):
         assert b.load().gdn_replay_strerror(st)
     assert b.load().gdn_replay_strerror(12345) == b"unknown status"
@@ -38,7 +38,7 @@ FAKE = 1 << 20  # a non-NULL, 16-byte-aligned address that is never dereferenced
 
 def _cache(**over):
     kw = dict(num_slots=4, num_v_heads=4, num_k_heads=2, d_k=16, d_v=16, ring_cap=8,
-              in_dtype=b.GDN_BF16, reserved=0, state=FAKE, ring_q=None, ring_k=FAKE,
+              in_dtype=b.GDN_BF16, sync_len=b.sync_entries(4, 2), state=FAKE, ring_q=None, ring_k=FAKE,
               ring_v=FAKE, ring_alpha=FAKE, ring_beta=FAKE, head=FAKE, len=FAKE, sync=FAKE,
               err=FAKE)
     kw.update(over)
@@ -85,6 +85,12 @@ def test_null_cache_rejected():
     (dict(state=FAKE + 4), b.GDN_EINVAL),          # misaligned
     (dict(ring_v=FAKE + 2), b.GDN_EINVAL),
     (dict(num_v_heads=8192, num_k_heads=8192), b.GDN_EUNSUPPORTED),
+    # the counter buffer's declared size: one entry short, none, negative
+    (dict(sync_len=b.sync_entries(4, 2) - 1), b.GDN_EINVAL),
+    (dict(sync_len=0), b.GDN_EINVAL),
+    (dict(sync_len=-1), b.GDN_EINVAL),
+    # more counters than an int32 count can describe
+    (dict(num_slots=1 << 30, sync_len=(1 << 31) - 1), b.GDN_EUNSUPPORTED),
 ])
 def test_cache_validation(over, status):
     c = _cache(**over)
@@ -281,8 +287,8 @@ def test_conv_call_validation():
 def test_grids_past_the_dispatch_limit_are_refused():
     """num_reqs * HV workgroups of 256 threads must fit a dispatch's 32-bit
     work-item count; the norm takes 32 work-items per (row, head) group."""
-    c = _cache(num_slots=1 << 20, num_v_heads=4096, num_k_heads=4096, d_k=64, d_v=64,
-               ring_cap=32)
+    c = _cache(num_slots=4096, num_v_heads=4096, num_k_heads=1, d_k=64, d_v=64,
+               ring_cap=32, sync_len=b.sync_entries(4096, 1))
     assert _verify(c, num_reqs=2048) == b.GDN_EUNSUPPORTED      # 2048 * 4096 * 256 = 2^31
     assert _verify_flush(c, num_reqs=2048) == b.GDN_EUNSUPPORTED
     assert b.flush_raw(c, 2048, FAKE, 1, None) == b.GDN_EUNSUPPORTED

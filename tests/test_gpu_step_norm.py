@@ -157,11 +157,12 @@ def test_step_norm_parity(d, varlen):
 
 
 def test_step_norm_pages_point():
-    """32 requests x 32 heads x 128, 3 steps (oracle chain on the first step's
-    outputs is left to the smaller cases: the boundary-aware check runs on all)."""
+    """32 requests x 32 heads x 128, 3 steps: the boundary-aware check of the
+    codes on the kernel's own outputs, and the fp64 chain (the oracle's
+    rollback and verify_flush, then the norm oracle) on every request."""
     wl = W["r32_hv32_hk16_d128_f16"]
-    say("case step_norm r32 full size")
-    for _ in _step_pair(wl, 910, 3):
+    say("case step_norm r32 full size, fp64 chain on every request")
+    for _ in _step_pair(wl, 910, 3, with_oracle=True):
         pass
 
 

@@ -20,7 +20,8 @@ GDN_DERR_DRAFT = 16
 EXPORTED = ("gdn_replay_verify", "gdn_replay_rollback", "gdn_replay_flush",
             "gdn_replay_verify_flush", "gdn_replay_verify_varlen",
             "gdn_replay_verify_flush_varlen", "gdn_replay_rollback_varlen",
-            "gdn_replay_rollback_verify_flush", "gdn_replay_sync_entries",
+            "gdn_replay_rollback_verify_flush", "gdn_replay_rollback_verify_flush_noalloc",
+            "gdn_replay_sync_entries",
             "gdn_replay_step_norm_fp8",
             "gdn_gated_rmsnorm_fp8", "gdn_causal_conv_update", "gdn_replay_strerror",
             "gdn_replay_version")
@@ -93,6 +94,9 @@ def load(path: str = LIB_PATH):
     lib.gdn_replay_rollback_verify_flush.argtypes = [P, I32, VP, VP, VP, I32, VP, I32, I32, VP,
                                                      VP, VP, VP, VP, VP, VP]
     lib.gdn_replay_rollback_verify_flush.restype = ctypes.c_int
+    lib.gdn_replay_rollback_verify_flush_noalloc.argtypes = \
+        lib.gdn_replay_rollback_verify_flush.argtypes
+    lib.gdn_replay_rollback_verify_flush_noalloc.restype = ctypes.c_int
     lib.gdn_replay_step_norm_fp8.argtypes = [P, I32, VP, VP, VP, I32, VP, I32, I32, VP, VP, VP,
                                              VP, VP, VP, ctypes.POINTER(GdnNormFp8), VP]
     lib.gdn_replay_step_norm_fp8.restype = ctypes.c_int
@@ -170,6 +174,17 @@ def rollback_verify_flush_raw(cache: GdnReplayCache, num_reqs, slot_idx, num_acc
                                                    num_accepted, prev_draft_lens, prev_draft,
                                                    draft_lens, draft_len, min_len, q, k, v, alpha,
                                                    beta, out, stream)
+
+
+def rollback_verify_flush_noalloc_raw(cache: GdnReplayCache, num_reqs, slot_idx, num_accepted,
+                                      prev_draft_lens, prev_draft, draft_lens, draft_len, min_len,
+                                      q, k, v, alpha, beta, out, stream) -> int:
+    return load().gdn_replay_rollback_verify_flush_noalloc(
+        ctypes.byref(cache), num_reqs, slot_idx, num_accepted, prev_draft_lens, prev_draft,
+        draft_lens, draft_len, min_len, q, k, v, alpha, beta, out, stream)
+
+
+NOALLOC_SYNC_ENTRIES = 65536   # GDN_REPLAY_NOALLOC_SYNC_ENTRIES
 
 
 def step_norm_fp8_raw(cache: GdnReplayCache, num_reqs, slot_idx, num_accepted, prev_draft_lens,

@@ -19,7 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdnreplay.so")
 
-SOURCES = ["api.cpp", "chunked.hip", "fused.hip", "recurrent.hip", "rollback.hip", "norm.hip", "conv.hip"]
+SOURCES = ["api.cpp", "chunked.hip", "fused.hip", "recurrent.hip", "rollback.hip", "norm.hip", "conv.hip",
+           "noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -237,6 +237,21 @@ int gdn_replay_rollback_verify_flush(const gdn_replay_cache *c, int32_t num_reqs
                                      int32_t min_len, const void *q, const void *k, const void *v,
                                      const float *alpha, const float *beta, float *out,
                                      hipStream_t stream) {
+  return gdnr::rollback_verify_flush_call(c, num_reqs, slot_idx, num_accepted, prev_draft_lens,
+                                          prev_draft, draft_lens, draft_len, min_len, q, k, v,
+                                          alpha, beta, out, stream, false);
+}
+
+}  // extern "C"
+
+namespace gdnr {
+
+int rollback_verify_flush_call(const gdn_replay_cache *c, int32_t num_reqs,
+                               const int32_t *slot_idx, const int32_t *num_accepted,
+                               const int32_t *prev_draft_lens, int32_t prev_draft,
+                               const int32_t *draft_lens, int32_t draft_len, int32_t min_len,
+                               const void *q, const void *k, const void *v, const float *alpha,
+                               const float *beta, float *out, hipStream_t stream, bool check_only) {
   gdnr::VerifyArgs a;
   const bool varlen = draft_lens != nullptr;
   int st = verify_args(c, num_reqs, slot_idx, draft_len, q, k, v, alpha, beta, out, &a, varlen,
@@ -245,6 +260,7 @@ int gdn_replay_rollback_verify_flush(const gdn_replay_cache *c, int32_t num_reqs
   if (prev_draft < 1 || prev_draft > c->ring_cap) return GDN_EINVAL;
   if (!num_accepted || !aligned(num_accepted, 4)) return GDN_EINVAL;
   if (prev_draft_lens && !aligned(prev_draft_lens, 4)) return GDN_EINVAL;
+  if (check_only) return GDN_OK;
   const bool f32 = c->in_dtype == GDN_F32;
   const bool one_chunk = gdnr::fused_supported(c->d_k, c->d_v, f32, draft_len, c->ring_cap);
   if (one_chunk || gdnr::fused_long_supported(c->d_k, c->d_v, f32, draft_len, c->ring_cap)) {
@@ -262,6 +278,10 @@ int gdn_replay_rollback_verify_flush(const gdn_replay_cache *c, int32_t num_reqs
   return verify_flush_impl(c, num_reqs, slot_idx, draft_len, min_len, q, k, v, alpha, beta, out,
                            stream, varlen, draft_lens);
 }
+
+}  // namespace gdnr
+
+extern "C" {
 
 int gdn_replay_step_norm_fp8(const gdn_replay_cache *c, int32_t num_reqs,
                              const int32_t *slot_idx, const int32_t *num_accepted,

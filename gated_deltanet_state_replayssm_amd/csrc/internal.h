@@ -132,6 +132,16 @@ struct ConvArgs {
 inline bool conv_width_supported(int k) { return k >= 1 && k <= kMaxConvWidth; }
 hipError_t launch_causal_conv_update(const ConvArgs &a, int width, hipStream_t stream);
 
+// gdn_replay_rollback_verify_flush with every host check; with check_only set
+// it returns after the checks (GDN_OK when the call would be launched) and
+// enqueues nothing.
+int rollback_verify_flush_call(const gdn_replay_cache *c, int32_t num_reqs,
+                               const int32_t *slot_idx, const int32_t *num_accepted,
+                               const int32_t *prev_draft_lens, int32_t prev_draft,
+                               const int32_t *draft_lens, int32_t draft_len, int32_t min_len,
+                               const void *q, const void *k, const void *v, const float *alpha,
+                               const float *beta, float *out, hipStream_t stream, bool check_only);
+
 // head dims with a compiled kernel
 inline bool dims_supported(int dk, int dv) {
   return dk == dv && (dk == 16 || dk == 32 || dk == 64 || dk == 128);

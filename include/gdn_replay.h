@@ -375,6 +375,36 @@ int gdn_causal_conv_update(const gdn_replay_cache *c, void *conv_ring, int32_t c
                            int32_t draft_len, const void *x, const float *weight,
                            const float *bias, void *y, hipStream_t stream);
 
+/*
+ * gdn_replay_rollback_verify_flush_noalloc — for callers that cannot allocate
+ * device memory: code under HIP graph capture, serving loops that must not
+ * allocate, harnesses that forbid it. The same call, with the same result, as
+ * gdn_replay_rollback_verify_flush, except that the arrival counters come from
+ * a library-owned device array instead of c->sync: c->sync and c->sync_len are
+ * ignored (they may be NULL and 0); the other fields and arguments are as for
+ * gdn_replay_rollback_verify_flush.
+ *
+ * Limit: gdn_replay_sync_entries(num_slots, HK) must not exceed
+ * GDN_REPLAY_NOALLOC_SYNC_ENTRIES (e.g. num_slots <= 1364 at HK = 16); larger
+ * caches get GDN_EUNSUPPORTED, with nothing enqueued, and must use
+ * gdn_replay_rollback_verify_flush with a counter buffer of their own.
+ * The array (GDN_REPLAY_NOALLOC_SYNC_ENTRIES int32, 256 KiB) exists once per
+ * GPU the library runs on and stays until the process ends; the first call on
+ * a device looks up its address (call with the stream's device current). Every
+ * call on a GPU shares that GPU's array: calls that overlap in time on one GPU
+ * (on other streams or threads) race on it and must not be issued. The
+ * counters are zero at load and every completed call leaves them zero. Nothing
+ * is allocated, by the library or on its behalf, in any call.
+ */
+#define GDN_REPLAY_NOALLOC_SYNC_ENTRIES 65536
+int gdn_replay_rollback_verify_flush_noalloc(const gdn_replay_cache *c, int32_t num_reqs,
+                                             const int32_t *slot_idx, const int32_t *num_accepted,
+                                             const int32_t *prev_draft_lens, int32_t prev_draft,
+                                             const int32_t *draft_lens, int32_t draft_len,
+                                             int32_t min_len, const void *q, const void *k,
+                                             const void *v, const float *alpha, const float *beta,
+                                             float *out, hipStream_t stream);
+
 /* Human-readable text of a gdn_status (static storage). */
 const char *gdn_replay_strerror(int status);
 

@@ -316,3 +316,25 @@ def test_struct_layout_matches_header():
     assert ctypes.sizeof(b.GdnReplayCache) == 8 * 4 + 10 * 8
     assert b.GdnReplayCache.state.offset == 32
     assert b.GdnReplayCache.err.offset == 32 + 9 * 8
+
+
+def test_noalloc_step_host_checks():
+    """The no-alloc one-call step: the caller's counter fields are ignored (NULL
+    and 0 accepted), every other check is the one-call step's, and a cache whose
+    counters do not fit the library's array is refused; all before any HIP call."""
+    f = FAKE
+    c = _cache(d_k=64, d_v=64, ring_cap=32, sync=None, sync_len=0)
+    call = lambda cache, **kw: b.rollback_verify_flush_noalloc_raw(
+        cache, kw.get("n", 2), f, kw.get("acc", f), None, 4, None, kw.get("d", 4), 16, f, f, f, f,
+        f, kw.get("out", f), None)
+    assert b.load().gdn_replay_rollback_verify_flush_noalloc(
+        None, 1, f, f, None, 4, None, 4, 16, f, f, f, f, f, f, None) == b.GDN_EINVAL
+    assert call(c, n=0) == b.GDN_OK                       # no request: nothing to do
+    assert call(c, acc=None) == b.GDN_EINVAL
+    assert call(c, d=0) == b.GDN_EINVAL
+    assert call(c, out=f + 4) == b.GDN_EINVAL
+    assert call(_cache(d_k=48, d_v=48, sync=None, sync_len=0)) == b.GDN_EUNSUPPORTED
+    big = _cache(num_slots=2000, num_v_heads=32, num_k_heads=16, d_k=128, d_v=128, ring_cap=32,
+                 sync=None, sync_len=0)
+    assert b.sync_entries(2000, 16) > b.NOALLOC_SYNC_ENTRIES
+    assert call(big) == b.GDN_EUNSUPPORTED

@@ -60,11 +60,14 @@ class GdnReplayCache(ctypes.Structure):
 _lib = None
 
 
-def load(path: str = LIB_PATH):
-    """Load the library (once) and declare the signatures. Raises if absent."""
+def load(path: str = None):
+    """Load the library (once) and declare the signatures. Raises if absent.
+    The in-tree build is used unless GDN_REPLAY_LIB names another build."""
     global _lib
     if _lib is not None:
         return _lib
+    if path is None:
+        path = os.environ.get("GDN_REPLAY_LIB", LIB_PATH)
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built; run gated_deltanet_state_replayssm_amd.build")
     # PyTorch ships its own HIP runtime. Load it first when it is installed, so
@@ -104,7 +107,8 @@ def load(path: str = LIB_PATH):
     lib.gdn_replay_sync_entries.restype = ctypes.c_int64
     lib.gdn_gated_rmsnorm_fp8.argtypes = [I32, I32, I32, VP, VP, VP, ctypes.c_float, VP, VP, VP]
     lib.gdn_gated_rmsnorm_fp8.restype = ctypes.c_int
-    lib.gdn_causal_conv_update.argtypes = [P, VP, I32, I32, I32, VP, I32, VP, VP, VP, VP, VP]
+    lib.gdn_causal_conv_update.argtypes = [P, VP, I32, I32, I32, VP, VP, VP, I32, I32, VP, VP,
+                                           VP, VP, VP]
     lib.gdn_causal_conv_update.restype = ctypes.c_int
     lib.gdn_replay_strerror.argtypes = [ctypes.c_int]
     lib.gdn_replay_strerror.restype = ctypes.c_char_p
@@ -266,16 +270,20 @@ def gated_rmsnorm_fp8(rows, num_heads, d_v, o, z, weight, eps, q, scale, stream)
 
 
 def causal_conv_update_raw(cache: GdnReplayCache, conv_ring, channels, width, num_reqs, slot_idx,
-                           draft_len, x, weight, bias, y, stream) -> int:
+                           draft_len, x, weight, bias, y, stream, num_accepted=None,
+                           prev_draft_lens=None, prev_draft=0) -> int:
     return load().gdn_causal_conv_update(ctypes.byref(cache), conv_ring, channels, width, num_reqs,
-                                         slot_idx, draft_len, x, weight, bias, y, stream)
+                                         slot_idx, num_accepted, prev_draft_lens, prev_draft,
+                                         draft_len, x, weight, bias, y, stream)
 
 
 def causal_conv_update(cache, conv_ring, channels, width, num_reqs, slot_idx, draft_len, x, weight,
-                       bias, y, stream) -> None:
+                       bias, y, stream, num_accepted=None, prev_draft_lens=None,
+                       prev_draft=0) -> None:
     _check("gdn_causal_conv_update",
            causal_conv_update_raw(cache, conv_ring, channels, width, num_reqs, slot_idx, draft_len,
-                                  x, weight, bias, y, stream))
+                                  x, weight, bias, y, stream, num_accepted, prev_draft_lens,
+                                  prev_draft))
 
 
 def sync_entries(num_slots: int, num_k_heads: int) -> int:

@@ -365,8 +365,9 @@ int gdn_gated_rmsnorm_fp8(int32_t rows, int32_t num_heads, int32_t d_v, const fl
 
 int gdn_causal_conv_update(const gdn_replay_cache *c, void *conv_ring, int32_t channels,
                            int32_t width, int32_t num_reqs, const int32_t *slot_idx,
-                           int32_t draft_len, const void *x, const float *weight,
-                           const float *bias, void *y, hipStream_t stream) {
+                           const int32_t *num_accepted, const int32_t *prev_draft_lens,
+                           int32_t prev_draft, int32_t draft_len, const void *x,
+                           const float *weight, const float *bias, void *y, hipStream_t stream) {
   int st = check_cache(c);
   if (st != GDN_OK) return st;
   if (channels < 2 || channels % 2 != 0) return GDN_EINVAL;
@@ -378,6 +379,11 @@ int gdn_causal_conv_update(const gdn_replay_cache *c, void *conv_ring, int32_t c
   if (draft_len > 65535) return GDN_EUNSUPPORTED;
   if (num_reqs == 0) return GDN_OK;
   if (!conv_ring || !slot_idx || !x || !weight || !y) return GDN_EINVAL;
+  if (num_accepted) {  // the previous draft's rollback is still pending
+    if (prev_draft < 1 || prev_draft > c->ring_cap) return GDN_EINVAL;
+    if (!aligned(num_accepted, 4) || (prev_draft_lens && !aligned(prev_draft_lens, 4)))
+      return GDN_EINVAL;
+  }
   if (!aligned(conv_ring, 4) || !aligned(slot_idx, 4) || !aligned(x, 4) || !aligned(weight, 4) ||
       (bias && !aligned(bias, 4)) || !aligned(y, 4))
     return GDN_EINVAL;
@@ -387,6 +393,9 @@ int gdn_causal_conv_update(const gdn_replay_cache *c, void *conv_ring, int32_t c
   a.draft = draft_len;
   a.channels = channels;
   a.slot_idx = slot_idx;
+  a.prev_accepted = num_accepted;
+  a.prev_draft_lens = num_accepted ? prev_draft_lens : nullptr;
+  a.prev_draft = num_accepted ? prev_draft : 0;
   a.ring = conv_ring;
   a.x = x;
   a.weight = weight;

@@ -8,7 +8,9 @@
 // inputs of the committed stream; they sit in the ring at
 // (head + len - K + 1 + m) mod C, the draft is appended at (head + len + j) mod C
 // (where the recurrence appends its rows), so a rollback (len += a) and a flush
-// (head += len) need no work here.
+// (head += len) need no work here. When the previous draft's rollback is still
+// to come (it is folded into the one-call step that runs after this kernel),
+// len + a of that rollback stands for len.
 //
 // One thread per pair of channels of a group of draft tokens of one request
 // (coalesced rows: consecutive threads take consecutive channels). fp32
@@ -54,10 +56,19 @@ __global__ __launch_bounds__(256) void causal_conv_update_kernel(ConvArgs a) {
     return;
   }
   const int C = c.cap;
-  const int head = c.head[s], n = c.len[s];
-  if (head < 0 || head >= C || n < 0 || n > C) {
+  const int head = c.head[s], n0 = c.len[s];
+  if (head < 0 || head >= C || n0 < 0 || n0 > C) {
     if (lead) raise_err(c.err, GDN_DERR_POINTER);
     return;
+  }
+  // The committed count the step that follows works from: with the previous
+  // draft's rollback still pending (folded into the one-call step), len + a
+  // under that step's checks (a failed rollback keeps len; the step flags it).
+  int n = n0;
+  if (a.prev_accepted) {
+    int bad;
+    const int bound = a.prev_draft_lens ? a.prev_draft_lens[r] : a.prev_draft;
+    n = rolled_from(n0, a.prev_accepted[r], bound, a.prev_draft, C, &bad);
   }
   // D + K - 1 <= C (host-checked): the draft never reaches the history it
   // reads; committed inputs older than that are never read again, so len + D

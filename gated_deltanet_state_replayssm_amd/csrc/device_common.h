@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/gdn_replay.h"
+
 namespace gdnr {
 
 // q/k/v element loads: bf16 bits (upcast is exact) or fp32.
@@ -45,6 +47,23 @@ __device__ __forceinline__ int request_draft(const int32_t *lens, int r, int dma
   if (!lens) return dmax;
   const int d = lens[r];
   return (d < 0 || d > dmax) ? -1 : d;
+}
+
+// Committed count of a slot once the accepted prefix of the previous draft is
+// committed (a rollback folded into a later call): len + a when the previous
+// draft's length `bound` is in [0, prev_draft], a in [0, bound] and
+// len + a <= cap; otherwise len, with the rollback's error bit in *bad (as a
+// separate rollback call would skip the request and flag it).
+__device__ __forceinline__ int rolled_from(int len, int a, int bound, int prev_draft, int cap,
+                                          int *bad) {
+  *bad = 0;
+  if (bound < 0 || bound > prev_draft)
+    *bad = GDN_DERR_DRAFT;
+  else if (a < 0 || a > bound)
+    *bad = GDN_DERR_ACCEPT;
+  else if (len + a > cap)
+    *bad = GDN_DERR_CAPACITY;
+  return *bad ? len : len + a;
 }
 
 }  // namespace gdnr

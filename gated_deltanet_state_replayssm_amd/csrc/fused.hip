@@ -215,23 +215,6 @@ struct Req {
   int roll_err;         // the folded rollback's error bit for this request (0: none)
 };
 
-// Committed count of request i once the accepted prefix of the previous draft
-// is committed (the rollback folded into this call): len + a when the previous
-// length is in [0, prev_draft], a in [0, that length] and len + a <= C;
-// otherwise len, with the rollback's error bit in *bad (as a separate rollback
-// call would skip the request and flag it).
-__device__ __forceinline__ int rolled_from(int len, int a, int bound, int prev_draft, int cap,
-                                           int *bad) {
-  *bad = 0;
-  if (bound < 0 || bound > prev_draft)
-    *bad = GDN_DERR_DRAFT;
-  else if (a < 0 || a > bound)
-    *bad = GDN_DERR_ACCEPT;
-  else if (len + a > cap)
-    *bad = GDN_DERR_CAPACITY;
-  return *bad ? len : len + a;
-}
-
 __device__ __forceinline__ int rolled_len(const VerifyArgs &va, int i, int len, int cap,
                                           int *bad) {
   const int bound = va.prev_draft_lens ? va.prev_draft_lens[i] : va.prev_draft;
@@ -396,63 +379,99 @@ __device__ Req ordered_request(const VerifyArgs &va, int mn, int q, int lane, Mo
   return o;
 }
 
-// End of a fused launch. Every workgroup counts itself in (after a barrier, so
-// that all its waves have read the pointers): HV per request rank on that
-// rank's counter, then the last of those on the grid counter. The grid's last
-// workgroup moves the pointers: a due slot's head += len, len = 0; with a
-// folded rollback, len += a for the others. With no due request and no
-// rollback nothing moves and no count is taken (every workgroup sees the same
-// count, as no pointer changes during the call).
+// Arrival count of a fused launch. The pointers (head, len) may move only once
+// every workgroup has read them, and a workgroup reads them in its ordering
+// pass only. So each workgroup counts itself in right after that pass (after a
+// barrier, so that all its waves have read): HV per request rank on that
+// rank's counter, then the last of those on the grid counter, and the
+// workgroup that brings the grid count to num_reqs moves the pointers at its
+// end (a due slot's head += len, len = 0; with a folded rollback, len += a for
+// the others). The atomics' returns are read where waiting for them costs
+// nothing: the rank count once the first staged inputs have arrived (it was
+// issued before them; loads and atomics return in issue order), the grid count
+// after the last contraction, whose result is read at the end. Neither count
+// sits at the end of a workgroup's life, where it would lengthen the launch's
+// tail. With no due request and no rollback nothing moves and no count is
+// taken (every workgroup sees the same count, as no pointer changes during the
+// call). Every counter is reset by its last arrival.
 template <bool ROLLBACK, bool VARLEN>
-__device__ __forceinline__ void end_of_grid(const VerifyArgs &va, const Req &rq, int mn,
-                                            int32_t *rank_ctr, int32_t *grid_ctr,
-                                            const Move *moves, int *grid_rank, int tid) {
-  const CacheView &c = va.c;
-  const int HV = c.hv;
-  if (!ROLLBACK && rq.due == 0) return;  // a folded rollback moves len in any case
-  __syncthreads();
-  if (tid == 0) {
-    int last = 0;
-    if (atomicAdd(rank_ctr, 1) == HV - 1) {
-      *rank_ctr = 0;
-      last = atomicAdd(grid_ctr, 1) == va.num_reqs - 1;
-    }
-    *grid_rank = last;
+struct Arrival {
+  bool counting;   // uniform: the call moves pointers
+  bool taken;      // uniform: the rank count has been read
+  bool gridded;    // uniform: the grid count has been taken (if this is the rank's last)
+  bool rank_last;  // wave 0, after take_rank(): last of its request rank to count in
+  int ticket;      // lane 0 of wave 0: the rank counter's value before this arrival
+  int gticket;     // lane 0 of wave 0: the grid counter's value before it (rank_last)
+
+  __device__ __forceinline__ void count_in(const Req &rq, int32_t *rank_ctr, int tid) {
+    counting = ROLLBACK || rq.due > 0;
+    taken = gridded = rank_last = false;
+    ticket = 0;
+    if (!counting) return;
+    __syncthreads();  // every wave has read the pointers
+    if (tid == 0) ticket = atomicAdd(rank_ctr, 1);
   }
-  __syncthreads();
-  if (!*grid_rank) return;
-  if (va.num_reqs <= 64) {  // moves worked out by the ordering pass
-    if (tid < va.num_reqs) {
-      const Move mv = moves[tid];
-      if (mv.slot >= 0) {
-        if (mv.head >= 0) c.head[mv.slot] = mv.head;
-        c.len[mv.slot] = mv.len;
+
+  // Wave 0 reads its rank count; called by every wave at the same point.
+  __device__ __forceinline__ void take_rank(int HV, int32_t *rank_ctr, int tid) {
+    if (!counting || taken) return;
+    taken = true;
+    if (__builtin_amdgcn_readfirstlane(tid) >= 64) return;  // (uniform: the wave's first lane)
+    rank_last = __builtin_amdgcn_readfirstlane(ticket) == HV - 1;
+    if (rank_last && tid == 0) *rank_ctr = 0;  // every arrival of the rank is in
+  }
+
+  // The last of a rank counts in at the grid counter.
+  __device__ __forceinline__ void grid_in(int HV, int32_t *rank_ctr, int32_t *grid_ctr,
+                                          int tid) {
+    if (!counting || gridded) return;
+    take_rank(HV, rank_ctr, tid);
+    gridded = true;
+    gticket = (rank_last && tid == 0) ? atomicAdd(grid_ctr, 1) : -1;
+  }
+
+  // End of the workgroup: the grid's last arrival moves the pointers (wave 0).
+  __device__ __forceinline__ void finish(const VerifyArgs &va, int mn, int32_t *rank_ctr,
+                                         int32_t *grid_ctr, const Move *moves, int tid) {
+    const CacheView &c = va.c;
+    if (!counting) return;
+    grid_in(c.hv, rank_ctr, grid_ctr, tid);
+    if (__builtin_amdgcn_readfirstlane(tid) >= 64 || !rank_last) return;
+    if (__builtin_amdgcn_readfirstlane(gticket) != va.num_reqs - 1) return;
+    const int lane = tid;
+    if (va.num_reqs <= 64) {  // moves worked out by the ordering pass
+      if (lane < va.num_reqs) {
+        const Move mv = moves[lane];
+        if (mv.slot >= 0) {
+          if (mv.head >= 0) c.head[mv.slot] = mv.head;
+          c.len[mv.slot] = mv.len;
+        }
+      }
+      if (lane == 0) *grid_ctr = 0;
+      return;
+    }
+    for (int i = lane; i < va.num_reqs; i += 64) {
+      const int si = va.slot_idx[i];
+      if (si < 0 || si >= c.num_slots) continue;
+      const int hs = c.head[si], n0 = c.len[si];
+      if (hs < 0 || hs >= c.cap || n0 < 0 || n0 > c.cap) continue;
+      int ns = n0;
+      if constexpr (ROLLBACK) {
+        int bad;
+        ns = rolled_len(va, i, n0, c.cap, &bad);
+      }
+      // a request with a bad draft length is not flushed (its rollback stands)
+      const bool skip = VARLEN && request_draft(va.draft_lens, i, va.draft) < 0;
+      if (ns >= mn && !skip) {
+        c.head[si] = hs + ns - (hs + ns >= c.cap ? c.cap : 0);
+        c.len[si] = 0;
+      } else if (ROLLBACK && ns != n0) {
+        c.len[si] = ns;
       }
     }
-    if (tid == 0) *grid_ctr = 0;
-    return;
+    if (lane == 0) *grid_ctr = 0;
   }
-  for (int i = tid; i < va.num_reqs; i += blockDim.x) {
-    const int si = va.slot_idx[i];
-    if (si < 0 || si >= c.num_slots) continue;
-    const int hs = c.head[si], n0 = c.len[si];
-    if (hs < 0 || hs >= c.cap || n0 < 0 || n0 > c.cap) continue;
-    int ns = n0;
-    if constexpr (ROLLBACK) {
-      int bad;
-      ns = rolled_len(va, i, n0, c.cap, &bad);
-    }
-    // a request with a bad draft length is not flushed (its rollback stands)
-    const bool skip = VARLEN && request_draft(va.draft_lens, i, va.draft) < 0;
-    if (ns >= mn && !skip) {
-      c.head[si] = hs + ns - (hs + ns >= c.cap ? c.cap : 0);
-      c.len[si] = 0;
-    } else if (ROLLBACK && ns != n0) {
-      c.len[si] = ns;
-    }
-  }
-  if (tid == 0) *grid_ctr = 0;
-}
+};
 
 // Flush fused into verify, ring capacity <= 32. A slot with len >= max(min_len,
 // 1) first folds its len committed tokens into the checkpoint and writes it
@@ -465,10 +484,10 @@ __device__ __forceinline__ void end_of_grid(const VerifyArgs &va, const Req &rq,
 // CU a similar share of them. Every workgroup derives the order from each
 // request's len, so len must not change while a workgroup may still read it:
 // the pointers of the due slots (head += len, len = 0) are moved by the last
-// workgroup of the grid to finish. It is found in two levels, so that no
-// counter sees more than one arrival per workgroup of a request group: the
-// HV workgroups of request rank q count in at that rank's counter (a 128-byte
-// line of its own), the last of them at the grid counter.
+// workgroup to count in after its ordering pass (Arrival). It is found in two
+// levels, so that no counter sees more than one arrival per workgroup of a
+// request group: the HV workgroups of request rank q count in at that rank's
+// counter (a 128-byte line of its own), the last of them at the grid counter.
 //
 // The draft is appended at (new head + j) mod C, which may wrap onto committed
 // key rows that the other value heads of the same key head are still reading
@@ -483,7 +502,7 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyA
   static_assert(DK % 32 == 0 && DV % (16 * NT) == 0 && (NT == 2 || NT == 4), "tile shape");
   typedef typename Cols<NT>::F F;
   __shared__ Smem<DK, DV> sm;
-  __shared__ int group_rank, grid_rank;
+  __shared__ int group_rank;
   __shared__ Move moves[64];
 
   const CacheView &c = va.c;
@@ -510,11 +529,11 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyA
   const bool lead = (h == 0 && tid == 0);
   int32_t *grid_ctr = c.sync;
   int32_t *rank_ctr = slot_counter(c, blockIdx.x / HV);
-
-  // every workgroup counts itself in at its end; the grid's last moves the pointers
-  auto finish = [&]() {
-    end_of_grid<ROLLBACK, VARLEN>(va, rq, mn, rank_ctr, grid_ctr, moves, &grid_rank, tid);
-  };
+  // every workgroup counts itself in once its pointers are read; the grid's
+  // last arrival moves the pointers at its end
+  Arrival<ROLLBACK, VARLEN> arr;
+  arr.count_in(rq, rank_ctr, tid);
+  auto finish = [&]() { arr.finish(va, mn, rank_ctr, grid_ctr, moves, tid); };
 
   const int s = rq.s;
   if (s < 0 || s >= c.num_slots) {
@@ -571,7 +590,10 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyA
       __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();  // the committed rows are read (and staged)
-    if (tid == 0) group_rank = atomicAdd(group_ctr, 1);
+    arr.take_rank(HV, rank_ctr, tid);
+    // count in for the key rows' append; the last wave waits for the return,
+    // which comes after its state loads, not the builder
+    if (tid == 64 * (WAVES - 1)) group_rank = atomicAdd(group_ctr, 1);
     if (wave == 0) build_tt<DK, DV>(sm, sgf.al, lane, g, l16);
     __syncthreads();
     f32x4 Y[2][NT], Z[2][NT], Wm[2][NT];
@@ -610,6 +632,7 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyA
     }
   }
   __syncthreads();
+  arr.take_rank(HV, rank_ctr, tid);
   if (wave == 0) {
     build_tt<DK, DV>(sm, al, lane, g, l16);
     if (WAVES == 1) build_c<DK, DV>(sm, al, lane, g, l16);
@@ -620,6 +643,7 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyA
 
   f32x4 Y[2][NT], Z[2][NT], Wm[2][NT];
   contract<DK, DV, NT, kY | kZ>(sm, H, g, l16, Y, Z);
+  arr.grid_in(HV, rank_ctr, grid_ctr, tid);
   if constexpr (NORM) {
     // the gate and weight load while W is solved; out may be absent
     const NormRsrc nr = norm_rsrc(va, r, h, DV, max(D, 1));
@@ -661,7 +685,7 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused_long(Ve
   static_assert(WAVES >= 2, "the T x T matrices are built by waves 0 and 1");
   typedef typename Cols<NT>::F F;
   __shared__ Smem<DK, DV> sm;
-  __shared__ int group_rank, grid_rank;
+  __shared__ int group_rank;
   __shared__ Move moves[64];
 
   const CacheView &c = va.c;
@@ -685,9 +709,9 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused_long(Ve
   const bool lead = (h == 0 && tid == 0);
   int32_t *grid_ctr = c.sync;
   int32_t *rank_ctr = slot_counter(c, blockIdx.x / HV);
-  auto finish = [&]() {
-    end_of_grid<ROLLBACK, VARLEN>(va, rq, mn, rank_ctr, grid_ctr, moves, &grid_rank, tid);
-  };
+  Arrival<ROLLBACK, VARLEN> arr;
+  arr.count_in(rq, rank_ctr, tid);
+  auto finish = [&]() { arr.finish(va, mn, rank_ctr, grid_ctr, moves, tid); };
 
   const int s = rq.s;
   if (s < 0 || s >= c.num_slots) {
@@ -756,6 +780,7 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused_long(Ve
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
   }
+  arr.take_rank(HV, rank_ctr, tid);
   // The thread index comes through an opaque copy so that the per-thread row
   // offsets are recomputed in every iteration rather than held in registers.
 #pragma nounroll
@@ -769,7 +794,8 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused_long(Ve
       __syncthreads();
     }
     // a due slot's fold inputs are all read: count in for the key rows' append
-    if (due && ch == nfold - 1 && tid == 0) group_rank = atomicAdd(group_ctr, 1);
+    // (the last wave waits for the return, which comes after its state loads)
+    if (due && ch == nfold - 1 && tid == 64 * (WAVES - 1)) group_rank = atomicAdd(group_ctr, 1);
     if (wave == 0) build_tt<DK, DV>(sm, al, lane, g, l16);
     __syncthreads();  // T x T matrices complete
     f32x4 Y[2][NT], Z[2][NT], Wm[2][NT];
@@ -805,6 +831,7 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused_long(Ve
   {
     f32x4 Y[2][NT], Z[2][NT], Wm[2][NT];
     contract<DK, DV, NT, kY | kZ>(sm, H, g, l16, Y, Z);
+    arr.grid_in(HV, rank_ctr, grid_ctr, tid);
     solve_w<DK, DV, NT>(sm, Y, col_of(), g, l16, Wm);
     emit_outputs<DK, DV, NT>(sm, Z, Wm, g, l16, t0, Treal, uo.B,
                              out_rsrc(va, r, h, DV, max(Dq, 1)), col_of() * 4, HV * DV * 4);

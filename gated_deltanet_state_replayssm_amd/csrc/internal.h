@@ -123,6 +123,12 @@ struct ConvArgs {
   CacheView c;
   int32_t num_reqs, draft, channels;
   const int32_t *slot_idx;
+  // the previous draft's rollback, not yet applied to len (the one-call step
+  // runs after this call): accepted counts (null: none) and the previous
+  // drafts' lengths (null: prev_draft for every request)
+  const int32_t *prev_accepted;
+  const int32_t *prev_draft_lens;
+  int32_t prev_draft;
   void *ring;            // [num_slots][C][channels] bf16
   const void *x;         // [num_reqs][draft][channels] bf16
   const float *weight;   // [channels][width]

@@ -358,8 +358,24 @@ int gdn_gated_rmsnorm_fp8(int32_t rows, int32_t num_heads, int32_t d_v, const fl
  * where x_{-m} (m >= 1) is conv_ring[s][(h + n - m) mod C][ch]; then the draft x
  * is appended at conv_ring[s][(h + n + j) mod C] (where gdn_replay_verify appends
  * its rows). Pointers are not changed: gdn_replay_rollback and gdn_replay_flush
- * (or verify_flush) move them for both rings. Call it before the step's
- * rollback, with the same slots and D as the step's verify.
+ * (or verify_flush) move them for both rings. Call it before the step's verify,
+ * with the same slots and D.
+ *
+ * Which len: with num_accepted == NULL, len[s] as it stands, i.e. after the
+ * previous draft's rollback (the separate calls: verify, rollback, flush per
+ * step, or verify_flush then rollback). With the one-call step
+ * (gdn_replay_rollback_verify_flush, gdn_replay_step_norm_fp8), whose rollback
+ * of the previous draft happens inside the step after this call, pass the
+ * step's num_accepted, prev_draft_lens and prev_draft: n is then len[s] + a,
+ * exactly the committed count that step works from (len[s] where the step's
+ * rollback fails: a outside [0, previous length], a previous length outside
+ * [0, prev_draft], or len + a > C; the step raises those errors, this call
+ * does not). Either way the draft lands where the step's verify appends its
+ * rows, and its history is the last K - 1 tokens the step has committed.
+ *   num_accepted    [num_reqs] int32 (device) or NULL; prev_draft_lens
+ *                   [num_reqs] int32 or NULL (every previous draft had
+ *                   prev_draft tokens); prev_draft 1..C (host) when
+ *                   num_accepted is given, ignored otherwise.
  *   channels even >= 2; width K in 1..8; D >= 1 with D + K - 1 <= C (the draft
  *   never overwrites the history it reads); inputs bf16 only (in_dtype).
  *   x, y      [num_reqs][D][channels] bf16 (y rounded to nearest even), 4-byte aligned.
@@ -372,8 +388,9 @@ int gdn_gated_rmsnorm_fp8(int32_t rows, int32_t num_heads, int32_t d_v, const fl
  */
 int gdn_causal_conv_update(const gdn_replay_cache *c, void *conv_ring, int32_t channels,
                            int32_t width, int32_t num_reqs, const int32_t *slot_idx,
-                           int32_t draft_len, const void *x, const float *weight,
-                           const float *bias, void *y, hipStream_t stream);
+                           const int32_t *num_accepted, const int32_t *prev_draft_lens,
+                           int32_t prev_draft, int32_t draft_len, const void *x,
+                           const float *weight, const float *bias, void *y, hipStream_t stream);
 
 /*
  * gdn_replay_rollback_verify_flush_noalloc — for callers that cannot allocate

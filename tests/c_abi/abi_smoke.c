@@ -102,8 +102,10 @@ int main(void) {
   CHECK(gdn_gated_rmsnorm_fp8(4, 2, 24, ffake, fake, ffake, 1e-6f, (uint8_t *)fake, ffake, 0) ==
         GDN_EUNSUPPORTED);
   CHECK(gdn_gated_rmsnorm_fp8(0, 2, 128, NULL, NULL, NULL, 1e-6f, NULL, NULL, 0) == GDN_OK);
-  CHECK(gdn_causal_conv_update(&c, fake, 3, 4, 2, ifake, 4, fake, ffake, NULL, fake, 0) ==
-        GDN_EINVAL); /* odd channel count */
+  CHECK(gdn_causal_conv_update(&c, fake, 3, 4, 2, ifake, NULL, NULL, 0, 4, fake, ffake, NULL,
+                               fake, 0) == GDN_EINVAL); /* odd channel count */
+  CHECK(gdn_causal_conv_update(&c, fake, 4, 4, 2, ifake, ifake, NULL, 0, 4, fake, ffake, NULL,
+                               fake, 0) == GDN_EINVAL); /* pending rollback without its length */
 
   printf("%s\n", fails ? "FAILED" : "OK");
   return fails != 0;

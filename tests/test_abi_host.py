@@ -282,6 +282,12 @@ def test_conv_call_validation():
     assert call(x=FAKE + 2) == b.GDN_EINVAL
     assert call(bias=FAKE + 2) == b.GDN_EINVAL
     assert call(num_reqs=0, x=None, conv_ring=None) == b.GDN_OK
+    # the pending rollback of the one-call step: its previous length in 1..C,
+    # aligned counts
+    assert call(num_accepted=FAKE, prev_draft=0) == b.GDN_EINVAL
+    assert call(num_accepted=FAKE, prev_draft=9) == b.GDN_EINVAL
+    assert call(num_accepted=FAKE + 2, prev_draft=4) == b.GDN_EINVAL
+    assert call(num_accepted=FAKE, prev_draft=4, prev_draft_lens=FAKE + 1) == b.GDN_EINVAL
 
 
 def test_grids_past_the_dispatch_limit_are_refused():

@@ -131,3 +131,68 @@ def test_conv_device_errors():
     assert (yh[1:3] == 7.0).all() and (yh[[0, 3]] != 7.0).all()
     ring = to_host(conv.ring)
     assert not ring[[2, 3]].any() and ring[0].any() and ring[1].any()
+
+
+def _run_one_call(wl, CH, K, steps, seed, bad_accept=False):
+    """The convolution composed with the one-call step: per step, the
+    convolution (given the step's pending rollback) and then
+    gdn_replay_rollback_verify_flush, on one cache; the oracle side commits the
+    previous draft's accepted prefix first and evaluates the convolution from
+    the committed count that gives, then runs verify_flush. With bad_accept, one
+    request per step passes an accepted count above its previous draft's length:
+    the step keeps its len (and flags ACCEPT), and so must the convolution."""
+    rng = np.random.default_rng(seed)
+    init = synth.make_cache_init(wl, rng)
+    cache = ReplayCache.from_numpy(init, wl.hv, wl.hk, wl.dk, wl.dv, wl.cap, wl.in_dtype)
+    conv = ConvRing(cache, CH, K)
+    orc_ptr = go.ReplayOracle(init, wl.hv, wl.hk, wl.dk, wl.dv, wl.cap, mode="replay")
+    orc = co.ConvOracle(np.zeros((wl.num_slots, wl.cap, CH), np.uint16), wl.cap)
+    w = rng.standard_normal((CH, K)).astype(np.float32) * 0.5
+    bias = rng.standard_normal(CH).astype(np.float32)
+    wd, bd = to_device(w), to_device(bias)
+    D = wl.draft
+    pending = {}
+    amb = 0
+    for step in range(steps):
+        slots = synth.make_slot_idx(wl, rng)
+        lens = rng.integers(0, D + 1, wl.num_reqs).astype(np.int32)
+        acc = synth.sample_accepted(wl, rng, draft_lens=lens)
+        pa = np.array([pending.get(int(s), (0, 0))[0] for s in slots], np.int32)
+        pl = np.array([pending.get(int(s), (0, 0))[1] for s in slots], np.int32)
+        if bad_accept and step > 0:
+            pa[0] = pl[0] + 1
+        x = synth.f32_to_bf16_bits(rng.standard_normal((wl.num_reqs, D, CH)).astype(np.float32))
+        dr = synth.make_draft(wl, rng)
+        say(f"  step {step} pa={list(pa)} pl={list(pl)} lens={list(lens)}")
+        sd, pad, pld, ld = to_device(slots), to_device(pa), to_device(pl), to_device(lens)
+        y = conv.update(sd, to_device(x), wd, bd, num_accepted=pad, prev_draft=D,
+                        prev_draft_lens=pld)
+        dd = {k: to_device(v) for k, v in dr.items()}
+        cache.rollback_verify_flush(sd, pad, D, wl.flush_min_len, dd["q"], dd["k"], dd["v"],
+                                    dd["alpha"], dd["beta"], prev_draft_lens=pld, draft_lens=ld)
+        torch.cuda.synchronize()
+        orc_ptr.rollback(slots, D, pa, draft_lens=pl)
+        ref, mag = orc.update(orc_ptr.head.copy(), orc_ptr.len.copy(), slots, x, w, bias,
+                              magnitudes=True)
+        orc_ptr.verify_flush(slots, wl.flush_min_len,
+                             *(dr[k] for k in ("q", "k", "v", "alpha", "beta")), draft_lens=lens)
+        # rows past a request's draft length are computed by the convolution
+        # (it takes the fixed block) and compared too
+        amb += _check_out(to_host(y), ref, mag)
+        assert np.array_equal(to_host(conv.ring), orc.ring), f"conv ring differs at step {step}"
+        assert np.array_equal(to_host(cache.head), orc_ptr.head.astype(np.int32))
+        assert np.array_equal(to_host(cache.len), orc_ptr.len.astype(np.int32))
+        assert int(cache.err.item()) == orc_ptr.err
+        pending = {int(s): (int(acc[i]), int(lens[i])) for i, s in enumerate(slots)}
+    return amb
+
+
+@pytest.mark.parametrize("bad_accept", [False, True])
+def test_conv_composes_with_the_one_call_step(bad_accept):
+    """Convolution then rollback_verify_flush, every step, per-request draft
+    lengths, ring capacity 32 shared by both rings, flush every 8."""
+    wl = synth.Workload("cv1", 6, 8, 4, 2, 64, 64, 32, 8, synth.BF16, 8, 1, "uniform",
+                        "uniform:0:15")
+    say(f"case conv + one-call step, bad_accept={bad_accept}")
+    amb = _run_one_call(wl, 384, 4, 10, 740 + bad_accept, bad_accept=bad_accept)
+    say(f"  {amb} outputs at a bf16 rounding midpoint")

@@ -223,36 +223,96 @@ def conv_leg(wl, layers, steps, warmup, width=4):
             "what": f"causal conv width {width} over [{R}][{D}][{CH}] with ring history"}
 
 
-def cpu_baseline(wl, seconds_budget=15.0):
-    """The fp64 oracle, as it stands, on a bounded sample of the same workload:
-    verify + rollback + flush of whole layers (every request, buffer 5 + draft D,
-    every slot flushed) until about `seconds_budget` seconds of CPU work."""
+# ---------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle on the host's cores
+# ---------------------------------------------------------------------------
+_CPU = {}   # inputs of the pool's workers, inherited by fork (set before the pool starts)
+
+
+def _cpu_worker(k):
+    """Slots s with s % n == k of one layer, through the steps the GPU timed:
+    verify_flush then rollback per step (the fused order), untimed up to the
+    first timed step. Returns the seconds spent in the timed steps."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import gdn_oracle as go
+    c = _CPU
+    wl, n, steps, timed_from = c["wl"], c["n"], c["steps"], c["timed_from"]
+    orc = go.ReplayOracle(c["init"], wl.hv, wl.hk, wl.dk, wl.dv, wl.cap, mode="replay")
+    spent = 0.0
+    with threadpool_limits(limits=1):
+        for i, (slots, acc, dl) in enumerate(steps):
+            mine = np.array([j for j, sl in enumerate(slots) if sl % n == k], dtype=np.int64)
+            if not len(mine):
+                continue
+            d = c["drafts"][i % 2]
+            t0 = time.perf_counter()
+            orc.verify_flush(slots[mine], wl.flush_min_len,
+                             *(d[x][mine] for x in ("q", "k", "v", "alpha", "beta")),
+                             draft_lens=None if dl is None else dl[mine])
+            orc.rollback(slots[mine], wl.draft, acc[mine],
+                         draft_lens=None if dl is None else dl[mine])
+            if i >= timed_from:
+                spent += time.perf_counter() - t0
+    return spent
+
+
+def cpu_baseline(wl, init, drafts, steps, warmup, max_cores=16, max_timed=10):
+    """The fp64 oracle, as it stands, on the schedule the GPU timed: layer 0's
+    cache, its two draft sets alternated as on the GPU, and the same slot
+    permutation, accepted counts and draft lengths per step, in the fused order
+    (verify_flush then rollback; the lengths at verify and the folded slots are
+    therefore those of the GPU's steps). Steps before the GPU's first timed
+    step run untimed; the first max_timed of the GPU's timed steps are timed
+    (a bounded sample: tens of seconds of CPU work). The slots are split over len(os.sched_getaffinity(0))
+    worker processes (at most max_cores; a slot's trajectory is independent of
+    the others'), each with one BLAS thread; the value is the slowest worker's
+    time per timed step, in us per layer. Runs before the GPU is touched (the
+    workers are forked)."""
+    import multiprocessing as mp
+    n = max(1, min(len(os.sched_getaffinity(0)), max_cores, wl.num_slots))
+    steps = steps[:warmup + max_timed]
+    _CPU.update(wl=wl, n=n, steps=steps, timed_from=warmup, init=init, drafts=drafts)
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(n) as pool:
+        spent = pool.map(_cpu_worker, range(n))
+    wall = time.perf_counter() - t0
+    timed = len(steps) - warmup
+    return {"value": round(max(spent) / timed * 1e6, 1), "unit": "us/layer", "cores": n,
+            "kind": "oracle",
+            "sample": f"layer 0 of {wl.name}: steps {warmup}..{len(steps) - 1} of the GPU's "
+                      f"schedule timed ({warmup} earlier steps untimed), verify_flush + "
+                      f"rollback of {wl.num_reqs} requests per step; fp64 NumPy, slots split "
+                      f"over {n} processes of 1 thread, slowest process's time; "
+                      f"{sum(spent):.1f} s of CPU work timed, {wall:.1f} s wall"}
+
+
+def cpu_single_thread(workload="r8_hv32_hk16_d128", layers=8):
+    """The oracle on one thread for a small workload (8 requests): one verify ->
+    rollback -> flush of every request per layer, us per layer."""
     from threadpoolctl import threadpool_limits
 
     from gated_deltanet_state_replayssm_amd import synth
     from oracle import gdn_oracle as go
-
-    done = 0
+    wl = synth.WORKLOADS[workload]
     spent = 0.0
-    while spent < seconds_budget and done < wl.layers:
-        rng = np.random.default_rng(synth.seed_for(wl.name, done, 999))
-        init = synth.make_cache_init(wl, rng, init_len=np.full(wl.num_slots, 5, np.int32))
-        orc = go.ReplayOracle(init, wl.hv, wl.hk, wl.dk, wl.dv, wl.cap, mode="replay")
-        dr = synth.make_draft(wl, rng)
-        slots = np.arange(wl.num_reqs, dtype=np.int32)
-        acc = synth.sample_accepted(wl, rng)
-        with threadpool_limits(limits=1):
+    with threadpool_limits(limits=1):
+        for L in range(layers):
+            rng = np.random.default_rng(synth.seed_for(wl.name, L, 0))
+            init = synth.make_cache_init(wl, rng)
+            orc = go.ReplayOracle(init, wl.hv, wl.hk, wl.dk, wl.dv, wl.cap, mode="replay")
+            slots = synth.make_slot_idx(wl, rng)
+            dr = synth.make_draft(wl, rng)
+            acc = synth.sample_accepted(wl, rng)
             t0 = time.perf_counter()
             orc.verify(slots, dr["q"], dr["k"], dr["v"], dr["alpha"], dr["beta"])
             orc.rollback(slots, wl.draft, acc)
             orc.flush(slots, 1)
             spent += time.perf_counter() - t0
-        done += 1
-    us_per_layer = spent / done * 1e6
-    return {"value": round(us_per_layer, 1), "unit": "us/layer", "cores": 1, "kind": "oracle",
-            "sample": f"{done} whole layer(s) of {wl.num_reqs} requests, committed buffer 5 + "
-                      f"draft {wl.draft}, every slot flushed; fp64 NumPy, 1 thread, "
-                      f"{spent:.1f} s timed"}
+    return {"value": round(spent / layers * 1e6, 1), "unit": "us/layer", "cores": 1,
+            "kind": "oracle", "workload": wl.name,
+            "sample": f"{layers} layers of {wl.name}: one verify -> rollback -> flush of "
+                      f"{wl.num_reqs} requests each; fp64 NumPy, 1 thread"}
 
 
 def sweep(args, workload="r32_hv32_hk16_d128_f64", buffer_lens=(0, 8, 16, 32, 48, 63),
@@ -368,9 +428,35 @@ def main():
               "build runs on a single MI355X (--gpus 1).", file=sys.stderr)
         sys.exit(2)
 
+    from gated_deltanet_state_replayssm_amd import synth
+
+    wl = synth.WORKLOADS[args.workload]
+    layers = args.layers or wl.layers
+    total = args.warmup + args.steps
+    # host-side inputs first: the CPU baseline runs on them before the GPU is touched
+    inits = []
+    for L in range(layers):
+        inits.append(synth.make_cache_init(wl, np.random.default_rng(synth.seed_for(wl.name, L, 0))))
+    init_len = inits[0]["len"].astype(np.int64)
+    # two draft sets per layer, alternated: values do not change the work done
+    host_drafts = []
+    for L in range(layers):
+        host_drafts.append([synth.make_draft(wl, np.random.default_rng(synth.seed_for(wl.name, L, 50 + j)))
+                            for j in range(2)])
+    rng = np.random.default_rng(synth.seed_for(wl.name, 0, 0))
+    steps = []
+    for _ in range(total):
+        slots = synth.make_slot_idx(wl, rng)
+        lens = synth.sample_draft_lens(wl, rng)   # None: every request drafts wl.draft
+        steps.append((slots, synth.sample_accepted(wl, rng, draft_lens=lens), lens))
+    cpu = None
+    if not args.no_cpu and not args.sweep:
+        cpu = cpu_baseline(wl, inits[0], host_drafts[0], steps, args.warmup)
+        cpu["single_thread"] = cpu_single_thread()
+
     import torch
 
-    from gated_deltanet_state_replayssm_amd import binding, synth
+    from gated_deltanet_state_replayssm_amd import binding
     from gated_deltanet_state_replayssm_amd.cache import ReplayCache, to_device
 
     binding.load()
@@ -380,8 +466,6 @@ def main():
     if args.sweep:
         sweep(args)
         return
-    wl = synth.WORKLOADS[args.workload]
-    layers = args.layers or wl.layers
     stream = torch.cuda.current_stream()
     # the step with the norm takes the single-chunk shapes only (its entry point
     # refuses others): bf16 inputs, d in {64, 128}, ring capacity and draft <= 32
@@ -390,27 +474,11 @@ def main():
     paths = (("fused", "separate", "step") + (("step_norm",) if norm_ok else ())
              if args.path == "all" else (args.path,))
 
-    inits = []
-    for L in range(layers):
-        inits.append(synth.make_cache_init(wl, np.random.default_rng(synth.seed_for(wl.name, L, 0))))
-    init_len = inits[0]["len"].astype(np.int64)
-    # two draft sets per layer, alternated: values do not change the work done
-    drafts = []
-    for L in range(layers):
-        ds = []
-        for j in range(2):
-            d = synth.make_draft(wl, np.random.default_rng(synth.seed_for(wl.name, L, 50 + j)))
-            ds.append({k: to_device(v) for k, v in d.items()})
-        drafts.append(ds)
-    out = torch.empty((wl.num_reqs, wl.draft, wl.hv, wl.dv), dtype=torch.float32, device="cuda")
-
-    total = args.warmup + args.steps
-    rng = np.random.default_rng(synth.seed_for(wl.name, 0, 0))
-    steps = []
-    for _ in range(total):
-        slots = synth.make_slot_idx(wl, rng)
-        lens = synth.sample_draft_lens(wl, rng)   # None: every request drafts wl.draft
-        steps.append((slots, synth.sample_accepted(wl, rng, draft_lens=lens), lens))
+    drafts = [[{k: to_device(v) for k, v in d.items()} for d in ds] for ds in host_drafts]
+    # each layer writes its own outputs (one shared buffer would stay in the
+    # Infinity Cache and understate the write traffic)
+    outs = [torch.empty((wl.num_reqs, wl.draft, wl.hv, wl.dv), dtype=torch.float32, device="cuda")
+            for _ in range(layers)]
     F = max(wl.flush_min_len, 1)
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
@@ -459,7 +527,7 @@ def main():
         ptr = lambda t: None if t is None else t.data_ptr()
         dptr = [[tuple(d[x].data_ptr() for x in ("q", "k", "v", "alpha", "beta")) for d in ds]
                 for ds in drafts]
-        R, D, FM, outp = wl.num_reqs, wl.draft, wl.flush_min_len, out.data_ptr()
+        R, D, FM = wl.num_reqs, wl.draft, wl.flush_min_len
         norms = []
         if path == "step_norm":   # per-layer gate, codes and scales; one weight
             g = torch.Generator(device="cuda").manual_seed(synth.seed_for(wl.name, 0, 94))
@@ -479,7 +547,7 @@ def main():
             sl, dl = ptr(sc["slots"]), ptr(sc["dl"])
             main, rb, fl = [], [], []
             for L in range(layers):
-                dp = dptr[L][step % 2] + (outp, sh)
+                dp = dptr[L][step % 2] + (outs[L].data_ptr(), sh)
                 if path == "fused":
                     main.append((lib.gdn_replay_verify_flush, (refs[L], R, sl, D, FM) + dp)
                                 if dl is None else
@@ -586,12 +654,12 @@ def main():
                 if path == "step":
                     caches[L].rollback_verify_flush(slots_buf, bufs["pacc"], wl.draft,
                                                     wl.flush_min_len, dd["q"], dd["k"], dd["v"],
-                                                    dd["alpha"], dd["beta"], out=out,
+                                                    dd["alpha"], dd["beta"], out=outs[L],
                                                     prev_draft_lens=bufs["plens"],
                                                     draft_lens=dl_buf)
                 else:
                     caches[L].verify_flush(slots_buf, wl.flush_min_len, dd["q"], dd["k"],
-                                           dd["v"], dd["alpha"], dd["beta"], out=out,
+                                           dd["v"], dd["alpha"], dd["beta"], out=outs[L],
                                            draft_lens=dl_buf)
             if path != "step":
                 for L in range(layers):
@@ -666,7 +734,7 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f32 state, bf16 hi/lo-split MFMA",
         "data": "synthetic",
         "config": {"workload": wl.name, "requests": wl.num_reqs, "v_heads": wl.hv,
                    "k_heads": wl.hk, "d_k": wl.dk, "d_v": wl.dv, "draft": wl.draft,
@@ -715,8 +783,8 @@ def main():
         line["separate_order"] = {"us_per_layer": round(sp["us_layer"], 2),
                                   "hbm_gbps": round(sp["gbps"], 1),
                                   "bytes_per_layer": int(sp["bytes_layer"])}
-    if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(wl)
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
 
 

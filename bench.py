@@ -257,7 +257,7 @@ def _cpu_worker(k):
     return spent
 
 
-def cpu_baseline(wl, init, drafts, steps, warmup, max_cores=16, max_timed=10):
+def cpu_baseline(wl, init, drafts, steps, warmup, max_cores=16, max_timed=30):
     """The fp64 oracle, as it stands, on the schedule the GPU timed: layer 0's
     cache, its two draft sets alternated as on the GPU, and the same slot
     permutation, accepted counts and draft lengths per step, in the fused order

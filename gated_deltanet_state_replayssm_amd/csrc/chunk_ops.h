@@ -102,6 +102,38 @@ struct Smem {
   float lgc[kCh];                  // the same, from the scan of the wave that builds Cm
 };
 
+// The arrays of Smem as LDS variables of their own, seen through one view (the
+// long replays, whose keys, values and queries arrive by LDS DMA while other
+// arrays are read). The compiler waits for an LDS DMA before every LDS access
+// it cannot tell apart from the DMA's writes; accesses to other variables it
+// can, so the DMA targets are variables of their own.
+template <int DK>
+union SmemQK {
+  uint16_t q[kCh][DK + kPadK];
+  uint16_t kt[DK][kCh + kPadT];
+};
+struct SmemMats {
+  float T[kCh][kCh + kPadF];
+  float Cm[kCh][kCh + kPadF];
+  float gam[kCh];
+  float lg[kCh];
+  float lgc[kCh];
+};
+template <int DK, int DV>
+struct SmemView {
+  uint16_t (&k)[kCh][DK + kPadK];
+  uint16_t (&q)[kCh][DK + kPadK];
+  uint16_t (&kt)[DK][kCh + kPadT];
+  uint16_t (&v)[kCh][DV + kPadK];
+  float (&T)[kCh][kCh + kPadF];
+  float (&Cm)[kCh][kCh + kPadF];
+  float (&gam)[kCh];
+  float (&bet)[kCh];
+  float (&alp)[kCh];
+  float (&lg)[kCh];
+  float (&lgc)[kCh];
+};
+
 // 8 bf16 of a token row in k-step s order: columns 32s+4g+{0..3}, 32s+16+4g+{0..3}
 template <int W>
 __device__ __forceinline__ bf16x8 rd_row(const uint16_t (*m)[W], int row, int col0) {
@@ -362,7 +394,8 @@ struct Stage {
     }
   }
 
-  __device__ __forceinline__ void store(Smem<DK, DV> &sm, int Treal, bool out_chunk) {
+  template <class SM>
+  __device__ __forceinline__ void store(SM &sm, int Treal, bool out_chunk) {
     const int tid = opaque_tid();
 #pragma unroll
     for (int it = 0; it < IK; ++it) {
@@ -393,7 +426,8 @@ struct Stage {
 
   // Verify's output chunk: write the draft rows to ring slots (head + B + j) mod C,
   // from LDS (one workgroup per key head writes k and q).
-  __device__ __forceinline__ void append(const Smem<DK, DV> &sm, const Srcs &sr, const Unit &u,
+  template <class SM>
+  __device__ __forceinline__ void append(const SM &sm, const Srcs &sr, const Unit &u,
                                          int t0, int Treal, bool kq_writer) const {
     const int tid = opaque_tid();
     // Recompute the row offsets here rather than keep those of the loads alive
@@ -423,6 +457,155 @@ struct Stage {
     }
   }
 };
+
+// ---- Staging the next chunk while the current one is computed (long replays)
+//
+// A barrier for LDS traffic only: this wave's LDS accesses are complete
+// (lgkmcnt) and no wave passes before all arrive. __syncthreads() also waits
+// for every LDS DMA this wave has in flight (its workgroup-scope release covers
+// writes to LDS by DMA), which would end the overlap the DMA is for. The
+// signal fences keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt untouched
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// One LDS DMA load: 16 bytes per lane from a buffer resource straight into LDS,
+// lane l writing bytes [16 l, 16 l + 16) from lds (uniform across the wave); no
+// registers are written and the wave runs on. An offset past the resource's
+// end writes zeros; lanes switched off leave LDS untouched.
+template <int AUX>
+__device__ __forceinline__ void dma16(Rsrc r, char *lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16,
+                                           voff, 0, 0, AUX);
+}
+
+// Rows 0 .. kCh - 1 of a padded token-major bf16 array [kCh][W + kPadK] in LDS
+// by LDS DMA, the instructions dealt to waves [0, NW) (wv: the caller's wave,
+// uniform). Instruction i writes the array's bytes [1024 i, 1024 i + 1024):
+// lane l the 16-byte piece p = 64 i + l, which is piece p mod PR of row p / PR
+// (PR pieces per row, the last one the row's padding: data = false, read from
+// nowhere). Lanes past the array's end are switched off. src(t, pc, dst, data)
+// issues the load of piece pc of row t.
+template <int W, int NW, typename F>
+__device__ __forceinline__ void dma_rows(uint16_t (*rows)[W + kPadK], int wv, int lane, F &&src) {
+  static_assert((W + kPadK) % 8 == 0, "rows of whole 16-byte pieces");
+  constexpr int PR = (W + kPadK) / 8, NP = kCh * PR, NI = (NP + 63) / 64;
+  char *base = reinterpret_cast<char *>(&rows[0][0]);
+  // every instruction's LDS address a constant offset into the array, so that
+  // the compiler sees which LDS reads the DMA cannot touch (it waits for the
+  // DMA before any LDS access it cannot tell apart)
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    if (i % NW == wv) {
+      const int p = 64 * i + lane;
+      if (NP % 64 == 0 || i < NI - 1 || p < NP) {
+        const int t = p / PR, pc = p - t * PR;
+        src(t, pc, base + 1024 * i, pc < PR - 1);
+      }
+    }
+  }
+}
+
+// One LDS DMA load of 4 bytes per lane (lane l writes lds + 4 l).
+template <int AUX>
+__device__ __forceinline__ void dma4(Rsrc r, char *lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 4,
+                                           voff, 0, 0, AUX);
+}
+
+// The staging of one chunk (rows [t0, t0 + Treal) of a token stream) issued
+// while the previous chunk is computed, all of it by LDS DMA (no registers stay
+// in flight across the chunk loop): keys once the previous chunk's contraction
+// has read its keys; values, beta and alpha once W has read the previous
+// values and beta; queries (output chunk) once the fold has read the
+// transposed keys that share their array. Rows past Treal, and committed rows'
+// queries, come in as zeros (a reader takes alpha = 1 past Treal). The caller's
+// barriers while the DMA is in flight are lds_barrier(); the next
+// __syncthreads() waits for it.
+template <int DK, int DV, int NW>
+struct Prefetch {
+  template <class SM>
+  __device__ __forceinline__ void issue_k(SM &sm, const Srcs &sr, const Unit &u, int t0,
+                                          int Treal) const {
+    const int tid = opaque_tid(), lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    dma_rows<DK, NW>(sm.k, wv, lane, [&](int t, int pc, char *dst, bool data) {
+      const RowAt<true> at(u, t0, t, Treal, DK * 2, sr.dk_row);
+      if (data && at.ring != kOOB)
+        dma16<0>(sr.rk, dst, at.ring + pc * 16);
+      else
+        dma16<kStream>(sr.dk, dst, data ? at.draft + pc * 16 : kOOB);
+    });
+  }
+
+  template <class SM>
+  __device__ __forceinline__ void issue_v(SM &sm, const Srcs &sr, const Unit &u, int t0,
+                                          int Treal) const {
+    const int tid = opaque_tid(), lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    dma_rows<DV, NW>(sm.v, wv, lane, [&](int t, int pc, char *dst, bool data) {
+      const RowAt<true> at(u, t0, t, Treal, DV * 2, sr.dv_row);
+      if (data && at.ring != kOOB)
+        dma16<0>(sr.rv, dst, at.ring + pc * 16);
+      else
+        dma16<kStream>(sr.dv, dst, data ? at.draft + pc * 16 : kOOB);
+    });
+    // beta then alpha (sm.bet and sm.alp adjacent): lane l < 32 beta of row l,
+    // lane 32 + l alpha of row l; by the last wave
+    if (wv == NW - 1) {
+      const int t = lane & (kCh - 1);
+      const RowAt<true> at(u, t0, t, Treal, 4, sr.dab_row);
+      char *dst = reinterpret_cast<char *>(&sm.bet[0]);
+      if (at.ring != kOOB) {
+        if (lane < kCh)
+          dma4<0>(sr.rb, dst, at.ring);
+        else
+          dma4<0>(sr.ra, dst, at.ring);
+      } else {
+        if (lane < kCh)
+          dma4<kStream>(sr.db, dst, at.draft);
+        else
+          dma4<kStream>(sr.da, dst, at.draft);
+      }
+    }
+  }
+
+  // the output chunk's queries (draft rows only), into the array that held the
+  // transposed keys of the folded chunks
+  template <class SM>
+  __device__ __forceinline__ void issue_q(SM &sm, const Srcs &sr, const Unit &u, int t0,
+                                          int Treal) const {
+    const int tid = opaque_tid(), lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    dma_rows<DK, NW>(sm.q, wv, lane, [&](int t, int pc, char *dst, bool data) {
+      const RowAt<true> at(u, t0, t, Treal, DK * 2, sr.dk_row);
+      dma16<kStream>(sr.dq, dst, data ? at.draft + pc * 16 : kOOB);
+    });
+  }
+};
+
+// The keys of a chunk transposed for the fold (sm.kt[d][t] = sm.k[t][d]), by
+// the NTHR threads j = 0 .. NTHR - 1 of the caller's numbering. A task is one
+// key column and 8 tokens: eight 2-byte reads, one 16-byte write.
+template <int DK, int DV, int NTHR, class SM>
+__device__ __forceinline__ void keys_to_kt(SM &sm, int j) {
+  constexpr int TASKS = DK * (kCh / 8);
+#pragma unroll
+  for (int it = 0; it < (TASKS + NTHR - 1) / NTHR; ++it) {
+    const int p = j + it * NTHR;
+    if (TASKS % NTHR == 0 || p < TASKS) {
+      const int d = p % DK, t0 = 8 * (p / DK);
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        w[e] = (uint32_t)sm.k[t0 + 2 * e][d] | ((uint32_t)sm.k[t0 + 2 * e + 1][d] << 16);
+      *reinterpret_cast<u32x4 *>(&sm.kt[d][t0]) = u32x4{w[0], w[1], w[2], w[3]};
+    }
+  }
+}
 
 // Inclusive scan over lanes 0..31 of a wave with DPP row shifts (within rows of
 // 16 lanes) and a row broadcast of lane 15 into the second row. Lanes 32..63 get
@@ -500,8 +683,8 @@ __device__ __forceinline__ void decay_tiles(const float *lg, int g, int l16, flo
 // C = L o (Q K^T), lower triangle including the diagonal (output chunk only).
 // Built by another wave than A and its inverse, from its own decay scan (kept
 // in sm.lgc), so the two run side by side; it writes only sm.Cm and sm.lgc.
-template <int DK, int DV>
-__device__ __forceinline__ void build_c(Smem<DK, DV> &sm, float al_staged, int lane, int g, int l16) {
+template <int DK, int DV, class SM>
+__device__ __forceinline__ void build_c(SM &sm, float al_staged, int lane, int g, int l16) {
   // issue priority meanwhile, as build_tt
   __builtin_amdgcn_s_setprio(3);
   {
@@ -530,8 +713,8 @@ __device__ __forceinline__ void build_c(Smem<DK, DV> &sm, float al_staged, int l
 // gamma and lg, built by one wave (no workgroup barriers inside: each step reads
 // only what this wave wrote, in program order). al_staged is this lane's staged
 // alpha, of token lane % 32.
-template <int DK, int DV>
-__device__ __forceinline__ void build_tt(Smem<DK, DV> &sm, float al_staged, int lane, int g, int l16) {
+template <int DK, int DV, class SM>
+__device__ __forceinline__ void build_tt(SM &sm, float al_staged, int lane, int g, int l16) {
   // The T x T matrices are one wave's work on every workgroup's critical path;
   // the wave takes issue priority over the other waves of its SIMD meanwhile.
   __builtin_amdgcn_s_setprio(3);
@@ -697,8 +880,8 @@ enum { kY = 1, kZ = 2 };
 // Y = K H and/or Z = Q H over d_k on MFMA, the state split into hi + lo bf16.
 // Both products share one split per k-step; a Z-only pass splits with
 // truncation so that it is never merged with (and kept alive from) a Y pass.
-template <int DK, int DV, int NT, int WHAT>
-__device__ __forceinline__ void contract(const Smem<DK, DV> &sm,
+template <int DK, int DV, int NT, int WHAT, class SM>
+__device__ __forceinline__ void contract(const SM &sm,
                                          const typename Cols<NT>::F (&H)[DK / 16][4], int g,
                                          int l16, f32x4 (&Y)[2][NT], f32x4 (&Z)[2][NT]) {
   constexpr int KS = DK / 32;
@@ -745,8 +928,8 @@ __device__ __forceinline__ void contract(const Smem<DK, DV> &sm,
 
 // X = beta (V - gamma Y), then W = (I + A)^-1 X (3-pass split product); this
 // lane's v entries are rows 16 a + 4 g + i, columns colL .. colL + NT - 1.
-template <int DK, int DV, int NT>
-__device__ __forceinline__ void solve_w(const Smem<DK, DV> &sm, const f32x4 (&Y)[2][NT], int colL,
+template <int DK, int DV, int NT, class SM>
+__device__ __forceinline__ void solve_w(const SM &sm, const f32x4 (&Y)[2][NT], int colL,
                                         int g, int l16, f32x4 (&Wm)[2][NT]) {
   typedef typename Cols<NT>::U U;
   bf16x8 xh[NT], xl[NT];
@@ -798,8 +981,8 @@ __device__ __forceinline__ Rsrc out_rsrc(const VerifyArgs &va, int r, int h, int
 
 // Draft outputs O = gamma Z + C W of chunk rows t (token t0 + t >= B, t < Treal).
 // out holds out[r][0..D-1][h][*] (rows row_bytes apart); col_off = 4 colL.
-template <int DK, int DV, int NT>
-__device__ __forceinline__ void emit_outputs(const Smem<DK, DV> &sm, const f32x4 (&Z)[2][NT],
+template <int DK, int DV, int NT, class SM>
+__device__ __forceinline__ void emit_outputs(const SM &sm, const f32x4 (&Z)[2][NT],
                                              const f32x4 (&Wm)[2][NT], int g, int l16, int t0,
                                              int Treal, int B, Rsrc out, uint32_t col_off,
                                              uint32_t row_bytes) {
@@ -843,8 +1026,8 @@ __device__ __forceinline__ void emit_outputs(const Smem<DK, DV> &sm, const f32x4
 }
 
 // Fold the chunk into the state: H <- gamma_T H + K^T (L[T-1] o W).
-template <int DK, int DV, int NT>
-__device__ __forceinline__ void fold_state(const Smem<DK, DV> &sm, const f32x4 (&Wm)[2][NT], int g,
+template <int DK, int DV, int NT, class SM>
+__device__ __forceinline__ void fold_state(const SM &sm, const f32x4 (&Wm)[2][NT], int g,
                                            int l16, typename Cols<NT>::F (&H)[DK / 16][4]) {
   constexpr int MT = DK / 16;
   const float gT = sm.gam[kCh - 1], lg31 = sm.lg[kCh - 1];

@@ -75,8 +75,8 @@ __device__ __forceinline__ float row16_reduce(float v) {
 // (OCP E4M3, round to nearest even, saturating). A row's DV values lie in one
 // DPP row (16 lanes) of each wave: sums and maxima are reduced over the lanes
 // with DPP moves, then across the waves through red[2][32][4] in LDS.
-template <int DK, int DV, int NT>
-__device__ __forceinline__ void emit_outputs_norm(const Smem<DK, DV> &sm,
+template <int DK, int DV, int NT, class SM>
+__device__ __forceinline__ void emit_outputs_norm(const SM &sm,
                                                   const f32x4 (&Z)[2][NT],
                                                   const f32x4 (&Wm)[2][NT], int g, int l16,
                                                   int wave, int Treal, int B, Rsrc out, int col,
@@ -684,7 +684,13 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused_long(Ve
   static_assert(DK % 32 == 0 && DV % (16 * NT) == 0 && (NT == 2 || NT == 4), "tile shape");
   static_assert(WAVES >= 2, "the T x T matrices are built by waves 0 and 1");
   typedef typename Cols<NT>::F F;
-  __shared__ Smem<DK, DV> sm;
+  __shared__ __align__(16) uint16_t lds_k[kCh][DK + kPadK];
+  __shared__ __align__(16) uint16_t lds_v[kCh][DV + kPadK];
+  __shared__ __align__(16) SmemQK<DK> lds_qk;
+  __shared__ __align__(16) SmemMats lds_m;
+  __shared__ __align__(16) float lds_ab[2][kCh];  // beta, alpha (filled by one DMA)
+  const SmemView<DK, DV> sm{lds_k,     lds_qk.q,  lds_qk.kt, lds_v,     lds_m.T,  lds_m.Cm,
+                            lds_m.gam, lds_ab[0], lds_ab[1], lds_m.lg, lds_m.lgc};
   __shared__ int group_rank;
   __shared__ Move moves[64];
 
@@ -755,14 +761,36 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused_long(Ve
   // the register-bound body do not fit the registers). The stream u1 starts at
   // head with the n committed tokens: a due slot's stream is those n tokens,
   // all folded (its state is then written and the draft verified from it as a
-  // stream of its own, B = 0); any other slot's is the n tokens and the draft,
-  // whose last chunk is the output chunk.
+  // stream of its own, B = 0, from where the folded tokens end); any other
+  // slot's is the n tokens and the draft, whose last chunk is the output chunk.
   const Unit u1{r, h, s, kh, head, n, due ? n : n + Dq, C};
+  const int hd = head + n - (head + n >= C ? C : 0);
+  const Unit ud{r, h, s, kh, hd, 0, Dq, C};
   const Srcs s1 = due ? make_srcs<DK, DV>(c, u1, nullptr, false)
                       : make_srcs<DK, DV>(c, u1, &va, true);
+  // The output chunk's resources (draft rows sized for Dq), built where they
+  // are used: kept across the chunk loop, they took scalar registers the loop
+  // needs and it spilled. The draft pointers come through opaque copies so
+  // that the compiler does not hoist the resources out of the loop.
+  auto out_srcs = [&]() {
+    VerifyArgs v2 = va;
+    const void *pk = va.k, *pq = va.q, *pv = va.v;
+    const float *pa = va.alpha, *pb = va.beta;
+    asm volatile("" : "+s"(pk), "+s"(pq), "+s"(pv), "+s"(pa), "+s"(pb));
+    v2.k = pk;
+    v2.q = pq;
+    v2.v = pv;
+    v2.alpha = pa;
+    v2.beta = pb;
+    return make_srcs<DK, DV>(c, due ? ud : u1, &v2, true);
+  };
   const int nch = (u1.T + kCh - 1) / kCh, T0 = u1.T - kCh * (nch - 1);
   const int nfold = due ? nch : nch - 1;
   const bool out0 = !due && nch == 1;  // chunk 0 is the output chunk
+  // the output chunk: the draft of a due slot, else the stream's last chunk
+  const Unit uo = due ? ud : u1;
+  const int t0 = due ? 0 : (nch == 1 ? 0 : T0 + kCh * (nch - 2));
+  const int Treal = due ? Dq : (nch == 1 ? T0 : kCh);
   {
     // waves SW.. load their state first; waves 0..SW-1 stage chunk 0, then load.
     // One load_state for both, so that the state is assigned its registers once
@@ -781,47 +809,56 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused_long(Ve
     __syncthreads();
   }
   arr.take_rank(HV, rank_ctr, tid);
+  // Every chunk after the first is staged while its predecessor is computed:
+  // its keys (with alpha and beta) once the contraction has read the previous
+  // keys, its values once W has read the previous values, by LDS DMA, so that
+  // the chunk is in LDS when the fold ends; the fold chunks' transposed keys are
+  // then made from the keys in LDS while wave 0 builds the T x T matrices.
+  Prefetch<DK, DV, WAVES> pf;
   // The thread index comes through an opaque copy so that the per-thread row
   // offsets are recomputed in every iteration rather than held in registers.
 #pragma nounroll
   for (int ch = 0; ch < nfold; ++ch) {
     const int lane = opaque_tid() % 64, g = lane >> 4, l16 = lane & 15;
-    if (ch > 0) {
-      Stage<DK, DV, NT, true> sg;
-      sg.load(s1, u1, T0 + kCh * (ch - 1), kCh, false);
-      sg.store(sm, kCh, false);
-      al = sg.al;
-      __syncthreads();
-    }
+    if (ch > 0) al = sm.alp[lane & (kCh - 1)];
     // a due slot's fold inputs are all read: count in for the key rows' append
     // (the last wave waits for the return, which comes after its state loads)
     if (due && ch == nfold - 1 && tid == 64 * (WAVES - 1)) group_rank = atomicAdd(group_ctr, 1);
-    if (wave == 0) build_tt<DK, DV>(sm, al, lane, g, l16);
-    __syncthreads();  // T x T matrices complete
+    if (wave == 0)
+      build_tt<DK, DV>(sm, al, lane, g, l16);
+    else if (ch > 0)
+      keys_to_kt<DK, DV, 64 * (WAVES - 1)>(sm, opaque_tid() - 64);
+    __syncthreads();  // T x T matrices and transposed keys complete
+    // the next chunk: the stream's next fold chunk, or the output chunk
+    const bool last = ch == nfold - 1;
     f32x4 Y[2][NT], Z[2][NT], Wm[2][NT];
     contract<DK, DV, NT, kY>(sm, H, g, l16, Y, Z);
+    __syncthreads();  // every wave has read the keys
+    if (!last)
+      pf.issue_k(sm, s1, u1, T0 + kCh * ch, kCh);
+    else
+      pf.issue_k(sm, out_srcs(), uo, t0, Treal);
     solve_w<DK, DV, NT>(sm, Y, col_of(), g, l16, Wm);
+    lds_barrier();  // every wave has read the values and beta
+    if (!last)
+      pf.issue_v(sm, s1, u1, T0 + kCh * ch, kCh);
+    else
+      pf.issue_v(sm, out_srcs(), uo, t0, Treal);
     fold_state<DK, DV, NT>(sm, Wm, g, l16, H);
-    __syncthreads();  // LDS is rewritten by the next chunk
+    // the next chunk is in LDS once its DMA is done: waited for here, so that
+    // no DMA is in flight across the loop's back edge (the compiler would then
+    // wait for all loads, the state's included, in the first chunk's build)
+    __syncthreads();
   }
 
   // ---- the output chunk
-  Unit uo = u1;
-  int t0 = nch == 1 ? 0 : T0 + kCh * (nch - 2), Treal = nch == 1 ? T0 : kCh;
-  if (due) {
-    store_state<DK, DV, NT>(st, st_off_of(), H);
-    const int hd = head + n - (head + n >= C ? C : 0);
-    uo = Unit{r, h, s, kh, hd, 0, Dq, C};
-    t0 = 0;
-    Treal = Dq;
-  }
-  const Srcs so = due ? make_srcs<DK, DV>(c, uo, &va, true) : s1;
+  const Srcs so = out_srcs();
+  if (!out0) pf.issue_q(sm, so, uo, t0, Treal);
+  if (due) store_state<DK, DV, NT>(st, st_off_of(), H);
   if (!out0) {
-    Stage<DK, DV, NT, true> sg;
-    sg.load(so, uo, t0, Treal, true);
-    sg.store(sm, Treal, true);
-    al = sg.al;
-    __syncthreads();
+    __syncthreads();  // (waits for the output chunk's DMA)
+    const int t = lane & (kCh - 1);
+    al = t < Treal ? sm.alp[t] : 1.f;
   }
   if (wave == 0)
     build_tt<DK, DV>(sm, al, lane, g, l16);

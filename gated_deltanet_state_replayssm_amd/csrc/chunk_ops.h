@@ -102,16 +102,15 @@ struct Smem {
   float lgc[kCh];                  // the same, from the scan of the wave that builds Cm
 };
 
-// The arrays of Smem as LDS variables of their own, seen through one view (the
-// long replays, whose keys, values and queries arrive by LDS DMA while other
-// arrays are read). The compiler waits for an LDS DMA before every LDS access
-// it cannot tell apart from the DMA's writes; accesses to other variables it
-// can, so the DMA targets are variables of their own.
-template <int DK>
-union SmemQK {
-  uint16_t q[kCh][DK + kPadK];
-  uint16_t kt[DK][kCh + kPadT];
-};
+// The LDS of the long replays: the arrays of Smem as LDS variables of their
+// own, seen through a view per key buffer. Keys, values, alpha and beta arrive
+// by LDS DMA while other arrays are read; the compiler waits for an LDS DMA
+// before every LDS access it cannot tell apart from the DMA's writes, and it
+// tells accesses to other variables apart, so each DMA target is a variable of
+// its own. Two key buffers (each chunk's keys land in one while the previous
+// chunk reads the other); the fold reads the transposed keys straight from the
+// token-major rows (rd_kt_tr), so there is no transposed copy, and the output
+// chunk's queries take the key buffer the chunk does not use.
 struct SmemMats {
   float T[kCh][kCh + kPadF];
   float Cm[kCh][kCh + kPadF];
@@ -120,10 +119,9 @@ struct SmemMats {
   float lgc[kCh];
 };
 template <int DK, int DV>
-struct SmemView {
+struct SmemLong {
   uint16_t (&k)[kCh][DK + kPadK];
   uint16_t (&q)[kCh][DK + kPadK];
-  uint16_t (&kt)[DK][kCh + kPadT];
   uint16_t (&v)[kCh][DV + kPadK];
   float (&T)[kCh][kCh + kPadF];
   float (&Cm)[kCh][kCh + kPadF];
@@ -141,6 +139,24 @@ __device__ __forceinline__ bf16x8 rd_row(const uint16_t (*m)[W], int row, int co
   const uint2 a = *reinterpret_cast<const uint2 *>(p);
   const uint2 b = *reinterpret_cast<const uint2 *>(p + 16);
   const uint4 v = {a.x, a.y, b.x, b.y};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// The A operand of K^T for key columns 16 mt + l16 (rows of the fold's
+// product) in the token order of tok_operand (tokens 4g + {0..3}, then
+// 16 + 4g + {0..3}), read from token-major key rows by two transposing LDS
+// reads (ds_read_b64_tr_b16). Within each 16-lane group, lane a passes the
+// address of 4 keys (row 4g + a / 4, columns 16 mt + 4 (a mod 4) ..); lane i
+// receives element i mod 4 of lanes i / 4, 4 + i / 4, 8 + i / 4 and
+// 12 + i / 4, i.e. column 16 mt + i of rows 4g .. 4g + 3.
+template <int W>
+__device__ __forceinline__ bf16x8 rd_kt_tr(const uint16_t (*m)[W], int mt, int g, int l16) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4 *lds_ptr;
+  const int r = 4 * g + (l16 >> 2), c = 16 * mt + 4 * (l16 & 3);
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)&m[r][c]);
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)&m[16 + r][c]);
+  const s16x4 v[2] = {a, b};
   return __builtin_bit_cast(bf16x8, v);
 }
 
@@ -394,7 +410,9 @@ struct Stage {
     }
   }
 
-  template <class SM>
+  // KT: write the transposed keys of a folded chunk (kernels whose fold reads
+  // them from the rows do not keep them)
+  template <bool KT = true, class SM>
   __device__ __forceinline__ void store(SM &sm, int Treal, bool out_chunk) {
     const int tid = opaque_tid();
 #pragma unroll
@@ -404,7 +422,7 @@ struct Stage {
       *reinterpret_cast<u32x4 *>(&sm.k[t][part * 8]) = k;
       if (out_chunk) {
         *reinterpret_cast<u32x4 *>(&sm.q[t][part * 8]) = qv[it];
-      } else {
+      } else if constexpr (KT) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           sm.kt[part * 8 + 2 * e][t] = (uint16_t)(k[e] & 0xffffu);
@@ -518,13 +536,12 @@ __device__ __forceinline__ void dma4(Rsrc r, char *lds, uint32_t voff) {
 
 // The staging of one chunk (rows [t0, t0 + Treal) of a token stream) issued
 // while the previous chunk is computed, all of it by LDS DMA (no registers stay
-// in flight across the chunk loop): keys once the previous chunk's contraction
-// has read its keys; values, beta and alpha once W has read the previous
-// values and beta; queries (output chunk) once the fold has read the
-// transposed keys that share their array. Rows past Treal, and committed rows'
-// queries, come in as zeros (a reader takes alpha = 1 past Treal). The caller's
-// barriers while the DMA is in flight are lds_barrier(); the next
-// __syncthreads() waits for it.
+// in flight across the chunk loop): keys, beta and alpha into the buffers the
+// current chunk does not use, values once W has read the previous values,
+// queries (output chunk) once the last fold has read the keys in their buffer.
+// Rows past Treal, and committed rows' queries, come in as zeros (a reader
+// takes alpha = 1 past Treal). The caller's barriers while the DMA is in flight
+// are lds_barrier(); the next __syncthreads() waits for it.
 template <int DK, int DV, int NW>
 struct Prefetch {
   template <class SM>
@@ -553,9 +570,15 @@ struct Prefetch {
       else
         dma16<kStream>(sr.dv, dst, data ? at.draft + pc * 16 : kOOB);
     });
-    // beta then alpha (sm.bet and sm.alp adjacent): lane l < 32 beta of row l,
-    // lane 32 + l alpha of row l; by the last wave
-    if (wv == NW - 1) {
+  }
+
+  // beta then alpha of the chunk's rows (sm.bet and sm.alp adjacent): lane
+  // l < 32 beta of row l, lane 32 + l alpha of row l; by the last wave
+  template <class SM>
+  __device__ __forceinline__ void issue_ab(SM &sm, const Srcs &sr, const Unit &u, int t0,
+                                           int Treal) const {
+    const int tid = opaque_tid(), lane = tid & 63;
+    if (__builtin_amdgcn_readfirstlane(tid >> 6) == NW - 1) {
       const int t = lane & (kCh - 1);
       const RowAt<true> at(u, t0, t, Treal, 4, sr.dab_row);
       char *dst = reinterpret_cast<char *>(&sm.bet[0]);
@@ -573,8 +596,7 @@ struct Prefetch {
     }
   }
 
-  // the output chunk's queries (draft rows only), into the array that held the
-  // transposed keys of the folded chunks
+  // the output chunk's queries (draft rows only)
   template <class SM>
   __device__ __forceinline__ void issue_q(SM &sm, const Srcs &sr, const Unit &u, int t0,
                                           int Treal) const {
@@ -587,24 +609,24 @@ struct Prefetch {
   }
 };
 
-// The keys of a chunk transposed for the fold (sm.kt[d][t] = sm.k[t][d]), by
-// the NTHR threads j = 0 .. NTHR - 1 of the caller's numbering. A task is one
-// key column and 8 tokens: eight 2-byte reads, one 16-byte write.
-template <int DK, int DV, int NTHR, class SM>
-__device__ __forceinline__ void keys_to_kt(SM &sm, int j) {
-  constexpr int TASKS = DK * (kCh / 8);
+// A chunk's keys, beta and alpha from the buffers the DMA fills to those the
+// chunk is computed from, by the NTHR threads j = 0 .. NTHR - 1 of the caller's
+// numbering (16 bytes a copy).
+template <int DK, int NTHR>
+__device__ __forceinline__ void copy_chunk_keys(const uint16_t (&kn)[kCh][DK + kPadK],
+                                                uint16_t (&kc)[kCh][DK + kPadK],
+                                                const float (&abn)[2][kCh], float (&abc)[2][kCh],
+                                                int j) {
+  constexpr int PK = (DK + kPadK) / 8, NK = kCh * PK, NA = 2 * kCh / 4;
+  const u32x4 *src = reinterpret_cast<const u32x4 *>(&kn[0][0]);
+  u32x4 *dst = reinterpret_cast<u32x4 *>(&kc[0][0]);
 #pragma unroll
-  for (int it = 0; it < (TASKS + NTHR - 1) / NTHR; ++it) {
+  for (int it = 0; it < (NK + NTHR - 1) / NTHR; ++it) {
     const int p = j + it * NTHR;
-    if (TASKS % NTHR == 0 || p < TASKS) {
-      const int d = p % DK, t0 = 8 * (p / DK);
-      uint32_t w[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        w[e] = (uint32_t)sm.k[t0 + 2 * e][d] | ((uint32_t)sm.k[t0 + 2 * e + 1][d] << 16);
-      *reinterpret_cast<u32x4 *>(&sm.kt[d][t0]) = u32x4{w[0], w[1], w[2], w[3]};
-    }
+    if (NK % NTHR == 0 || p < NK) dst[p] = src[p];
   }
+  if (j < NA)
+    reinterpret_cast<u32x4 *>(&abc[0][0])[j] = reinterpret_cast<const u32x4 *>(&abn[0][0])[j];
 }
 
 // Inclusive scan over lanes 0..31 of a wave with DPP row shifts (within rows of
@@ -1026,7 +1048,8 @@ __device__ __forceinline__ void emit_outputs(const SM &sm, const f32x4 (&Z)[2][N
 }
 
 // Fold the chunk into the state: H <- gamma_T H + K^T (L[T-1] o W).
-template <int DK, int DV, int NT, class SM>
+// TR: the transposed keys come from the key rows by transposing reads (no kt).
+template <int DK, int DV, int NT, bool TR = false, class SM>
 __device__ __forceinline__ void fold_state(const SM &sm, const f32x4 (&Wm)[2][NT], int g,
                                            int l16, typename Cols<NT>::F (&H)[DK / 16][4]) {
   constexpr int MT = DK / 16;
@@ -1050,7 +1073,11 @@ __device__ __forceinline__ void fold_state(const SM &sm, const f32x4 (&Wm)[2][NT
   }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    const bf16x8 kt = rd_row(sm.kt, 16 * mt + l16, 4 * g);
+    bf16x8 kt;
+    if constexpr (TR)
+      kt = rd_kt_tr(sm.k, mt, g, l16);
+    else
+      kt = rd_row(sm.kt, 16 * mt + l16, 4 * g);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       f32x4 acc = {H[mt][0][nt] * gT, H[mt][1][nt] * gT, H[mt][2][nt] * gT, H[mt][3][nt] * gT};

@@ -684,13 +684,21 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused_long(Ve
   static_assert(DK % 32 == 0 && DV % (16 * NT) == 0 && (NT == 2 || NT == 4), "tile shape");
   static_assert(WAVES >= 2, "the T x T matrices are built by waves 0 and 1");
   typedef typename Cols<NT>::F F;
-  __shared__ __align__(16) uint16_t lds_k[kCh][DK + kPadK];
+  __shared__ __align__(16) uint16_t lds_kn[kCh][DK + kPadK];
+  __shared__ __align__(16) uint16_t lds_kc[kCh][DK + kPadK];
   __shared__ __align__(16) uint16_t lds_v[kCh][DV + kPadK];
-  __shared__ __align__(16) SmemQK<DK> lds_qk;
   __shared__ __align__(16) SmemMats lds_m;
-  __shared__ __align__(16) float lds_ab[2][kCh];  // beta, alpha (filled by one DMA)
-  const SmemView<DK, DV> sm{lds_k,     lds_qk.q,  lds_qk.kt, lds_v,     lds_m.T,  lds_m.Cm,
-                            lds_m.gam, lds_ab[0], lds_ab[1], lds_m.lg, lds_m.lgc};
+  __shared__ __align__(16) float lds_abn[2][kCh];  // beta, alpha (filled by one DMA)
+  __shared__ __align__(16) float lds_abc[2][kCh];
+  // A chunk arrives in the "n" buffers (keys, beta, alpha) and is copied to
+  // the "c" buffers while wave 0 builds its T x T matrices from the n ones;
+  // then the next chunk's DMA refills the n buffers while the contraction, W
+  // and the fold read the c ones. The output chunk stays in the n buffers, its
+  // queries in keys buffer c.
+  const SmemLong<DK, DV> smn{lds_kn,    lds_kc,     lds_v,      lds_m.T,  lds_m.Cm,
+                             lds_m.gam, lds_abn[0], lds_abn[1], lds_m.lg, lds_m.lgc};
+  const SmemLong<DK, DV> smc{lds_kc,    lds_kn,     lds_v,      lds_m.T,  lds_m.Cm,
+                             lds_m.gam, lds_abc[0], lds_abc[1], lds_m.lg, lds_m.lgc};
   __shared__ int group_rank;
   __shared__ Move moves[64];
 
@@ -800,7 +808,7 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused_long(Ve
     if (wave < SW) {
       Stage<DK, DV, NT, true, 64 * SW> sg0;
       sg0.load(s1, u1, 0, T0, out0);
-      sg0.store(sm, T0, out0);
+      sg0.template store<false>(smn, T0, out0);
       al = sg0.al;
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -809,50 +817,55 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused_long(Ve
     __syncthreads();
   }
   arr.take_rank(HV, rank_ctr, tid);
-  // Every chunk after the first is staged while its predecessor is computed:
-  // its keys (with alpha and beta) once the contraction has read the previous
-  // keys, its values once W has read the previous values, by LDS DMA, so that
-  // the chunk is in LDS when the fold ends; the fold chunks' transposed keys are
-  // then made from the keys in LDS while wave 0 builds the T x T matrices.
+  // Every chunk after the first is staged by LDS DMA while its predecessor is
+  // computed: its keys, beta and alpha once the predecessor's T x T matrices
+  // are built (and its keys copied), its values once W has read the previous
+  // values. While DMA is in flight the barriers are lds_barrier(): a
+  // __syncthreads() waits for it. The one at a chunk's end does wait, so that
+  // no DMA is in flight across the loop's back edge (the compiler would then
+  // wait for all loads, the state's included, in the first chunk's build).
   Prefetch<DK, DV, WAVES> pf;
-  // The thread index comes through an opaque copy so that the per-thread row
-  // offsets are recomputed in every iteration rather than held in registers.
 #pragma nounroll
   for (int ch = 0; ch < nfold; ++ch) {
+    // the thread index through an opaque copy: the per-thread offsets are
+    // recomputed in every chunk rather than held in registers
     const int lane = opaque_tid() % 64, g = lane >> 4, l16 = lane & 15;
-    if (ch > 0) al = sm.alp[lane & (kCh - 1)];
+    const bool last = ch == nfold - 1;
     // a due slot's fold inputs are all read: count in for the key rows' append
     // (the last wave waits for the return, which comes after its state loads)
-    if (due && ch == nfold - 1 && tid == 64 * (WAVES - 1)) group_rank = atomicAdd(group_ctr, 1);
-    if (wave == 0)
-      build_tt<DK, DV>(sm, al, lane, g, l16);
-    else if (ch > 0)
-      keys_to_kt<DK, DV, 64 * (WAVES - 1)>(sm, opaque_tid() - 64);
-    __syncthreads();  // T x T matrices and transposed keys complete
+    if (due && last && tid == 64 * (WAVES - 1)) group_rank = atomicAdd(group_ctr, 1);
+    if (wave == 0) {
+      if (ch > 0) al = smn.alp[lane & (kCh - 1)];
+      build_tt<DK, DV>(smn, al, lane, g, l16);
+    } else {
+      copy_chunk_keys<DK, 64 * (WAVES - 1)>(lds_kn, lds_kc, lds_abn, lds_abc, opaque_tid() - 64);
+    }
+    lds_barrier();  // T x T matrices built, keys, beta and alpha copied
     // the next chunk: the stream's next fold chunk, or the output chunk
-    const bool last = ch == nfold - 1;
+    if (!last) {
+      pf.issue_k(smn, s1, u1, T0 + kCh * ch, kCh);
+      pf.issue_ab(smn, s1, u1, T0 + kCh * ch, kCh);
+    } else {
+      const Srcs so = out_srcs();
+      pf.issue_k(smn, so, uo, t0, Treal);
+      pf.issue_ab(smn, so, uo, t0, Treal);
+    }
     f32x4 Y[2][NT], Z[2][NT], Wm[2][NT];
-    contract<DK, DV, NT, kY>(sm, H, g, l16, Y, Z);
-    __syncthreads();  // every wave has read the keys
+    contract<DK, DV, NT, kY>(smc, H, g, l16, Y, Z);
+    solve_w<DK, DV, NT>(smc, Y, col_of(), g, l16, Wm);
+    lds_barrier();  // every wave has read the values
     if (!last)
-      pf.issue_k(sm, s1, u1, T0 + kCh * ch, kCh);
+      pf.issue_v(smn, s1, u1, T0 + kCh * ch, kCh);
     else
-      pf.issue_k(sm, out_srcs(), uo, t0, Treal);
-    solve_w<DK, DV, NT>(sm, Y, col_of(), g, l16, Wm);
-    lds_barrier();  // every wave has read the values and beta
-    if (!last)
-      pf.issue_v(sm, s1, u1, T0 + kCh * ch, kCh);
-    else
-      pf.issue_v(sm, out_srcs(), uo, t0, Treal);
-    fold_state<DK, DV, NT>(sm, Wm, g, l16, H);
-    // the next chunk is in LDS once its DMA is done: waited for here, so that
-    // no DMA is in flight across the loop's back edge (the compiler would then
-    // wait for all loads, the state's included, in the first chunk's build)
-    __syncthreads();
+      pf.issue_v(smn, out_srcs(), uo, t0, Treal);
+    fold_state<DK, DV, NT, true>(smc, Wm, g, l16, H);
+    __syncthreads();  // (waits for the next chunk's DMA)
   }
 
-  // ---- the output chunk
+  // ---- the output chunk (in the n buffers)
+  const SmemLong<DK, DV> &sm = smn;
   const Srcs so = out_srcs();
+  // its queries into keys buffer c, which the last fold has finished reading
   if (!out0) pf.issue_q(sm, so, uo, t0, Treal);
   if (due) store_state<DK, DV, NT>(st, st_off_of(), H);
   if (!out0) {

@@ -683,6 +683,11 @@ __device__ __forceinline__ void gram3(const uint16_t (*p)[W], const uint16_t (*q
   }
 }
 
+// 2^x by the hardware instruction (v_exp_f32). The decays' exponents are
+// differences of clamped log2 prefix sums, x <= 0 up to rounding; results below
+// 2^-126 (flushed or denormal) are negligible next to the terms they multiply.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // L[t][j] for the three tiles of gram3, zero above the diagonal
 __device__ __forceinline__ void decay_tiles(const float *lg, int g, int l16, float (&Lv)[3][4]) {
   float lgv[2][4], lgc[2];
@@ -698,7 +703,7 @@ __device__ __forceinline__ void decay_tiles(const float *lg, int g, int l16, flo
     for (int i = 0; i < 4; ++i) {
       const int ta = b == 0 ? 0 : 1, tb = b == 2 ? 1 : 0;
       const int t = 16 * ta + 4 * g + i, j = 16 * tb + l16;
-      Lv[b][i] = (j <= t) ? exp2f(lgv[ta][i] - lgc[tb]) : 0.f;
+      Lv[b][i] = (j <= t) ? exp2_hw(lgv[ta][i] - lgc[tb]) : 0.f;
     }
 }
 
@@ -769,94 +774,40 @@ __device__ __forceinline__ void build_tt(SM &sm, float al_staged, int lane, int 
       }
   }
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  // ---- (I + A)^-1 in place, by recursive 2 x 2 blocking: T = [[T00, 0], [T10, T11]]
-  // with T10 = -T11 (A10 T00). 4 x 4 diagonal blocks by forward substitution, then
-  // 8 x 8 and 16 x 16 blocks on VALU, then the 32 x 32 level on MFMA. Each level
-  // overwrites the A10 block it has read with T10; the A10 T00 products of the
-  // VALU levels go to the (zero) upper-right block, which is cleared after use.
-  // Every step reads everything it needs before it writes (one wave, LDS
-  // accesses in program order).
-  {
-    // 4 x 4 diagonal blocks q = 0..7: lane = (q, column cc)
-    const int q = (lane >> 2) & 7, cc = lane & 3, r0 = 4 * q;
-    const float a10 = sm.T[r0 + 1][r0], a20 = sm.T[r0 + 2][r0], a21 = sm.T[r0 + 2][r0 + 1];
-    const float a30 = sm.T[r0 + 3][r0], a31 = sm.T[r0 + 3][r0 + 1], a32 = sm.T[r0 + 3][r0 + 2];
-    const float x0 = cc == 0 ? 1.f : 0.f;
-    const float x1 = cc == 1 ? 1.f : (cc < 1 ? -a10 * x0 : 0.f);
-    const float x2 = cc == 2 ? 1.f : (cc < 2 ? -(a20 * x0 + a21 * x1) : 0.f);
-    const float x3 = cc == 3 ? 1.f : -(a30 * x0 + a31 * x1 + a32 * x2);
-    if (lane < 32) {
-      sm.T[r0][r0 + cc] = x0;
-      sm.T[r0 + 1][r0 + cc] = x1;
-      sm.T[r0 + 2][r0 + cc] = x2;
-      sm.T[r0 + 3][r0 + cc] = x3;
+  // ---- (I + A)^-1 in place, as T = [[T00, 0], [T10, T11]] with T00, T11 the
+  // inverses of the 16 x 16 diagonal blocks and T10 = -T11 (A10 T00).
+  // The diagonal blocks by forward substitution, one lane per column (lane
+  // 16 b + c: column c of block b): x_r = [r == c] - sum_{m < r} A[r][m] x_m,
+  // with x_m = 0 above the diagonal, so every lane runs the same unrolled
+  // recurrence. The rows of A are read (broadcast) before the block is
+  // overwritten (one wave, LDS accesses in program order).
+  if (lane < 2 * 16) {
+    const int b = lane >> 4, c = lane & 15, r0 = 16 * b;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float row[16];
+#pragma unroll
+      for (int q = 0; q < (r + 3) / 4; ++q) {
+        const float4 v = *reinterpret_cast<const float4 *>(&sm.T[r0 + r][r0 + 4 * q]);
+        row[4 * q] = v.x;
+        row[4 * q + 1] = v.y;
+        row[4 * q + 2] = v.z;
+        row[4 * q + 3] = v.w;
+      }
+      // two partial sums halve the dependent chain
+      float s0 = r == c ? 1.f : 0.f, s1 = 0.f;
+#pragma unroll
+      for (int m = 0; m < r; ++m) {
+        if (m & 1)
+          s1 = fmaf(-row[m], x[m], s1);
+        else
+          s0 = fmaf(-row[m], x[m], s0);
+      }
+      x[r] = s0 + s1;
     }
-  }
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  {
-    // 8 x 8 blocks p = 0..3: lane = (p, i, j) over the 4 x 4 lower-left block
-    const int p = lane >> 4, i = (lane >> 2) & 3, j = lane & 3, r0 = 8 * p;
-    float av[4], tv[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      av[k] = sm.T[r0 + 4 + i][r0 + k];
-      tv[k] = sm.T[r0 + k][r0 + j];
-    }
-    float m = 0.f;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) m = fmaf(av[k], tv[k], m);
-    sm.T[r0 + i][r0 + 4 + j] = m;
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    float t11[4], mv[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      t11[k] = sm.T[r0 + 4 + i][r0 + 4 + k];
-      mv[k] = sm.T[r0 + k][r0 + 4 + j];
-    }
-    float t = 0.f;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) t = fmaf(t11[k], mv[k], t);
-    sm.T[r0 + 4 + i][r0 + j] = -t;
-    sm.T[r0 + i][r0 + 4 + j] = 0.f;
-  }
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  {
-    // 16 x 16 blocks b = 0, 1: lane = (b, i, j0) over the 8 x 8 lower-left block,
-    // two columns j0 and j0 + 4 per lane
-    const int b = lane >> 5, i = (lane >> 2) & 7, j0 = lane & 3, r0 = 16 * b;
-    float av[8], tv[2][8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      av[k] = sm.T[r0 + 8 + i][r0 + k];
-      tv[0][k] = sm.T[r0 + k][r0 + j0];
-      tv[1][k] = sm.T[r0 + k][r0 + j0 + 4];
-    }
-    float m0 = 0.f, m1 = 0.f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      m0 = fmaf(av[k], tv[0][k], m0);
-      m1 = fmaf(av[k], tv[1][k], m1);
-    }
-    sm.T[r0 + i][r0 + 8 + j0] = m0;
-    sm.T[r0 + i][r0 + 12 + j0] = m1;
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    float t11[8], mv[2][8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      t11[k] = sm.T[r0 + 8 + i][r0 + 8 + k];
-      mv[0][k] = sm.T[r0 + k][r0 + 8 + j0];
-      mv[1][k] = sm.T[r0 + k][r0 + 12 + j0];
-    }
-    float t0 = 0.f, t1 = 0.f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      t0 = fmaf(t11[k], mv[0][k], t0);
-      t1 = fmaf(t11[k], mv[1][k], t1);
-    }
-    sm.T[r0 + 8 + i][r0 + j0] = -t0;
-    sm.T[r0 + 8 + i][r0 + j0 + 4] = -t1;
-    sm.T[r0 + i][r0 + 8 + j0] = 0.f;
-    sm.T[r0 + i][r0 + 12 + j0] = 0.f;
+    for (int r = 0; r < 16; ++r) sm.T[r0 + r][r0 + c] = x[r];
   }
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   {
@@ -1060,7 +1011,7 @@ __device__ __forceinline__ void fold_state(const SM &sm, const f32x4 (&Wm)[2][NT
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) lt[a][i] = exp2f(lg31 - sm.lg[16 * a + 4 * g + i]);
+      for (int i = 0; i < 4; ++i) lt[a][i] = exp2_hw(lg31 - sm.lg[16 * a + 4 * g + i]);
     f32x4 Wp[2][NT];
 #pragma unroll
     for (int a = 0; a < 2; ++a)

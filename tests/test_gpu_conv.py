@@ -94,12 +94,15 @@ def _run(wl, CH, K, steps, seed, with_bias=True, fused=False):
     return amb
 
 
-@pytest.mark.parametrize("K,CH,fused", [(4, 256, False), (4, 1024, True), (2, 66, False),
-                                        (1, 8, True), (8, 130, False)])
-def test_conv_schedule(K, CH, fused):
-    wl = synth.Workload("cv", 5, 7, 4, 2, 32, 32, 16, 4, synth.BF16, 6, 1, "uniform",
+# channels a multiple of 8 take the 16-byte kernel (groups of 4 draft tokens;
+# drafts of 5 and 7 leave a ragged group), the others the 4-byte one
+@pytest.mark.parametrize("K,CH,fused,D", [(4, 256, False, 4), (4, 1024, True, 4), (2, 66, False, 4),
+                                          (1, 8, True, 4), (8, 130, False, 4), (8, 136, False, 5),
+                                          (3, 24, True, 7)])
+def test_conv_schedule(K, CH, fused, D):
+    wl = synth.Workload("cv", 5, 7, 4, 2, 32, 32, 16, D, synth.BF16, 6, 1, "uniform",
                         "uniform:0:5")
-    say(f"case conv K={K} CH={CH} fused={fused}")
+    say(f"case conv K={K} CH={CH} fused={fused} D={D}")
     amb = _run(wl, CH, K, 12, 700 + K * 10 + CH, with_bias=(K % 2 == 0), fused=fused)
     say(f"  {amb} outputs at a bf16 rounding midpoint")
 

@@ -642,12 +642,14 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyA
   __syncthreads();  // T x T matrices complete
 
   f32x4 Y[2][NT], Z[2][NT], Wm[2][NT];
-  contract<DK, DV, NT, kY | kZ>(sm, H, g, l16, Y, Z);
-  arr.grid_in(HV, rank_ctr, grid_ctr, tid);
   if constexpr (NORM) {
-    // the gate and weight load while W is solved; out may be absent
+    // the gate and weight load while the state is contracted and W solved
+    // (issued after the contraction, their round trip fell into the launch's
+    // tail; issued before the T x T build, they spill); out may be absent
     const NormRsrc nr = norm_rsrc(va, r, h, DV, max(D, 1));
     const Gate gt = load_gate<DV, NT>(va, nr, col_of(), g, u.B, u.T);
+    contract<DK, DV, NT, kY | kZ>(sm, H, g, l16, Y, Z);
+    arr.grid_in(HV, rank_ctr, grid_ctr, tid);
     solve_w<DK, DV, NT>(sm, Y, col_of(), g, l16, Wm);
     __shared__ __align__(16) float nred[2][kCh][4];
     emit_outputs_norm<DK, DV, NT>(
@@ -655,6 +657,8 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyA
         va.out ? out_rsrc(va, r, h, DV, max(D, 1)) : make_rsrc(nullptr, 0), col_of(), va, nr, gt,
         nred);
   } else {
+    contract<DK, DV, NT, kY | kZ>(sm, H, g, l16, Y, Z);
+    arr.grid_in(HV, rank_ctr, grid_ctr, tid);
     solve_w<DK, DV, NT>(sm, Y, col_of(), g, l16, Wm);
     emit_outputs<DK, DV, NT>(sm, Z, Wm, g, l16, 0, u.T, u.B, out_rsrc(va, r, h, DV, max(D, 1)),
                              col_of() * 4, HV * DV * 4);

@@ -44,6 +44,14 @@ namespace {
 
 
 constexpr int kCh = kChunkTokens;  // tokens per chunk
+// Split output chunk: when a single-chunk replay has at most 16 committed
+// tokens and at most 16 draft tokens, the committed rows sit at rows 0 .. B - 1,
+// the draft at rows 16 .. 16 + D - 1, and the rows between are empty (k = q =
+// v = 0, beta = 0, alpha = 1): such a row adds nothing to A, W, the decays or
+// the products, so every output is unchanged, and the draft's outputs lie in
+// the second 16-row tile: the output products and the fused norm's per-row
+// reductions skip the first.
+constexpr int kGapRow = kCh / 2;
 constexpr int kPadK = 8;   // bf16 padding per token row of K / Q in LDS
 constexpr int kPadT = 8;   // bf16 padding per row of K^T
 constexpr int kPadF = 4;   // fp32 padding per row of the 32 x 32 matrices
@@ -344,9 +352,14 @@ template <bool VERIFY>
 struct RowAt {
   uint32_t ring, draft, append;  // ring read, draft read, ring append (draft rows)
   __device__ __forceinline__ RowAt(const Unit &u, int t0, int t, int Treal, uint32_t ring_row,
-                                   uint32_t draft_row) {
-    const int tok = t0 + t;
-    const bool real = t < Treal;
+                                   uint32_t draft_row, bool gap = false) {
+    int tok = t0 + t;
+    bool real = t < Treal;
+    if (gap) {  // split output chunk (t0 = 0): see kGapRow
+      const bool dr = t >= kGapRow;
+      tok = dr ? t - kGapRow + u.B : t;
+      real = dr ? tok < u.T : t < u.B;
+    }
     const bool in_ring = !VERIFY || tok < u.B;
     int pos = u.head + tok;
     pos -= pos >= u.C ? u.C : 0;  // head < C and tok < C for real rows
@@ -374,12 +387,12 @@ struct Stage {
   float al, be;
 
   __device__ __forceinline__ void load(const Srcs &sr, const Unit &u, int t0, int Treal,
-                                       bool out_chunk) {
+                                       bool out_chunk, bool gap = false) {
     const int tid = opaque_tid();
 #pragma unroll
     for (int it = 0; it < IK; ++it) {
       const int p = tid + it * THREADS, t = p / PK, part = p % PK;
-      const RowAt<VERIFY> at(u, t0, t, Treal, DK * 2, sr.dk_row);
+      const RowAt<VERIFY> at(u, t0, t, Treal, DK * 2, sr.dk_row, gap);
       if constexpr (VERIFY) {
         kv[it] = bload_rd<u32x4>(at.ring != kOOB, sr.rk, at.ring + part * 16, sr.dk,
                                  at.draft + part * 16);
@@ -392,7 +405,7 @@ struct Stage {
 #pragma unroll
     for (int it = 0; it < IV; ++it) {
       const int p = tid + it * THREADS, t = p / PV, part = p % PV;
-      const RowAt<VERIFY> at(u, t0, t, Treal, DV * 2, sr.dv_row);
+      const RowAt<VERIFY> at(u, t0, t, Treal, DV * 2, sr.dv_row, gap);
       if constexpr (VERIFY)
         vv[it] = bload_rd<u32x4>(at.ring != kOOB, sr.rv, at.ring + part * 16, sr.dv,
                                  at.draft + part * 16);
@@ -400,7 +413,7 @@ struct Stage {
         vv[it] = bload<u32x4>(sr.rv, at.ring + part * 16);
     }
     const int t = tid & (kCh - 1);
-    const RowAt<VERIFY> at(u, t0, t, Treal, 4, sr.dab_row);
+    const RowAt<VERIFY> at(u, t0, t, Treal, 4, sr.dab_row, gap);
     if constexpr (VERIFY) {
       al = bload_rd<float>(at.ring != kOOB, sr.ra, at.ring, sr.da, at.draft);
       be = bload_rd<float>(at.ring != kOOB, sr.rb, at.ring, sr.db, at.draft);
@@ -412,8 +425,10 @@ struct Stage {
 
   // KT: write the transposed keys of a folded chunk (kernels whose fold reads
   // them from the rows do not keep them)
+  // (gapB >= 0: a split output chunk with gapB committed and gapD draft rows)
   template <bool KT = true, class SM>
-  __device__ __forceinline__ void store(SM &sm, int Treal, bool out_chunk) {
+  __device__ __forceinline__ void store(SM &sm, int Treal, bool out_chunk, int gapB = -1,
+                                        int gapD = 0) {
     const int tid = opaque_tid();
 #pragma unroll
     for (int it = 0; it < IK; ++it) {
@@ -435,7 +450,11 @@ struct Stage {
       const int p = tid + it * THREADS, t = p / PV, part = p % PV;
       *reinterpret_cast<u32x4 *>(&sm.v[t][part * 8]) = vv[it];
     }
-    if ((tid & (kCh - 1)) >= Treal) al = 1.f;  // padding rows: alpha = 1, beta = 0 (read as 0)
+    {  // padding rows (and a split chunk's empty rows): alpha = 1, beta = 0 (read as 0)
+      const int t = tid & (kCh - 1);
+      const bool pad = gapB < 0 ? t >= Treal : (t < kGapRow ? t >= gapB : t - kGapRow >= gapD);
+      if (pad) al = 1.f;
+    }
     if (tid < kCh) {
       sm.alp[tid] = al;
       sm.bet[tid] = be;
@@ -446,7 +465,8 @@ struct Stage {
   // from LDS (one workgroup per key head writes k and q).
   template <class SM>
   __device__ __forceinline__ void append(const SM &sm, const Srcs &sr, const Unit &u,
-                                         int t0, int Treal, bool kq_writer) const {
+                                         int t0, int Treal, bool kq_writer,
+                                         bool gap = false) const {
     const int tid = opaque_tid();
     // Recompute the row offsets here rather than keep those of the loads alive
     // in registers through the whole kernel: the copy of the unit is opaque to
@@ -457,7 +477,7 @@ struct Stage {
 #pragma unroll
       for (int it = 0; it < IK; ++it) {
         const int p = tid + it * THREADS, t = p / PK, part = p % PK;
-        const RowAt<VERIFY> at(u2, t0, t, Treal, DK * 2, sr.dk_row);
+        const RowAt<VERIFY> at(u2, t0, t, Treal, DK * 2, sr.dk_row, gap);
         bstore(*reinterpret_cast<const u32x4 *>(&sm.k[t][part * 8]), sr.rk, at.append + part * 16);
         bstore(*reinterpret_cast<const u32x4 *>(&sm.q[t][part * 8]), sr.rq, at.append + part * 16);
       }
@@ -465,11 +485,11 @@ struct Stage {
 #pragma unroll
     for (int it = 0; it < IV; ++it) {
       const int p = tid + it * THREADS, t = p / PV, part = p % PV;
-      const RowAt<VERIFY> at(u2, t0, t, Treal, DV * 2, sr.dv_row);
+      const RowAt<VERIFY> at(u2, t0, t, Treal, DV * 2, sr.dv_row, gap);
       bstore(*reinterpret_cast<const u32x4 *>(&sm.v[t][part * 8]), sr.rv, at.append + part * 16);
     }
     if (tid < kCh) {
-      const RowAt<VERIFY> at(u2, t0, tid, Treal, 4, sr.dab_row);
+      const RowAt<VERIFY> at(u2, t0, tid, Treal, 4, sr.dab_row, gap);
       bstore(sm.alp[tid], sr.ra, at.append);
       bstore(sm.bet[tid], sr.rb, at.append);
     }
@@ -853,6 +873,8 @@ enum { kY = 1, kZ = 2 };
 // Y = K H and/or Z = Q H over d_k on MFMA, the state split into hi + lo bf16.
 // Both products share one split per k-step; a Z-only pass splits with
 // truncation so that it is never merged with (and kept alive from) a Y pass.
+// (A split output chunk needs only Z's second tile; skipping the first, at run
+// time or in a second pass, measured no faster and the second pass spilled.)
 template <int DK, int DV, int NT, int WHAT, class SM>
 __device__ __forceinline__ void contract(const SM &sm,
                                          const typename Cols<NT>::F (&H)[DK / 16][4], int g,
@@ -958,7 +980,7 @@ template <int DK, int DV, int NT, class SM>
 __device__ __forceinline__ void emit_outputs(const SM &sm, const f32x4 (&Z)[2][NT],
                                              const f32x4 (&Wm)[2][NT], int g, int l16, int t0,
                                              int Treal, int B, Rsrc out, uint32_t col_off,
-                                             uint32_t row_bytes) {
+                                             uint32_t row_bytes, int a0 = 0) {
   typedef typename Cols<NT>::F F;
   asm volatile("" : "+v"(B));  // recompute the row offsets here (see Stage::append)
   bf16x8 wh[NT], wl[NT];
@@ -967,12 +989,14 @@ __device__ __forceinline__ void emit_outputs(const SM &sm, const f32x4 (&Z)[2][N
   float crow[2][8], ga[2][4];
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
+    if (a < a0) continue;  // a split chunk: no draft rows in tile 0
     rd_frow(sm.Cm, 16 * a + l16, g, crow[a]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) ga[a][i] = sm.gam[16 * a + 4 * g + i];
   }
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
+    if (a < a0) continue;  // a split chunk: no draft rows in tile 0
     bf16x8 chh, chl;
     split8(crow[a], chh, chl);
     f32x4 O[NT];

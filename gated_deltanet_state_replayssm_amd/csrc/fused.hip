@@ -81,7 +81,8 @@ __device__ __forceinline__ void emit_outputs_norm(const SM &sm,
                                                   const f32x4 (&Wm)[2][NT], int g, int l16,
                                                   int wave, int Treal, int B, Rsrc out, int col,
                                                   const VerifyArgs &va, const NormRsrc &nr,
-                                                  const Gate &gt, float (*red)[kCh][4]) {
+                                                  const Gate &gt, float (*red)[kCh][4],
+                                                  int a0 = 0) {
   typedef typename Cols<NT>::F F;
   constexpr int WAVES = DV / (16 * NT);
   constexpr float kE4M3Max = 448.f;
@@ -92,6 +93,11 @@ __device__ __forceinline__ void emit_outputs_norm(const SM &sm,
   f32x4 O[2][NT];
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
+    if (a < a0) {  // a split chunk: no draft rows in tile 0
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) O[a][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      continue;
+    }
     float crow[8], ga[4];
     rd_frow(sm.Cm, 16 * a + l16, g, crow);
 #pragma unroll
@@ -611,20 +617,28 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyA
   // waves 0..SW-1 stage while the others' state loads stream in.
   const Unit u{r, h, s, kh, hd, B, B + D, C};
   const Srcs sr = make_srcs<DK, DV>(c, u, &va, true);
+  // With the norm, a split output chunk (kGapRow: committed rows from 0, draft
+  // rows from 16) when both fit; its draft rows are the chunk's rows [ob, oT).
+  // The norm's per-row reductions then cover one 16-row tile instead of two
+  // (1 us less per launch at 32 requests); without the norm the split measured
+  // 0.2 us slower, and the plain step keeps the layout of the separate verify.
+  const bool split = NORM && B <= kGapRow && D <= kGapRow;
+  const int ob = split ? kGapRow : B, oT = split ? kGapRow + D : B + D;
+  const int gB = split ? B : -1;
   Stage<DK, DV, NT, true> sga;
   Stage<DK, DV, NT, true, 64 * SW> sgs;
   float al;  // this lane's staged alpha (token lane % 32)
   if (due) {
-    sga.load(sr, u, 0, u.T, true);
-    sga.store(sm, u.T, true);
+    sga.load(sr, u, 0, u.T, true, split);
+    sga.store(sm, u.T, true, gB, D);
     al = sga.al;
   } else {
     if (wave >= SW) {
       load_state<DK, DV, NT>(st, st_off_of(), H);
       al = 1.f;
     } else {
-      sgs.load(sr, u, 0, u.T, true);
-      sgs.store(sm, u.T, true);
+      sgs.load(sr, u, 0, u.T, true, split);
+      sgs.store(sm, u.T, true, gB, D);
       al = sgs.al;
       __builtin_amdgcn_sched_barrier(0);
       load_state<DK, DV, NT>(st, st_off_of(), H);
@@ -647,27 +661,27 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyA
     // (issued after the contraction, their round trip fell into the launch's
     // tail; issued before the T x T build, they spill); out may be absent
     const NormRsrc nr = norm_rsrc(va, r, h, DV, max(D, 1));
-    const Gate gt = load_gate<DV, NT>(va, nr, col_of(), g, u.B, u.T);
+    const Gate gt = load_gate<DV, NT>(va, nr, col_of(), g, ob, oT);
     contract<DK, DV, NT, kY | kZ>(sm, H, g, l16, Y, Z);
     arr.grid_in(HV, rank_ctr, grid_ctr, tid);
     solve_w<DK, DV, NT>(sm, Y, col_of(), g, l16, Wm);
     __shared__ __align__(16) float nred[2][kCh][4];
     emit_outputs_norm<DK, DV, NT>(
-        sm, Z, Wm, g, l16, wave, u.T, u.B,
+        sm, Z, Wm, g, l16, wave, oT, ob,
         va.out ? out_rsrc(va, r, h, DV, max(D, 1)) : make_rsrc(nullptr, 0), col_of(), va, nr, gt,
-        nred);
+        nred, split ? 1 : 0);
   } else {
     contract<DK, DV, NT, kY | kZ>(sm, H, g, l16, Y, Z);
     arr.grid_in(HV, rank_ctr, grid_ctr, tid);
     solve_w<DK, DV, NT>(sm, Y, col_of(), g, l16, Wm);
-    emit_outputs<DK, DV, NT>(sm, Z, Wm, g, l16, 0, u.T, u.B, out_rsrc(va, r, h, DV, max(D, 1)),
-                             col_of() * 4, HV * DV * 4);
+    emit_outputs<DK, DV, NT>(sm, Z, Wm, g, l16, 0, oT, ob, out_rsrc(va, r, h, DV, max(D, 1)),
+                             col_of() * 4, HV * DV * 4, split ? 1 : 0);
   }
   const bool kq_writer = due ? group_rank == G - 1 : h % G == 0;
   if (due)
-    sga.append(sm, sr, u, 0, u.T, kq_writer);
+    sga.append(sm, sr, u, 0, u.T, kq_writer, split);
   else if (wave < SW)
-    sgs.append(sm, sr, u, 0, u.T, kq_writer);
+    sgs.append(sm, sr, u, 0, u.T, kq_writer, split);
   if (due && kq_writer && tid == 0) *group_ctr = 0;  // every member has counted in
   finish();
 }

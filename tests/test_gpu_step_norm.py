@@ -125,14 +125,24 @@ def _step_pair(wl, seed, steps, varlen_lens=False, with_oracle=False, write_out=
         for name in FIELDS:
             assert torch.equal(_bits(getattr(a, name)), _bits(getattr(b, name))), name
         ob = out_b.cpu().numpy()
+        Ds = np.full(R, D) if lens is None else lens
+        rows = np.arange(D)[None, :] < Ds[:, None]          # draft rows of every request
         if write_out:
-            assert torch.equal(_bits(o_a), _bits(out_b)), "out"
+            # the fused kernel places the draft at fixed rows of its chunk (a
+            # split output chunk), which changes the rounding order only; rows
+            # past a request's draft keep their canary in both
+            oa_h = o_a.cpu().numpy()
+            assert np.array_equal(oa_h[~rows], ob[~rows]) and (ob[~rows] == 3.0).all(), "out rows"
+            scale = max(float(np.abs(ob[rows]).max()), 1e-30)
+            assert np.abs(oa_h[rows] - ob[rows]).max() <= 2e-4 * scale, "out"
         else:
             assert o_a is None
         qn, sn = q.cpu().numpy(), s.cpu().numpy()
-        Ds = np.full(R, D) if lens is None else lens
-        rows = np.arange(D)[None, :] < Ds[:, None]          # draft rows of every request
-        ambig += _check_codes(ob, zb, w, qn, sn, rows)
+        # the boundary-aware check runs on the fused kernel's own outputs (its
+        # rounding order is not the separate step's); without them, the codes
+        # are checked against a run that writes them (and the fp64 chain)
+        if write_out:
+            ambig += _check_codes(oa_h, zb, w, qn, sn, rows)
         assert (qn[~rows] == CANARY_Q).all() and (sn[~rows] == CANARY_S).all()
         if orc is not None:
             orc.rollback(slots, D, pa, draft_lens=pl)

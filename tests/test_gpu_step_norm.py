@@ -157,12 +157,17 @@ def _step_pair(wl, seed, steps, varlen_lens=False, with_oracle=False, write_out=
     say(f"  {ambig} codes at a rounding midpoint (either neighbour accepted)")
 
 
-@pytest.mark.parametrize("d,varlen", [(128, False), (128, True), (64, False), (64, True)])
-def test_step_norm_parity(d, varlen):
-    wl = synth.Workload("sn", 6, 8, 8, 4, d, d, 32, 16, synth.BF16, 16, 1, "clipnormal:12:3",
-                        "uniform:0:15")
-    say(f"case step_norm d={d} varlen={varlen}")
-    for _ in _step_pair(wl, 900 + d + varlen, 5, varlen_lens=varlen, with_oracle=True):
+# draft 16 and a flush every 16: the split output chunk (draft rows from row
+# 16); a flush every 24 (up to 23 committed rows) or a draft of 20: the plain
+# layout for those slots
+@pytest.mark.parametrize("d,varlen,draft,flush", [(128, False, 16, 16), (128, True, 16, 16),
+                                                  (64, False, 16, 16), (64, True, 16, 16),
+                                                  (128, False, 8, 24), (128, True, 20, 12)])
+def test_step_norm_parity(d, varlen, draft, flush):
+    wl = synth.Workload("sn", 6, 8, 8, 4, d, d, 32, draft, synth.BF16, flush, 1,
+                        "clipnormal:12:3", f"uniform:0:{min(flush, 32 - draft) - 1}")
+    say(f"case step_norm d={d} varlen={varlen} draft={draft} flush={flush}")
+    for _ in _step_pair(wl, 900 + d + varlen + draft, 5, varlen_lens=varlen, with_oracle=True):
         pass
 
 

@@ -54,11 +54,11 @@ KERNEL_SRCS = [os.path.join(ROOT, "gated_deltanet_state_replayssm_amd", "csrc", 
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-def measured_traffic(kernel: str):
-    """HBM bytes per launch of `kernel` ("verify", "flush" or "verify_flush")
-    measured with rocprofv3 FETCH_SIZE / WRITE_SIZE (scaled by a copy of known
-    size) and recorded in a profiles/ summary, or None when no summary matches
-    the current kernel source."""
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` ("verify", "flush", "verify_flush", ...)
+    on `workload`, measured with rocprofv3 FETCH_SIZE / WRITE_SIZE (scaled by a
+    copy of known size) and recorded in a profiles/ summary, or None when no
+    summary of that workload matches the current kernel source."""
     import glob
     import hashlib
     import re
@@ -68,9 +68,10 @@ def measured_traffic(kernel: str):
     sha = h.hexdigest()[:16]
     for path in sorted(glob.glob(os.path.join(PROFILES, "*.md"))):
         for line in open(path):
-            m = re.search(r"traffic source_sha=(\w+)((?: \w+_mb_per_launch=[\d.]+)+)", line)
-            if m and m.group(1) == sha:
-                vals = dict(re.findall(r"(\w+)_mb_per_launch=([\d.]+)", m.group(2)))
+            m = re.search(r"traffic source_sha=(\w+) workload=(\w+)((?: \w+_mb_per_launch=[\d.]+)+)",
+                          line)
+            if m and m.group(1) == sha and m.group(2) == workload:
+                vals = dict(re.findall(r"(\w+)_mb_per_launch=([\d.]+)", m.group(3)))
                 if kernel in vals:
                     return int(float(vals[kernel]) * 1e6)
     return None
@@ -749,7 +750,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": dom["gbps"],
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(dom["gbps"] / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic(dominant),
+                     "traffic": measured_traffic(dominant, wl.name),
                      "bytes_per_launch": dom["bytes"], "us_per_launch": dom["us"]},
         "pages_context": {"b200_custom_kernel_us_per_layer": "23-24",
                           "b200_triton_us_per_layer": "72-80"},

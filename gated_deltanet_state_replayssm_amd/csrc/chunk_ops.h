@@ -967,6 +967,62 @@ __device__ __forceinline__ void solve_w(const SM &sm, const f32x4 (&Y)[2][NT], i
   }
 }
 
+// The output chunk's outputs need W only through C W = C (I + A)^-1 diag(beta)
+// (V - diag(gamma) Y): M = C (I + A)^-1 diag(beta) depends on the inputs alone,
+// so it is formed once the T x T matrices are built (ahead of the state) and
+// then O = gamma Z + M X' with X' = V - diag(gamma) Y, one product after the
+// contraction instead of two. build_m: one wave, M into sm.Cm (in place: every
+// read of Cm and T precedes the writes, LDS accesses of a wave in program
+// order). Tiles (0,0), (1,0), (1,1) (tile (0,1) of C, and so of M, is zero);
+// fp32 operands split into hi + lo bf16 as in the other products.
+template <int DK, int DV, class SM>
+__device__ __forceinline__ void build_m(SM &sm, int g, int l16) {
+  bf16x8 ch[2], cl[2], th[2], tl[2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    float crow[8], tcol[8];
+    rd_frow(sm.Cm, 16 * a + l16, g, crow);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      tcol[j] = sm.T[4 * g + j][16 * a + l16];
+      tcol[4 + j] = sm.T[16 + 4 * g + j][16 * a + l16];
+    }
+    split8(crow, ch[a], cl[a]);
+    split8(tcol, th[a], tl[a]);
+  }
+  float bcol[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) bcol[b] = sm.bet[16 * b + l16];
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+  for (int b = 0; b < 3; ++b) {
+    const int ta = b == 0 ? 0 : 1, tb = b == 2 ? 1 : 0;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    acc = mfma(ch[ta], th[tb], acc);
+    acc = mfma(ch[ta], tl[tb], acc);
+    acc = mfma(cl[ta], th[tb], acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sm.Cm[16 * ta + 4 * g + i][16 * tb + l16] = acc[i] * bcol[tb];
+  }
+}
+
+// X' = V - gamma Y (the output chunk's operand of M); this lane's entries as in
+// solve_w.
+template <int DK, int DV, int NT, class SM>
+__device__ __forceinline__ void x_prime(const SM &sm, const f32x4 (&Y)[2][NT], int colL, int g,
+                                        f32x4 (&Xm)[2][NT]) {
+  typedef typename Cols<NT>::U U;
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float ga = sm.gam[16 * a + 4 * g + i];
+      const U vv = *reinterpret_cast<const U *>(&sm.v[16 * a + 4 * g + i][colL]);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) Xm[a][nt][i] = bf16_to_f32(vv[nt]) - ga * Y[a][nt][i];
+    }
+}
+
 // out[r][0..D-1][h][0..DV-1] of one (request, value head), rows HV DV floats apart;
 // D >= 1 is the request's draft length (request r's rows start at r * va.draft)
 __device__ __forceinline__ Rsrc out_rsrc(const VerifyArgs &va, int r, int h, int DV, int D) {

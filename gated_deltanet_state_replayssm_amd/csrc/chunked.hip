@@ -149,9 +149,11 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_chunked(Verif
     else if (wave == 1)
       build_c<DK, DV>(sm, al, lane, g, l16);
     __syncthreads();  // T x T matrices complete
+    if (wave == 1) build_m<DK, DV>(sm, g, l16);
     f32x4 Y[2][NT], Z[2][NT], Wm[2][NT];
     contract<DK, DV, NT, kY | kZ>(sm, H, g, l16, Y, Z);
-    solve_w<DK, DV, NT>(sm, Y, col_of(), g, l16, Wm);
+    lds_barrier();  // M complete (LDS only)
+    x_prime<DK, DV, NT>(sm, Y, col_of(), g, Wm);
     emit_outputs<DK, DV, NT>(sm, Z, Wm, g, l16, t0, Treal, u.B, out_rsrc(va, r, h, DV, T - u.B),
                              col_of() * 4, HV * DV * 4);
     // the draft rows, from LDS; the thread mapping is that of the stage type
@@ -267,10 +269,17 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_single(Verify
     build_c<DK, DV>(sm, sg.al, lane, g, l16);
   }
   __syncthreads();  // T x T matrices complete
+  if constexpr (VERIFY) {
+    if (wave == (WAVES > 1 ? 1 : 0)) build_m<DK, DV>(sm, g, l16);
+  }
 
   f32x4 Y[2][NT], Z[2][NT], Wm[2][NT];
   contract<DK, DV, NT, VERIFY ? (kY | kZ) : kY>(sm, H, g, l16, Y, Z);
-  solve_w<DK, DV, NT>(sm, Y, colL, g, l16, Wm);
+  if constexpr (VERIFY) {
+    lds_barrier();  // M complete (LDS only)
+    x_prime<DK, DV, NT>(sm, Y, colL, g, Wm);
+  } else
+    solve_w<DK, DV, NT>(sm, Y, colL, g, l16, Wm);
   if constexpr (VERIFY) {
     emit_outputs<DK, DV, NT>(sm, Z, Wm, g, l16, 0, T, u.B, out_rsrc(va, r, h, DV, T - u.B),
                              colL * 4, HV * DV * 4);

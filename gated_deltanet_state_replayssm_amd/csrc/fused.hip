@@ -654,6 +654,7 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyA
     build_c<DK, DV>(sm, al, lane, g, l16);
   }
   __syncthreads();  // T x T matrices complete
+  if (wave == (WAVES > 1 ? 1 : 0)) build_m<DK, DV>(sm, g, l16);
 
   f32x4 Y[2][NT], Z[2][NT], Wm[2][NT];
   if constexpr (NORM) {
@@ -664,7 +665,8 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyA
     const Gate gt = load_gate<DV, NT>(va, nr, col_of(), g, ob, oT);
     contract<DK, DV, NT, kY | kZ>(sm, H, g, l16, Y, Z);
     arr.grid_in(HV, rank_ctr, grid_ctr, tid);
-    solve_w<DK, DV, NT>(sm, Y, col_of(), g, l16, Wm);
+    lds_barrier();  // M complete (LDS only)
+    x_prime<DK, DV, NT>(sm, Y, col_of(), g, Wm);
     __shared__ __align__(16) float nred[2][kCh][4];
     emit_outputs_norm<DK, DV, NT>(
         sm, Z, Wm, g, l16, wave, oT, ob,
@@ -673,7 +675,8 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyA
   } else {
     contract<DK, DV, NT, kY | kZ>(sm, H, g, l16, Y, Z);
     arr.grid_in(HV, rank_ctr, grid_ctr, tid);
-    solve_w<DK, DV, NT>(sm, Y, col_of(), g, l16, Wm);
+    lds_barrier();  // M complete (LDS only)
+    x_prime<DK, DV, NT>(sm, Y, col_of(), g, Wm);
     emit_outputs<DK, DV, NT>(sm, Z, Wm, g, l16, 0, oT, ob, out_rsrc(va, r, h, DV, max(D, 1)),
                              col_of() * 4, HV * DV * 4, split ? 1 : 0);
   }
@@ -896,11 +899,13 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused_long(Ve
   else if (wave == 1)
     build_c<DK, DV>(sm, al, lane, g, l16);
   __syncthreads();  // T x T matrices complete
+  if (wave == 1) build_m<DK, DV>(sm, g, l16);
   {
     f32x4 Y[2][NT], Z[2][NT], Wm[2][NT];
     contract<DK, DV, NT, kY | kZ>(sm, H, g, l16, Y, Z);
     arr.grid_in(HV, rank_ctr, grid_ctr, tid);
-    solve_w<DK, DV, NT>(sm, Y, col_of(), g, l16, Wm);
+    lds_barrier();  // M complete (LDS only)
+    x_prime<DK, DV, NT>(sm, Y, col_of(), g, Wm);
     emit_outputs<DK, DV, NT>(sm, Z, Wm, g, l16, t0, Treal, uo.B,
                              out_rsrc(va, r, h, DV, max(Dq, 1)), col_of() * 4, HV * DV * 4);
   }

@@ -131,45 +131,35 @@ __device__ __forceinline__ void emit_outputs_norm(const SM &sm,
            ((t0 >= B && t0 < Treal) || (t0 + 4 >= B && t0 + 4 < Treal) ||
             (t0 + 8 >= B && t0 + 8 < Treal) || (t0 + 12 >= B && t0 + 12 < Treal));
   };
-  // Mean square of each row: the rows' reductions are independent chains. 1/r
-  // comes from the hardware reciprocal square root (1 ulp) and the gate's
-  // 1/(1 + e^-z) and 1/max|y| from the hardware reciprocal: r only sets the
-  // scale (the codes are y / max|y|, where it cancels), and all three sit far
-  // inside the scale's and the codes' tolerance.
-  float acc[2][4];
+  // One pass over each row, one exchange between the waves: the mean square
+  // and the largest |u_j|, u_j = o_j w_j silu(z_j). Since y_j = u_j / r, the
+  // row's max |y| is max |u| / r and the codes y_j / s = 448 u_j / max|u| need
+  // no r at all; r sets only the scale s = max|u| / (448 r). 1/r comes from the
+  // hardware reciprocal square root (1 ulp) and the gate's 1/(1 + e^-z) and
+  // 1/max|u| from the hardware reciprocal, all far inside the scale's and the
+  // codes' tolerance. The rows' reductions are independent chains.
+  float u[2][NT][4];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (!slot_live(a, i)) continue;
-      float ss = 0.f;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) ss = fmaf(O[a][nt][i], O[a][nt][i], ss);
-      acc[a][i] = row16_reduce<false>(ss);
-      if (l16 == 15) red[0][16 * a + 4 * g + i][wave] = acc[a][i];
-    }
-  __syncthreads();
-  float y[2][NT][4];
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (!slot_live(a, i)) continue;
-      const float4 p = *reinterpret_cast<const float4 *>(red[0][16 * a + 4 * g + i]);
-      const float tot = WAVES == 4 ? (p.x + p.y) + (p.z + p.w) : p.x + p.y;
-      const float rinv =
-          __builtin_amdgcn_rsqf(fmaxf(fmaf(tot, 1.f / DV, va.norm_eps), 1.17549435e-38f));
-      float amax = 0.f;
+      float ss = 0.f, mx = 0.f;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
+        ss = fmaf(O[a][nt][i], O[a][nt][i], ss);
         const uint32_t zb = gt.z[a][i];
         const float zf = __uint_as_float(nt == 0 ? zb << 16 : zb & 0xffff0000u);
         const float gate = zf * __builtin_amdgcn_rcpf(1.f + __expf(-zf));
-        y[a][nt][i] = O[a][nt][i] * rinv * gt.w[nt] * gate;
-        amax = fmaxf(amax, fabsf(y[a][nt][i]));
+        u[a][nt][i] = O[a][nt][i] * gt.w[nt] * gate;
+        mx = fmaxf(mx, fabsf(u[a][nt][i]));
       }
-      acc[a][i] = row16_reduce<true>(amax);
-      if (l16 == 15) red[1][16 * a + 4 * g + i][wave] = acc[a][i];
+      ss = row16_reduce<false>(ss);
+      mx = row16_reduce<true>(mx);
+      if (l16 == 15) {
+        red[0][16 * a + 4 * g + i][wave] = ss;
+        red[1][16 * a + 4 * g + i][wave] = mx;
+      }
     }
   __syncthreads();
 #pragma unroll
@@ -179,23 +169,34 @@ __device__ __forceinline__ void emit_outputs_norm(const SM &sm,
       if (!slot_live(a, i)) continue;
       const int t = 16 * a + 4 * g + i;
       const bool row = t < Treal && t >= B;
-      const float4 p = *reinterpret_cast<const float4 *>(red[1][t]);
-      const float amax = WAVES == 4 ? fmaxf(fmaxf(p.x, p.y), fmaxf(p.z, p.w)) : fmaxf(p.x, p.y);
-      float scale = 1.f, inv = 1.f;
+      const float4 p = *reinterpret_cast<const float4 *>(red[0][t]);
+      const float4 m = *reinterpret_cast<const float4 *>(red[1][t]);
+      const float tot = WAVES == 4 ? (p.x + p.y) + (p.z + p.w) : p.x + p.y;
+      const float umax = WAVES == 4 ? fmaxf(fmaxf(m.x, m.y), fmaxf(m.z, m.w)) : fmaxf(m.x, m.y);
+      const float rinv =
+          __builtin_amdgcn_rsqf(fmaxf(fmaf(tot, 1.f / DV, va.norm_eps), 1.17549435e-38f));
+      const float amax = umax * rinv;  // max |y|
+      float scale = 1.f, inv = 1.f;    // inv: 448 / max|u|
       if (amax >= 0x1p-126f) {
         scale = amax * (1.f / kE4M3Max);
-        inv = kE4M3Max * __builtin_amdgcn_rcpf(amax);
-      } else if (amax > 0.f) {  // a subnormal maximum: exact quotients
+      } else if (amax > 0.f) {  // a subnormal maximum: the exact quotient
         scale = amax / kE4M3Max;
-        inv = kE4M3Max / amax;
       }
+      if (umax >= 0x1p-126f)
+        inv = kE4M3Max * __builtin_amdgcn_rcpf(umax);
+      else if (umax > 0.f)
+        inv = kE4M3Max / umax;
       // clamp first: the conversion then never sees a value past the largest code
-      const float c0 = fminf(fmaxf(y[a][0][i] * inv, -kE4M3Max), kE4M3Max);
-      const float c1 = fminf(fmaxf(y[a][1][i] * inv, -kE4M3Max), kE4M3Max);
+      const float c0 = fminf(fmaxf(u[a][0][i] * inv, -kE4M3Max), kE4M3Max);
+      const float c1 = fminf(fmaxf(u[a][1][i] * inv, -kE4M3Max), kE4M3Max);
       const uint32_t packed = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c0, c1, 0, false);
-      bstore((uint16_t)(packed & 0xffff), nr.q, row ? (uint32_t)(t - B) * q_row + col : kOOB);
+      // write-back stores: the four waves' 32-byte pieces of a row's 128 code
+      // bytes meet in L2 and leave it as one line (written through, each piece
+      // went to memory on its own: 20 us of 135 at 128 requests)
+      bstore<uint16_t, 0>((uint16_t)(packed & 0xffff), nr.q,
+                          row ? (uint32_t)(t - B) * q_row + col : kOOB);
       if (wave == 0 && l16 == 0)
-        bstore(scale, nr.scale, row ? (uint32_t)(t - B) * s_row : kOOB);
+        bstore<float, 0>(scale, nr.scale, row ? (uint32_t)(t - B) * s_row : kOOB);
     }
 }
 
@@ -667,7 +668,11 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyA
     arr.grid_in(HV, rank_ctr, grid_ctr, tid);
     lds_barrier();  // M complete (LDS only)
     x_prime<DK, DV, NT>(sm, Y, col_of(), g, Wm);
-    __shared__ __align__(16) float nred[2][kCh][4];
+    // the norm's cross-wave partials in the T x T array: (I + A)^-1 has no
+    // reader after M (an array of their own took the LDS past 4 workgroups
+    // per CU: 39.4 KB)
+    float(*nred)[kCh][4] = reinterpret_cast<float(*)[kCh][4]>(&sm.T[0][0]);
+    static_assert(sizeof(sm.T) >= 2 * kCh * 4 * sizeof(float), "partials fit");
     emit_outputs_norm<DK, DV, NT>(
         sm, Z, Wm, g, l16, wave, oT, ob,
         va.out ? out_rsrc(va, r, h, DV, max(D, 1)) : make_rsrc(nullptr, 0), col_of(), va, nr, gt,

@@ -501,6 +501,44 @@ struct Arrival {
 // for their fold. So each workgroup of a due slot counts itself in at the
 // (slot, key head) counter once its fold inputs are staged, and the last
 // one of the key head's group appends k and q (the others have read by then).
+// Warms L2 with one dword of every 128-byte line of a request's draft rows
+// (keys and queries of key head kh, values, alpha and beta of value head h),
+// one line per thread: issued at the start, when memory is quiet, by the
+// workgroup at the request's unordered position. The workgroup that stages
+// those rows after the ordering pass has the same value head and, with HV a
+// multiple of 8, runs on the same XCD (position mod 8), so its reads then hit
+// that L2 instead of queueing behind the state stream. Returns the OR of the
+// loaded words, for the caller to consume at its end.
+template <int DK, int DV>
+__device__ __forceinline__ uint32_t warm_draft(const VerifyArgs &va, int rn, int h, int kh,
+                                               int tid) {
+  constexpr int KL = DK * 2 / 128, VL = DV * 2 / 128;  // lines per key / value row
+  const int HV = va.c.hv, HK = va.c.hk, D = va.draft;
+  const int64_t d0 = (int64_t)rn * D;
+  int t = tid, a = 0;
+  if (t >= D * KL) { t -= D * KL; a = 1; }
+  if (a == 1 && t >= D * KL) { t -= D * KL; a = 2; }
+  if (a == 2 && t >= D * VL) { t -= D * VL; a = 3; }
+  if (a == 3 && t >= D) { t -= D; a = 4; }
+  if (a == 4 && t >= D) return 0u;  // past the request's lines
+  const uint32_t kq_bytes = (D - 1) * HK * DK * 2 + DK * 2;
+  Rsrc r;
+  uint32_t off;
+  if (a <= 1) {
+    r = make_rsrc(static_cast<const uint16_t *>(a == 0 ? va.k : va.q) + (d0 * HK + kh) * DK,
+                  kq_bytes);
+    off = (uint32_t)(t / KL) * HK * DK * 2 + (t % KL) * 128;
+  } else if (a == 2) {
+    r = make_rsrc(static_cast<const uint16_t *>(va.v) + (d0 * HV + h) * DV,
+                  (D - 1) * HV * DV * 2 + DV * 2);
+    off = (uint32_t)(t / VL) * HV * DV * 2 + (t % VL) * 128;
+  } else {
+    r = make_rsrc((a == 3 ? va.alpha : va.beta) + d0 * HV + h, (D - 1) * HV * 4 + 4);
+    off = (uint32_t)t * HV * 4;
+  }
+  return bload<uint32_t>(r, off);
+}
+
 template <int DK, int DV, int NT, bool VARLEN, bool ROLLBACK, bool NORM>
 __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyArgs va,
                                                                          int min_len) {
@@ -530,9 +568,23 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyA
     return (uint32_t)((4 * ((t & 63) >> 4) * DV + (t / 64) * 16 * NT + NT * (t & 15)) * 4);
   };
   const int mn = max(min_len, 1);
+  const int h = head_of(blockIdx.x % HV, HV, G);
+  // (the first generation of workgroups only, 256 CUs x 4: later ones start
+  // with memory busy, where the extra requests measured 1 % slower)
+  uint32_t warm = 0u;
+  if (blockIdx.x < 1024) warm = warm_draft<DK, DV>(va, blockIdx.x / HV, h, h / G, tid);
+  if constexpr (NORM) {
+    // and the gate rows the norm reads (two lines of bf16 per row at d_v 128)
+    constexpr int ZL = DV * 2 / 128;
+    const int t = tid - 128;
+    if (blockIdx.x < 1024 && t >= 0 && t < va.draft * ZL) {
+      const NormRsrc nr = norm_rsrc(va, blockIdx.x / HV, h, DV, va.draft);
+      warm |= bload<uint32_t>(nr.z, (uint32_t)(t / ZL) * HV * DV * 2 + (t % ZL) * 128);
+    }
+  }
   const Req rq = ordered_request<ROLLBACK, VARLEN>(va, mn, blockIdx.x / HV, lane,
                                                   wave == 0 ? moves : nullptr);
-  const int r = rq.r, h = head_of(blockIdx.x % HV, HV, G);
+  const int r = rq.r;
   const bool lead = (h == 0 && tid == 0);
   int32_t *grid_ctr = c.sync;
   int32_t *rank_ctr = slot_counter(c, blockIdx.x / HV);
@@ -691,6 +743,7 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyA
   else if (wave < SW)
     sgs.append(sm, sr, u, 0, u.T, kq_writer, split);
   if (due && kq_writer && tid == 0) *group_ctr = 0;  // every member has counted in
+  asm volatile("" ::"v"(warm));  // (the warming loads' results, consumed)
   finish();
 }
 

@@ -466,8 +466,8 @@ struct Stage {
   template <class SM>
   __device__ __forceinline__ void append(const SM &sm, const Srcs &sr, const Unit &u,
                                          int t0, int Treal, bool kq_writer,
-                                         bool gap = false) const {
-    const int tid = opaque_tid();
+                                         bool gap = false, int tid0 = 0) const {
+    const int tid = opaque_tid() - tid0;  // threads tid0 .. tid0 + THREADS - 1
     // Recompute the row offsets here rather than keep those of the loads alive
     // in registers through the whole kernel: the copy of the unit is opaque to
     // the compiler, so it cannot reuse them.

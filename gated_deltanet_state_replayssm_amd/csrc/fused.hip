@@ -699,6 +699,13 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyA
     }
   }
   __syncthreads();
+  // The draft rows go to the ring now, off the launch's tail, by the waves
+  // that build nothing.
+  constexpr int AW = WAVES >= 4 ? 2 : 1;  // appending waves: the last AW
+  const bool kq_writer = due ? group_rank == G - 1 : h % G == 0;
+  if (wave >= WAVES - AW)
+    Stage<DK, DV, NT, true, 64 * AW>{}.append(sm, sr, u, 0, u.T, kq_writer, split,
+                                              64 * (WAVES - AW));
   arr.take_rank(HV, rank_ctr, tid);
   if (wave == 0) {
     build_tt<DK, DV>(sm, al, lane, g, l16);
@@ -737,11 +744,6 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyA
     emit_outputs<DK, DV, NT>(sm, Z, Wm, g, l16, 0, oT, ob, out_rsrc(va, r, h, DV, max(D, 1)),
                              col_of() * 4, HV * DV * 4, split ? 1 : 0);
   }
-  const bool kq_writer = due ? group_rank == G - 1 : h % G == 0;
-  if (due)
-    sga.append(sm, sr, u, 0, u.T, kq_writer, split);
-  else if (wave < SW)
-    sgs.append(sm, sr, u, 0, u.T, kq_writer, split);
   if (due && kq_writer && tid == 0) *group_ctr = 0;  // every member has counted in
   asm volatile("" ::"v"(warm));  // (the warming loads' results, consumed)
   finish();

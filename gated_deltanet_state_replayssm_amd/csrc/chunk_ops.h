@@ -562,30 +562,37 @@ __device__ __forceinline__ void dma4(Rsrc r, char *lds, uint32_t voff) {
 // Rows past Treal, and committed rows' queries, come in as zeros (a reader
 // takes alpha = 1 past Treal). The caller's barriers while the DMA is in flight
 // are lds_barrier(); the next __syncthreads() waits for it.
+// RING: every row of the chunk is a committed ring row (a folded chunk: the
+// draft is always in the stream's last chunk), so each piece has one source
+// and no lane takes the draft's branch.
 template <int DK, int DV, int NW>
 struct Prefetch {
-  template <class SM>
+  template <bool RING = false, class SM>
   __device__ __forceinline__ void issue_k(SM &sm, const Srcs &sr, const Unit &u, int t0,
                                           int Treal) const {
     const int tid = opaque_tid(), lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     dma_rows<DK, NW>(sm.k, wv, lane, [&](int t, int pc, char *dst, bool data) {
       const RowAt<true> at(u, t0, t, Treal, DK * 2, sr.dk_row);
-      if (data && at.ring != kOOB)
+      if constexpr (RING)
+        dma16<0>(sr.rk, dst, data ? at.ring + pc * 16 : kOOB);
+      else if (data && at.ring != kOOB)
         dma16<0>(sr.rk, dst, at.ring + pc * 16);
       else
         dma16<kStream>(sr.dk, dst, data ? at.draft + pc * 16 : kOOB);
     });
   }
 
-  template <class SM>
+  template <bool RING = false, class SM>
   __device__ __forceinline__ void issue_v(SM &sm, const Srcs &sr, const Unit &u, int t0,
                                           int Treal) const {
     const int tid = opaque_tid(), lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     dma_rows<DV, NW>(sm.v, wv, lane, [&](int t, int pc, char *dst, bool data) {
       const RowAt<true> at(u, t0, t, Treal, DV * 2, sr.dv_row);
-      if (data && at.ring != kOOB)
+      if constexpr (RING)
+        dma16<0>(sr.rv, dst, data ? at.ring + pc * 16 : kOOB);
+      else if (data && at.ring != kOOB)
         dma16<0>(sr.rv, dst, at.ring + pc * 16);
       else
         dma16<kStream>(sr.dv, dst, data ? at.draft + pc * 16 : kOOB);
@@ -594,7 +601,7 @@ struct Prefetch {
 
   // beta then alpha of the chunk's rows (sm.bet and sm.alp adjacent): lane
   // l < 32 beta of row l, lane 32 + l alpha of row l; by the last wave
-  template <class SM>
+  template <bool RING = false, class SM>
   __device__ __forceinline__ void issue_ab(SM &sm, const Srcs &sr, const Unit &u, int t0,
                                            int Treal) const {
     const int tid = opaque_tid(), lane = tid & 63;
@@ -602,7 +609,7 @@ struct Prefetch {
       const int t = lane & (kCh - 1);
       const RowAt<true> at(u, t0, t, Treal, 4, sr.dab_row);
       char *dst = reinterpret_cast<char *>(&sm.bet[0]);
-      if (at.ring != kOOB) {
+      if (RING || at.ring != kOOB) {
         if (lane < kCh)
           dma4<0>(sr.rb, dst, at.ring);
         else

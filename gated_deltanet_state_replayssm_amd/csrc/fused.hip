@@ -924,8 +924,8 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused_long(Ve
     lds_barrier();  // T x T matrices built, keys, beta and alpha copied
     // the next chunk: the stream's next fold chunk, or the output chunk
     if (!last) {
-      pf.issue_k(smn, s1, u1, T0 + kCh * ch, kCh);
-      pf.issue_ab(smn, s1, u1, T0 + kCh * ch, kCh);
+      pf.template issue_k<true>(smn, s1, u1, T0 + kCh * ch, kCh);
+      pf.template issue_ab<true>(smn, s1, u1, T0 + kCh * ch, kCh);
     } else {
       const Srcs so = out_srcs();
       pf.issue_k(smn, so, uo, t0, Treal);
@@ -936,7 +936,7 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused_long(Ve
     solve_w<DK, DV, NT>(smc, Y, col_of(), g, l16, Wm);
     lds_barrier();  // every wave has read the values
     if (!last)
-      pf.issue_v(smn, s1, u1, T0 + kCh * ch, kCh);
+      pf.template issue_v<true>(smn, s1, u1, T0 + kCh * ch, kCh);
     else
       pf.issue_v(smn, out_srcs(), uo, t0, Treal);
     fold_state<DK, DV, NT, true>(smc, Wm, g, l16, H);

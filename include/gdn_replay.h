@@ -210,8 +210,9 @@ int gdn_replay_verify_flush(const gdn_replay_cache *c, int32_t num_reqs, const i
  *
  * The draft arrays keep the layout of the fixed-length calls with
  * D = max_draft: request i's tokens are rows 0 .. D_i - 1 of its max_draft-row
- * block of q, k, v, alpha, beta and out. Rows D_i .. max_draft - 1 are neither
- * read nor written.
+ * block of q, k, v, alpha, beta and out, so all num_reqs * max_draft rows must
+ * be allocated. Rows D_i .. max_draft - 1 are never written and their values
+ * are never used (verify_flush may load them into cache ahead of use).
  *
  *   draft_lens [num_reqs] int32 (device).   max_draft: 1..C (host value).
  * Device errors as for the fixed-length calls, plus DRAFT when D_i is outside

@@ -434,7 +434,15 @@ struct Arrival {
     if (!counting || gridded) return;
     take_rank(HV, rank_ctr, tid);
     gridded = true;
-    gticket = (rank_last && tid == 0) ? atomicAdd(grid_ctr, 1) : -1;
+    // A buffer atomic at an opaque per-lane offset: at a uniform address the
+    // compiler rewrites the atomic as a wave-wide one and waits for its return
+    // at once, which also waits for every store issued before it. Its return is
+    // awaited where it is read, at the end.
+    int off = 0;
+    asm volatile("" : "+v"(off));
+    gticket = -1;
+    if (rank_last && tid == 0)
+      gticket = __builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(1, make_rsrc(grid_ctr, 4), off, 0, 0);
   }
 
   // End of the workgroup: the grid's last arrival moves the pointers (wave 0).
@@ -881,10 +889,15 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused_long(Ve
   const int t0 = due ? 0 : (nch == 1 ? 0 : T0 + kCh * (nch - 2));
   const int Treal = due ? Dq : (nch == 1 ? T0 : kCh);
   {
-    // waves SW.. load their state first; waves 0..SW-1 stage chunk 0, then load.
-    // One load_state for both, so that the state is assigned its registers once
-    // (two call sites met at the chunk loop with two assignments, and the
-    // copies between them spilled).
+    // Waves 0..SW-1 stage chunk 0, then load their state. In a workgroup with
+    // two fold chunks or more (the launch's long chains) waves SW.. load their
+    // state at once; in one with a shorter chain they wait until chunk 0 is
+    // staged, so that the long chains' inputs and states enter the memory
+    // queues ahead of theirs (1 us less per launch at 32 requests, capacity
+    // 80). One load_state for both, so that the state is assigned its
+    // registers once (two call sites met at the chunk loop with two
+    // assignments, and the copies between them spilled). The barriers wait for
+    // LDS only.
     al = 1.f;
     if (wave < SW) {
       Stage<DK, DV, NT, true, 64 * SW> sg0;
@@ -892,19 +905,29 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused_long(Ve
       sg0.template store<false>(smn, T0, out0);
       al = sg0.al;
     }
+    if (nfold < 2) lds_barrier();
     __builtin_amdgcn_sched_barrier(0);
     load_state<DK, DV, NT>(st, st_off_of(), H);
     __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
+    if (nfold >= 2) lds_barrier();
+  }
+  // A fold chunk 0 has its T x T matrices built (and its keys copied) while the
+  // state loads are in flight, ahead of the loop: the state's registers are
+  // copied into the loop's at its entry, and those copies wait for the loads.
+  if (nfold > 0) {
+    if (wave == 0)
+      build_tt<DK, DV>(smn, al, lane, g, l16);
+    else
+      copy_chunk_keys<DK, 64 * (WAVES - 1)>(lds_kn, lds_kc, lds_abn, lds_abc, opaque_tid() - 64);
   }
   arr.take_rank(HV, rank_ctr, tid);
   // Every chunk after the first is staged by LDS DMA while its predecessor is
   // computed: its keys, beta and alpha once the predecessor's T x T matrices
   // are built (and its keys copied), its values once W has read the previous
   // values. While DMA is in flight the barriers are lds_barrier(): a
-  // __syncthreads() waits for it. The one at a chunk's end does wait, so that
-  // no DMA is in flight across the loop's back edge (the compiler would then
-  // wait for all loads, the state's included, in the first chunk's build).
+  // __syncthreads() waits for it. The one at a chunk's end does wait (with the
+  // values' DMA left in flight across the loop's back edge, the compiler waits
+  // for it before the next chunk's first LDS read anyway).
   Prefetch<DK, DV, WAVES> pf;
 #pragma nounroll
   for (int ch = 0; ch < nfold; ++ch) {
@@ -915,11 +938,13 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused_long(Ve
     // a due slot's fold inputs are all read: count in for the key rows' append
     // (the last wave waits for the return, which comes after its state loads)
     if (due && last && tid == 64 * (WAVES - 1)) group_rank = atomicAdd(group_ctr, 1);
-    if (wave == 0) {
-      if (ch > 0) al = smn.alp[lane & (kCh - 1)];
-      build_tt<DK, DV>(smn, al, lane, g, l16);
-    } else {
-      copy_chunk_keys<DK, 64 * (WAVES - 1)>(lds_kn, lds_kc, lds_abn, lds_abc, opaque_tid() - 64);
+    if (ch > 0) {
+      if (wave == 0) {
+        al = smn.alp[lane & (kCh - 1)];
+        build_tt<DK, DV>(smn, al, lane, g, l16);
+      } else {
+        copy_chunk_keys<DK, 64 * (WAVES - 1)>(lds_kn, lds_kc, lds_abn, lds_abc, opaque_tid() - 64);
+      }
     }
     lds_barrier();  // T x T matrices built, keys, beta and alpha copied
     // the next chunk: the stream's next fold chunk, or the output chunk
@@ -948,17 +973,22 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused_long(Ve
   const Srcs so = out_srcs();
   // its queries into keys buffer c, which the last fold has finished reading
   if (!out0) pf.issue_q(sm, so, uo, t0, Treal);
-  if (due) store_state<DK, DV, NT>(st, st_off_of(), H);
+  // waits for the output chunk's DMA or, with one chunk, for the state
+  __syncthreads();
   if (!out0) {
-    __syncthreads();  // (waits for the output chunk's DMA)
     const int t = lane & (kCh - 1);
     al = t < Treal ? sm.alp[t] : 1.f;
   }
+  // The folded state is written after the last wait for loads: the memory
+  // counter retires in issue order, so any later wait would wait for these
+  // stores too. Past this point the barriers wait for LDS only and the grid
+  // count's return is awaited at the end.
+  if (due) store_state<DK, DV, NT>(st, st_off_of(), H);
   if (wave == 0)
     build_tt<DK, DV>(sm, al, lane, g, l16);
   else if (wave == 1)
     build_c<DK, DV>(sm, al, lane, g, l16);
-  __syncthreads();  // T x T matrices complete
+  lds_barrier();  // T x T matrices complete
   if (wave == 1) build_m<DK, DV>(sm, g, l16);
   {
     f32x4 Y[2][NT], Z[2][NT], Wm[2][NT];

@@ -428,21 +428,27 @@ struct Arrival {
     if (rank_last && tid == 0) *rank_ctr = 0;  // every arrival of the rank is in
   }
 
-  // The last of a rank counts in at the grid counter.
+  // The last of a rank counts in at the grid counter. DEFER: the return is
+  // awaited where it is read, at the end (a buffer atomic at an opaque per-lane
+  // offset; at a uniform address the compiler rewrites the atomic as a
+  // wave-wide one and waits for its return at once, which also waits for every
+  // store issued before it).
+  template <bool DEFER = false>
   __device__ __forceinline__ void grid_in(int HV, int32_t *rank_ctr, int32_t *grid_ctr,
                                           int tid) {
     if (!counting || gridded) return;
     take_rank(HV, rank_ctr, tid);
     gridded = true;
-    // A buffer atomic at an opaque per-lane offset: at a uniform address the
-    // compiler rewrites the atomic as a wave-wide one and waits for its return
-    // at once, which also waits for every store issued before it. Its return is
-    // awaited where it is read, at the end.
-    int off = 0;
-    asm volatile("" : "+v"(off));
-    gticket = -1;
-    if (rank_last && tid == 0)
-      gticket = __builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(1, make_rsrc(grid_ctr, 4), off, 0, 0);
+    if constexpr (DEFER) {
+      int off = 0;
+      asm volatile("" : "+v"(off));
+      gticket = -1;
+      if (rank_last && tid == 0)
+        gticket =
+            __builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(1, make_rsrc(grid_ctr, 4), off, 0, 0);
+    } else {
+      gticket = (rank_last && tid == 0) ? atomicAdd(grid_ctr, 1) : -1;
+    }
   }
 
   // End of the workgroup: the grid's last arrival moves the pointers (wave 0).
@@ -993,7 +999,7 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused_long(Ve
   {
     f32x4 Y[2][NT], Z[2][NT], Wm[2][NT];
     contract<DK, DV, NT, kY | kZ>(sm, H, g, l16, Y, Z);
-    arr.grid_in(HV, rank_ctr, grid_ctr, tid);
+    arr.template grid_in<true>(HV, rank_ctr, grid_ctr, tid);  // (the state's stores in flight)
     lds_barrier();  // M complete (LDS only)
     x_prime<DK, DV, NT>(sm, Y, col_of(), g, Wm);
     emit_outputs<DK, DV, NT>(sm, Z, Wm, g, l16, t0, Treal, uo.B,

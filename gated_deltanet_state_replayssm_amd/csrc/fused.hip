@@ -889,15 +889,22 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused_long(Ve
   };
   const int nch = (u1.T + kCh - 1) / kCh, T0 = u1.T - kCh * (nch - 1);
   const int nfold = due ? nch : nch - 1;
-  // The long chains (two fold chunks or more) issue at raised priority over the
-  // other workgroups on their SIMDs (the T x T builds raise it further, then
-  // drop it to 0: it is raised again after each). 39.6-39.8 -> 38.3-38.6 us per
-  // launch at 32 requests, capacity 80; raising the due slots alone: no gain.
-  const bool long_chain = nfold >= 2;
-  auto chain_prio = [&]() {
-    if (long_chain) __builtin_amdgcn_s_setprio(2);
+  // A workgroup issues at a priority that grows with the fold chunks it has
+  // left (2 for two or more, 1 for one, 0 in the output stage) over the other
+  // workgroups on its SIMDs, so that the longest remaining chains go first. The
+  // T x T builds raise it to 3 and drop it to 0; it is set again after each.
+  // 39.6-39.8 -> 37.0-37.2 us per launch at 32 requests, capacity 80 (a fixed
+  // 2 for workgroups with two fold chunks or more: 38.3-38.6; for the due
+  // slots alone: no gain).
+  auto chain_prio = [&](int left) {
+    if (left >= 2)
+      __builtin_amdgcn_s_setprio(2);
+    else if (left == 1)
+      __builtin_amdgcn_s_setprio(1);
+    else
+      __builtin_amdgcn_s_setprio(0);
   };
-  chain_prio();
+  chain_prio(nfold);
   const bool out0 = !due && nch == 1;  // chunk 0 is the output chunk
   // the output chunk: the draft of a due slot, else the stream's last chunk
   const Unit uo = due ? ud : u1;
@@ -935,7 +942,7 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused_long(Ve
     else
       copy_chunk_keys<DK, 64 * (WAVES - 1)>(lds_kn, lds_kc, lds_abn, lds_abc, opaque_tid() - 64);
   }
-  chain_prio();
+  chain_prio(nfold);
   arr.take_rank(HV, rank_ctr, tid);
   // Every chunk after the first is staged by LDS DMA while its predecessor is
   // computed: its keys, beta and alpha once the predecessor's T x T matrices
@@ -955,10 +962,11 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused_long(Ve
     // (the last wave waits for the return, which comes after its state loads)
     if (due && last && tid == 64 * (WAVES - 1)) group_rank = atomicAdd(group_ctr, 1);
     if (ch > 0) {
+      chain_prio(nfold - ch);
       if (wave == 0) {
         al = smn.alp[lane & (kCh - 1)];
         build_tt<DK, DV>(smn, al, lane, g, l16);
-        chain_prio();
+        chain_prio(nfold - ch);
       } else {
         copy_chunk_keys<DK, 64 * (WAVES - 1)>(lds_kn, lds_kc, lds_abn, lds_abc, opaque_tid() - 64);
       }
@@ -1005,7 +1013,6 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused_long(Ve
     build_tt<DK, DV>(sm, al, lane, g, l16);
   else if (wave == 1)
     build_c<DK, DV>(sm, al, lane, g, l16);
-  chain_prio();
   lds_barrier();  // T x T matrices complete
   if (wave == 1) build_m<DK, DV>(sm, g, l16);
   {

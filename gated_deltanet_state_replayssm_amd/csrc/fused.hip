@@ -241,10 +241,11 @@ struct Move {
 // start of the call, which is what the end-of-grid loop reads too: no pointer
 // changes before the last workgroup.
 //
-// CHAINS (several-chunk replays, up to 64 requests): requests whose workgroups
-// fold two chunks or more come first, due ones first among them, then the rest,
-// due first, so that the long chains are spread over the CUs (36.9 -> 36.2 us
-// per launch at 32 requests, capacity 80; four classes by chunk count: even).
+// CHAINS (several-chunk replays, up to 64 requests): requests in the order of
+// the chunks their workgroups fold (three or more, two, fewer), due first
+// within each class, so that the long chains come first and are spread over
+// the CUs (36.9 -> 36.2 us per launch at 32 requests, capacity 80, with two
+// classes; with three, and the three-chunk chains' state loaded first, 35.6).
 template <bool ROLLBACK, bool VARLEN, bool CHAINS = false>
 __device__ Req ordered_request(const VerifyArgs &va, int mn, int q, int lane, Move *moves) {
   const int R = va.num_reqs;
@@ -305,12 +306,14 @@ __device__ Req ordered_request(const VerifyArgs &va, int mn, int q, int lane, Mo
         const int nch = ((du ? ne : ne + dl) + kCh - 1) / kCh;
         nf = du ? nch : nch - 1;
       }
-      const uint64_t lm = __ballot(nf >= 2), all = lanes(0);
-      const uint64_t ms[4] = {lm & dm, lm & ~dm & all, ~lm & dm & all, ~lm & ~dm & all};
+      const uint64_t all = lanes(0);
+      const uint64_t c3 = __ballot(nf >= 3), c2 = __ballot(nf == 2);
+      const uint64_t c1 = all & ~c3 & ~c2;
+      const uint64_t ms[6] = {c3 & dm, c3 & ~dm, c2 & dm, c2 & ~dm, c1 & dm, c1 & ~dm};
       int left = q;
       r = 0;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
+      for (int k = 0; k < 6; ++k) {
         const int cnt = __popcll(ms[k]);
         if (left >= 0 && left < cnt) r = nth_bit(ms[k], left);
         left -= cnt;
@@ -793,8 +796,8 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused(VerifyA
 // above 32). A due slot folds its n committed tokens chunk by chunk, writes the
 // folded state once and verifies the draft from it (one chunk, B = 0); any
 // other slot replays its committed tokens and the draft as replay_chunked's
-// verify does. The work order puts requests with two fold chunks or more first
-// (up to 64 requests; then due first, as replay_fused). The draft append of a
+// verify does. The work order puts requests with more fold chunks first (up to
+// 64 requests; then due first, as replay_fused). The draft append of a
 // due slot's key and query rows (by the last workgroup of the key head to have
 // staged all its fold inputs) and the end-of-grid pointer move are those of
 // replay_fused.
@@ -939,14 +942,15 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused_long(Ve
   const int Treal = due ? Dq : (nch == 1 ? T0 : kCh);
   {
     // Waves 0..SW-1 stage chunk 0, then load their state. In a workgroup with
-    // two fold chunks or more (the launch's long chains) waves SW.. load their
-    // state at once; in one with a shorter chain they wait until chunk 0 is
-    // staged, so that the long chains' inputs and states enter the memory
-    // queues ahead of theirs (1 us less per launch at 32 requests, capacity
-    // 80). One load_state for both, so that the state is assigned its
-    // registers once (two call sites met at the chunk loop with two
-    // assignments, and the copies between them spilled). The barriers wait for
-    // LDS only.
+    // three fold chunks or more (the launch's longest chains) waves SW.. load
+    // their state at once; in one with a shorter chain they wait until chunk 0
+    // is staged, so that the longest chains' inputs and states enter the
+    // memory queues ahead of theirs (at 32 requests, capacity 80, a threshold
+    // of two chunks saved 1 us per launch, and three another 0.4 us with the
+    // wave priorities below). One load_state for both, so that the state is
+    // assigned its registers once (two call sites met at the chunk loop with
+    // two assignments, and the copies between them spilled). The barriers wait
+    // for LDS only.
     al = 1.f;
     if (wave < SW) {
       Stage<DK, DV, NT, true, 64 * SW> sg0;
@@ -954,11 +958,11 @@ __global__ __launch_bounds__(64 * (DV / (16 * NT)), 4) void replay_fused_long(Ve
       sg0.template store<false>(smn, T0, out0);
       al = sg0.al;
     }
-    if (nfold < 2) lds_barrier();
+    if (nfold < 3) lds_barrier();
     __builtin_amdgcn_sched_barrier(0);
     load_state<DK, DV, NT>(st, st_off_of(), H);
     __builtin_amdgcn_sched_barrier(0);
-    if (nfold >= 2) lds_barrier();
+    if (nfold >= 3) lds_barrier();
   }
   // A fold chunk 0 has its T x T matrices built (and its keys copied) while the
   // state loads are in flight, ahead of the loop: the state's registers are

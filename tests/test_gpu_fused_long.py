@@ -155,3 +155,15 @@ def test_long_one_call_step_bitwise():
             x, y = x.view(torch.int16), y.view(torch.int16)
         assert torch.equal(x, y), name
     assert not a.sync.any()
+
+
+@pytest.mark.parametrize("R,one_call", [(64, False), (65, False), (64, True)])
+def test_long_work_order_at_the_lane_limit(R, one_call):
+    """64 requests (the ordering pass ranks them by fold chunks in one wave's
+    lanes) and 65 (the pass over rounds of 64, due first), with committed
+    counts that give every chunk class (none to three fold chunks)."""
+    wl = synth.Workload("lord", R, R + 8, 2, 1, 64, 64, 80, 16, synth.BF16, 48, 1,
+                        "clipnormal:12:3", "uniform:0:64")
+    say(f"case long work order R={R} one_call={one_call}")
+    pairs = run_schedule(wl, 3, 640 + R, label=f"lord{R}", fused=not one_call, one_call=one_call)
+    assert sum(p.flushed_count for p in pairs) > 0
